@@ -1,0 +1,416 @@
+"""Plain, slow, obviously-correct CPU fp64 oracle of the deterministic MoE layer.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
+the CPU-baseline leg of bench.py, never by the product path.
+
+Sources (cited by title and section):
+  [MoK card] "Mixture-Of-Kittens (MoK)" project card,
+             agentlenshq.com/zh-CN/projects/ghp:cursor/mixture-of-kittens
+  [MoK clip] "Mixture-of-Kittens: Cursor open-sources an MoE training
+             megakernel", miguoliang.com/clip/mixture-of-kittens
+  [OCP MX]   OCP Microscaling Formats (MX) Specification v1.0 (the MXFP8 block
+             format the card names but does not define).
+
+Everything is float64. Inputs that are bf16/fp32 on the device are passed in
+already widened to float64 (exact). Expert weights are passed as a sequence
+`experts` with experts[e] -> (Wg [I][H], Wu [I][H], Wd [H][I]) float64, so a
+caller can convert one expert at a time.
+
+Notation: T tokens, H hidden, I expert intermediate size, E experts, k picks
+per token, R = T*k routed rows, flat row i = t*k + j, permuted row p.
+
+Readings where the pages are silent (each stated where it is used):
+  * the expert FFN is SwiGLU with no biases: h = silu(x.Wg^T) * (x.Wu^T),
+    out = h.Wd^T, silu(a) = a*sigmoid(a);
+  * "stable" permutation = sort rows by expert id, ties by flat index i;
+  * an expert id outside [0, E) sets status bit 0; such rows are placed after
+    all valid rows (ascending i), are not counted in any expert, and their
+    expert output is zero;
+  * the combine uses topk_w as given (no renormalisation), j ascending;
+  * minibatch m holds permuted rows [m*M, (m+1)*M) and lives in ring slot
+    m mod N_s;
+  * the gradient "of the router weights" is d y / d topk_w.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+STATUS_BAD_EXPERT_ID = 1
+
+
+# ============================================================================ schedule
+def schedule(topk_ids, E):
+    """Routing schedule built from the top-k choices.
+
+    [MoK card] "Using the functional API": the schedule is built from the
+    top-k expert choices and is shared by forward and backward.
+    [MoK clip] Key points, bullet 4: routed-token counts stay on the device;
+    How-to item 2: one schedule table serves all four exchange passes.
+
+    counts[e]  = #{i : f[i] = e}
+    offsets    = exclusive prefix sum of counts, offsets[E] = #valid rows
+    perm[p]    = flat row i placed at permuted position p (stable by i)
+    dest[i]    = p with perm[p] = i
+    """
+    f = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    R = f.size
+    valid = (f >= 0) & (f < E)
+    status = 0 if valid.all() else STATUS_BAD_EXPERT_ID
+    key = np.where(valid, f, E)                      # invalid rows sort last
+    counts = np.bincount(key, minlength=E + 1)[:E].astype(np.int64)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(key, kind="stable").astype(np.int64)
+    dest = np.empty(R, np.int64)
+    dest[perm] = np.arange(R, dtype=np.int64)
+    return {"counts": counts, "offsets": offsets, "perm": perm, "dest": dest,
+            "status": status, "R": R, "E": E}
+
+
+def minibatch_count(R, M):
+    """Number of fixed-size minibatches of M permuted rows ([MoK clip] Key
+    points, bullet 3: a tunable minibatch is the unit of overlap)."""
+    return (R + M - 1) // M
+
+
+def ring_row(p, M, n_slots):
+    """Row of the ring token buffer that permuted row p occupies.
+
+    [MoK clip] Key points, bullet 4 and How-to item 4: a fixed-size ring
+    ("macrobatch") of token slots reused on the device. Minibatch m = p // M
+    goes to slot m mod n_slots; the row keeps its offset inside the minibatch.
+    """
+    p = np.asarray(p, dtype=np.int64)
+    return ((p // M) % n_slots) * M + p % M
+
+
+# ============================================================================ expert FFN
+def sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def silu(a):
+    return a * sigmoid(a)
+
+
+def swiglu(a, b):
+    """SwiGLU gate: silu(a) * b ([MoK clip] Key points, bullet 5 and the key
+    chart name the expert FFN "SwiGLU"; gate = a, up = b)."""
+    return silu(a) * b
+
+
+def expert_ffn(X, Wg, Wu, Wd):
+    """One expert's SwiGLU FFN on rows X [n][H] -> (out [n][H], a, b, h)."""
+    a = X @ Wg.T
+    b = X @ Wu.T
+    h = swiglu(a, b)
+    return h @ Wd.T, a, b, h
+
+
+# ============================================================================ forward
+def forward(x, topk_ids, topk_w, experts):
+    """MoE layer forward: dispatch -> per-expert SwiGLU FFN -> weighted combine.
+
+    [MoK clip] Conclusion and the key chart: router top-k -> dispatch of token
+    rows to their experts -> expert FFN (SwiGLU) -> combine -> weighted sum.
+    [MoK clip] How-to item 6: a fixed accumulation order; here the combine
+    adds j = 0..k-1 in ascending order.
+
+    Returns y [T][H] and ctx = {sched, obuf [R][H] (flat row order),
+    a, b [R][I] (permuted order)}.
+    """
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    k = ids.shape[1]
+    E = len(experts)
+    s = schedule(ids, E)
+    R = T * k
+    obuf = np.zeros((R, H), np.float64)
+    I = np.asarray(experts[0][0]).shape[0] if E else 0
+    a_all = np.zeros((R, I), np.float64)
+    b_all = np.zeros((R, I), np.float64)
+    for e in range(E):
+        lo, hi = s["offsets"][e], s["offsets"][e + 1]
+        if hi == lo:
+            continue
+        P = s["perm"][lo:hi]
+        Wg, Wu, Wd = experts[e]
+        out, a, b, _ = expert_ffn(x[P // k], Wg, Wu, Wd)
+        obuf[P] = out
+        a_all[lo:hi] = a
+        b_all[lo:hi] = b
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    y = np.zeros((T, H), np.float64)
+    ob = obuf.reshape(T, k, H)
+    for j in range(k):
+        y += w[:, j:j + 1] * ob[:, j, :]
+    return y, {"sched": s, "obuf": obuf, "a": a_all, "b": b_all}
+
+
+def forward_tokens(x_rows, ids_rows, w_rows, experts):
+    """y for a subset of tokens, straight from the definition
+    y[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x[t]) (rows with an invalid id add 0).
+    Also returns the per-(t, j) expert outputs [n][k][H]."""
+    x_rows = np.asarray(x_rows, np.float64)
+    n, H = x_rows.shape
+    ids_rows = np.asarray(ids_rows).reshape(n, -1)
+    w_rows = np.asarray(w_rows, np.float64).reshape(n, -1)
+    k = ids_rows.shape[1]
+    E = len(experts)
+    outs = np.zeros((n, k, H), np.float64)
+    for e in sorted(set(int(v) for v in ids_rows.reshape(-1) if 0 <= v < E)):
+        sel = np.argwhere(ids_rows == e)
+        Wg, Wu, Wd = experts[e]
+        out, _, _, _ = expert_ffn(x_rows[sel[:, 0]], Wg, Wu, Wd)
+        outs[sel[:, 0], sel[:, 1]] = out
+    y = np.zeros((n, H), np.float64)
+    for j in range(k):
+        y += w_rows[:, j:j + 1] * outs[:, j, :]
+    return y, outs
+
+
+# ============================================================================ backward
+def _swiglu_backward(dh, a, b):
+    """d/da and d/db of silu(a)*b:
+    dA = dh * b * sig(a) * (1 + a * (1 - sig(a))),  dB = dh * a * sig(a)."""
+    sg = sigmoid(a)
+    return dh * b * sg * (1.0 + a * (1.0 - sg)), dh * a * sg
+
+
+def backward(x, topk_ids, topk_w, experts, dy):
+    """Backward of the layer for upstream gradient dy [T][H].
+
+    [MoK card] "What it is" and "Using the functional API": forward and
+    backward are both provided, backward reuses the schedule.
+    [MoK clip] How-to item 2: backward is reverse-combine (dY to the routed
+    rows) then reverse-dispatch (row gradients back to their token).
+
+    Returns dict dx [T][H], dWg/dWu [E][I][H], dWd [E][H][I], dw [T][k].
+    An expert with no rows gets exact zero weight gradients.
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    k = ids.shape[1]
+    E = len(experts)
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    y, ctx = forward(x, ids, w, experts)
+    s = ctx["sched"]
+    R = T * k
+    I = np.asarray(experts[0][0]).shape[0]
+    ob = ctx["obuf"].reshape(T, k, H)
+    dw = np.einsum("th,tjh->tj", dy, ob)           # reverse-combine: d w[t, j]
+    wf = w.reshape(-1)
+    dxrows = np.zeros((R, H), np.float64)
+    dWg = np.zeros((E, I, H))
+    dWu = np.zeros((E, I, H))
+    dWd = np.zeros((E, H, I))
+    for e in range(E):
+        lo, hi = s["offsets"][e], s["offsets"][e + 1]
+        if hi == lo:
+            continue
+        P = s["perm"][lo:hi]
+        Wg, Wu, Wd = experts[e]
+        X = x[P // k]
+        a, b = ctx["a"][lo:hi], ctx["b"][lo:hi]
+        h = swiglu(a, b)
+        dO = wf[P][:, None] * dy[P // k]           # reverse-combine: dY to rows
+        dh = dO @ Wd
+        dWd[e] = dO.T @ h
+        dA, dB = _swiglu_backward(dh, a, b)
+        dWg[e] = dA.T @ X
+        dWu[e] = dB.T @ X
+        dxrows[P] = dA @ Wg + dB @ Wu
+    dx = dxrows.reshape(T, k, H).sum(axis=1)       # reverse-dispatch
+    return {"dx": dx, "dWg": dWg, "dWu": dWu, "dWd": dWd, "dw": dw, "y": y}
+
+
+def backward_tokens(x_rows, ids_rows, w_rows, experts, dy_rows):
+    """dx and dw for a subset of tokens, from the per-row definition:
+    dw[t,j] = <dy[t], FFN_e(x[t])>; dx[t] = sum_j (dA Wg_e + dB Wu_e) with
+    dO = w[t,j] dy[t]."""
+    x_rows = np.asarray(x_rows, np.float64)
+    dy_rows = np.asarray(dy_rows, np.float64)
+    n, H = x_rows.shape
+    ids_rows = np.asarray(ids_rows).reshape(n, -1)
+    w_rows = np.asarray(w_rows, np.float64).reshape(n, -1)
+    k = ids_rows.shape[1]
+    E = len(experts)
+    dx = np.zeros((n, H))
+    dw = np.zeros((n, k))
+    for e in sorted(set(int(v) for v in ids_rows.reshape(-1) if 0 <= v < E)):
+        sel = np.argwhere(ids_rows == e)
+        t, j = sel[:, 0], sel[:, 1]
+        Wg, Wu, Wd = experts[e]
+        out, a, b, _ = expert_ffn(x_rows[t], Wg, Wu, Wd)
+        dw[t, j] = np.sum(dy_rows[t] * out, axis=1)
+        dh = (w_rows[t, j][:, None] * dy_rows[t]) @ Wd
+        dA, dB = _swiglu_backward(dh, a, b)
+        np.add.at(dx, t, dA @ Wg + dB @ Wu)
+    return dx, dw
+
+
+def backward_expert_weights(e, x, topk_ids, topk_w, experts, dy):
+    """(dWg[e], dWu[e], dWd[e]) for one expert from all rows routed to it."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    k = ids.shape[1]
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    sel = np.argwhere(ids == e)                     # ascending flat index
+    Wg, Wu, Wd = experts[e]
+    I = Wg.shape[0]
+    if sel.size == 0:
+        return np.zeros((I, H)), np.zeros((I, H)), np.zeros((H, I))
+    t, j = sel[:, 0], sel[:, 1]
+    X = x[t]
+    _, a, b, h = expert_ffn(X, Wg, Wu, Wd)
+    dO = w[t, j][:, None] * np.asarray(dy, np.float64)[t]
+    dh = dO @ Wd
+    dA, dB = _swiglu_backward(dh, a, b)
+    return dA.T @ X, dB.T @ X, dO.T @ h
+
+
+# ============================================================================ MXFP8
+# [MoK card] "Core concepts" table and "Limits": MXFP8 is a low-precision
+# weight format, weights are pre-quantized by an op before the kernel sees
+# them. The block format is the one [OCP MX] defines: 32 elements share one
+# E8M0 scale (2^(s-127)); each element is FP8 E4M3 (bias 7, no infinities,
+# S.1111.111 = NaN, largest finite 448).
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code):
+    """Value of an E4M3 code (vectorised). NaN for S.1111.111."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    sub = m * 2.0 ** -9
+    nrm = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    v = np.where(e == 0, sub, nrm)
+    v = np.where((e == 0xF) & ((c & 7) == 7), np.nan, v)
+    return sign * v
+
+
+def _round_half_even(q):
+    return np.round(q)                               # numpy rounds half to even
+
+
+def e4m3_encode(v):
+    """Round float64 values to E4M3, nearest-even, saturating at +-448.
+    The sign bit is copied from the input, so -0.0 and negative values that
+    round to zero give 0x80."""
+    v = np.asarray(v, np.float64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    code = np.zeros(a.shape, np.int64)
+    # subnormal range |v| < 2^-6: step 2^-9; a quotient of 8 is code 0x08 (2^-6)
+    sub = a < 2.0 ** -6
+    code = np.where(sub, _round_half_even(a * 2.0 ** 9).astype(np.int64), code)
+    # normal range: exponent from frexp, 3 mantissa bits
+    mant, ex = np.frexp(np.where(sub, 1.0, a))      # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                       # a = (2*mant) * 2^e
+    q = _round_half_even((2.0 * mant - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 0, q)
+    ncode = ((e + 7) << 3) | q
+    ncode = np.where(a > E4M3_MAX, 0x7E, np.minimum(ncode, 0x7E))
+    code = np.where(sub, code, ncode)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize(v):
+    """Quantize along the last axis in blocks of 32 ([OCP MX] scale rule).
+
+    Per block: amax = max |v|; e = floor(log2 amax) - 8 (8 = largest E4M3
+    exponent); scale byte s = clamp(e + 127, 0, 254), s = 0 for an all-zero
+    block; code = E4M3(v / 2^(s - 127)), round to nearest even, saturating.
+    Returns (codes uint8 [..., K], scales uint8 [..., K/32]).
+    """
+    v = np.asarray(v, np.float64)
+    K = v.shape[-1]
+    assert K % 32 == 0
+    blocks = v.reshape(v.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    s = np.clip(ex - 1 - 8 + 127, 0, 254)
+    s = np.where(amax > 0, s, 0).astype(np.int64)
+    scale = np.exp2(s.astype(np.float64) - 127.0)
+    codes = e4m3_encode(blocks / scale[..., None])
+    return codes.reshape(v.shape), s.astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales):
+    codes = np.asarray(codes)
+    K = codes.shape[-1]
+    vals = e4m3_decode(codes).reshape(codes.shape[:-1] + (K // 32, 32))
+    scale = np.exp2(np.asarray(scales, np.float64) - 127.0)
+    return (vals * scale[..., None]).reshape(codes.shape)
+
+
+def mxfp8_roundtrip(v):
+    return mxfp8_dequantize(*mxfp8_quantize(v))
+
+
+def _mx_experts(experts):
+    """Expert weights as the MXFP8 kernel sees them: each matrix quantized
+    along its contraction axis (H for Wg/Wu, I for Wd) and dequantized."""
+    class _Q:
+        def __len__(self):
+            return len(experts)
+
+        def __getitem__(self, e):
+            Wg, Wu, Wd = experts[e]
+            return mxfp8_roundtrip(Wg), mxfp8_roundtrip(Wu), mxfp8_roundtrip(Wd)
+    return _Q()
+
+
+def _mx_ffn(X, Wg, Wu, Wd):
+    a = mxfp8_roundtrip(X) @ Wg.T
+    b = mxfp8_roundtrip(X) @ Wu.T
+    h = mxfp8_roundtrip(swiglu(a, b))
+    return h @ Wd.T
+
+
+def forward_mxfp8(x, topk_ids, topk_w, experts):
+    """MXFP8 forward: both GEMMs take MXFP8 operands. Weights are quantized
+    along their contraction axis, each gathered x row along H, and the SwiGLU
+    output h along I; accumulation and the combine are exact (fp64)."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    k = ids.shape[1]
+    qexp = _mx_experts(experts)
+    s = schedule(ids, len(experts))
+    obuf = np.zeros((T * k, H))
+    for e in range(len(experts)):
+        lo, hi = s["offsets"][e], s["offsets"][e + 1]
+        if hi == lo:
+            continue
+        P = s["perm"][lo:hi]
+        obuf[P] = _mx_ffn(x[P // k], *qexp[e])
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    y = np.einsum("tj,tjh->th", w, obuf.reshape(T, k, H))
+    return y, {"sched": s, "obuf": obuf}
+
+
+def forward_mxfp8_tokens(x_rows, ids_rows, w_rows, experts):
+    """forward_mxfp8 restricted to a subset of tokens (per-row definition)."""
+    x_rows = np.asarray(x_rows, np.float64)
+    n, H = x_rows.shape
+    ids_rows = np.asarray(ids_rows).reshape(n, -1)
+    w_rows = np.asarray(w_rows, np.float64).reshape(n, -1)
+    k = ids_rows.shape[1]
+    qexp = _mx_experts(experts)
+    outs = np.zeros((n, k, H))
+    for e in sorted(set(int(v) for v in ids_rows.reshape(-1) if 0 <= v < len(experts))):
+        sel = np.argwhere(ids_rows == e)
+        outs[sel[:, 0], sel[:, 1]] = _mx_ffn(x_rows[sel[:, 0]], *qexp[e])
+    return np.einsum("tj,tjh->th", w_rows, outs), outs
+
