@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the deterministic MoE layer on one MI355X.
+
+One step = one pass of the whole layer on one batch of synthetic input:
+routing schedule -> forward (saving the backward context) -> backward.
+Default workload: bf16, T=4096 tokens, H=2048, E=64 experts, top-8, I=768,
+near-uniform routing. Inputs are seeded and already resident in HBM when the
+timed region starts.
+
+Prints ONE JSON line. `value` is layer TFLOP/s: algorithmic FLOPs
+(forward 6*R*H*I + backward 12*R*H*I, R = T*k routed rows, padding excluded)
+divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd/bwd TFLOP/s + tokens/s, bf16 & MXFP8; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBS = 8000.0
+
+# algorithmic FLOPs per routed row of each GEMM kernel, in units of H*I
+GEMM_FLOPS_PER_ROW = {
+    "gateup_gemm": 4, "down_gemm": 2, "bwd_dh_gemm": 2, "bwd_dwd_gemm": 2,
+    "bwd_dwgu_gemm": 4, "bwd_dx_gemm": 4, "fwd_persistent": 6,
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="reference workload id (0-4)")
+    ap.add_argument("--cpu-tokens", type=int, default=1024,
+                    help="tokens in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--driver", type=int, default=0)
+    ap.add_argument("--minibatch-rows", type=int, default=0)
+    ap.add_argument("--ring-slots", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok):
+    """The fp64 oracle (as it stands) on the first n_tok tokens of the same
+    workload: forward + backward, reported in the same unit."""
+    import numpy as np
+    import oracle
+    from synthetic import bf16_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+
+    class Ex:
+        def __len__(self):
+            return p.E
+
+        def __getitem__(self, e):
+            return tuple(bf16_to_f32(m[e]).astype(np.float64) for m in (wg, wu, wd))
+
+    xs = bf16_to_f32(x[:n_tok]).astype(np.float64)
+    dys = bf16_to_f32(dy[:n_tok]).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.backward(xs, ids[:n_tok], w[:n_tok].astype(np.float64), Ex(), dys)   # runs forward too
+    dt = time.perf_counter() - t0
+    flops = 18.0 * n_tok * p.k * p.H * p.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tok} of {p.T} tokens (forward+backward, fp64 NumPy), {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    from synthetic import CONFIGS, make_all_experts, make_dy, make_routing, make_x
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    p = CONFIGS[args.config]
+    log(f"[bench] workload {p.name}: generating inputs")
+    x = make_x(p)
+    ids, w = make_routing(p, x)
+    wg, wu, wd = make_all_experts(p, threads=16)
+    dy = make_dy(p)
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    dx_ = dev16(x)
+    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    dw_ = torch.from_numpy(w).cuda()
+    weights = (dev16(wg), dev16(wu), dev16(wd))
+    ddy = dev16(dy)
+    cfg = dict(driver=args.driver, minibatch_rows=args.minibatch_rows, ring_slots=args.ring_slots)
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True, **cfg)
+    y = torch.empty_like(dx_)
+    gx = torch.empty_like(dx_)
+    gwg, gwu, gwd = (torch.empty_like(t) for t in weights)
+    gtw = torch.empty_like(dw_)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mok.build_schedule(ws.problem, dids, ws.schedule, ws.config, stream)
+        mok.forward(ws.problem, ws.schedule, dx_, dw_, weights, y, ws.workspace, ws.fwd_ctx,
+                    ws.config, stream)
+        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, dx_, dw_, weights, ddy, gx, gwg, gwu,
+                     gwd, gtw, ws.workspace, ws.config, stream)
+
+    def fwd_only():
+        mok.build_schedule(ws.problem, dids, ws.schedule, ws.config, stream)
+        mok.forward(ws.problem, ws.schedule, dx_, dw_, weights, y, ws.workspace, None, ws.config,
+                    stream)
+
+    def timed(fn, steps, trace):
+        torch.cuda.synchronize()
+        if trace:
+            mok.trace_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if trace:
+            mok.trace_enable(False)
+        stats = mok.trace_collect() if trace else {}
+        return e0.elapsed_time(e1) / steps, stats
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ms_step, stats = timed(step, args.steps, trace=True)
+    log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
+    ms_fwd, fstats = timed(fwd_only, args.steps, trace=True)
+
+    R, H, I = p.R, p.H, p.I
+    flops_step = p.fwd_flops() + p.bwd_flops()
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # per-kernel live timings (HIP events on the launch stream, timed region)
+    kernels = {}
+    for name, (n, tot, mx) in stats.items():
+        rec = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
+               "avg_launch_ms": tot / n}
+        if name in GEMM_FLOPS_PER_ROW:
+            fl = GEMM_FLOPS_PER_ROW[name] * R * H * I * args.steps
+            rec["tflops"] = fl / (tot * 1e-3) / 1e12
+        kernels[name] = rec
+    gemms = {k: v for k, v in kernels.items() if "tflops" in v}
+    dom = max(gemms, key=lambda k: gemms[k]["ms_per_step"])
+    dn = stats[dom][0]
+    dom_flops_per_launch = GEMM_FLOPS_PER_ROW[dom] * R * H * I * args.steps / dn
+    achieved = gemms[dom]["tflops"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": dom_flops_per_launch,
+                "avg_launch_ms": stats[dom][1] / dn}
+    move = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
+               for k in ("schedule", "gather", "combine", "reverse_combine", "bwd_gather",
+                         "reverse_dispatch"))
+    gemm_ms = sum(v["ms_per_step"] for v in gemms.values())
+    fwd_flops = p.fwd_flops()
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"MoE SwiGLU layer fwd+bwd: {p.name}", "T": p.T, "H": H, "I": I,
+                   "E": p.E, "topk": p.k, "routed_rows": R, "minibatch_rows": ws.config.minibatch_rows
+                   or mok.schedule_layout(ws.problem, ws.config).minibatch_rows,
+                   "ring_slots": mok.schedule_layout(ws.problem, ws.config).ring_slots,
+                   "driver": "persistent" if args.driver == 0 else "launch-per-minibatch"},
+        "tokens_per_s": round(p.T / (ms_step * 1e-3), 1),
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
+        "sched_gather_combine_share": round(move / ms_step, 4),
+        "schedule_share": round(kernels.get("schedule", {}).get("ms_per_step", 0.0) / ms_step, 4),
+        "forward": {"ms": round(ms_fwd, 4), "tflops": round(fwd_flops / (ms_fwd * 1e-3) / 1e12, 2),
+                    "tokens_per_s": round(p.T / (ms_fwd * 1e-3), 1)},
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if args.cpu_tokens > 0:
+        log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(p, x, ids, w, wg, wu, wd, dy, min(args.cpu_tokens, p.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

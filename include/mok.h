@@ -1,0 +1,220 @@
+/*
+ * mok.h -- C ABI of a deterministic mixture-of-experts layer for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The layer routes each of T tokens to k of E experts, runs every routed row
+ * through its expert's SwiGLU FFN and adds the k expert outputs back with the
+ * router's combine weights; its backward returns the gradients of the input,
+ * of every expert weight and of the combine weights. Sources, cited by title
+ * and section:
+ *   [MoK card] "Mixture-Of-Kittens (MoK)" project card (agentlenshq.com):
+ *              "What it is", "Using the functional API", "Core concepts".
+ *   [MoK clip] "Mixture-of-Kittens: Cursor open-sources an MoE training
+ *              megakernel" (miguoliang.com clip): "Key points", "How to",
+ *              and the key chart.
+ *   [OCP MX]   OCP Microscaling Formats (MX) Specification v1.0.
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked [host]. `stream` is a
+ *     hipStream_t passed as void* (NULL = the default stream).
+ *   - Calls that take a stream only enqueue work on it: they never
+ *     synchronize the host with the device, never allocate memory and never
+ *     read device memory from the host ([MoK clip] Key points, bullet 4:
+ *     routing counts stay on the device).
+ *   - The caller owns and allocates every buffer (sizes from
+ *     mok_buffer_sizes) and keeps it alive until the enqueued work is done.
+ *     Inputs and outputs must not alias. The library keeps no per-call state.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Errors found on the host return a negative mok_status before anything
+ *     is enqueued. Errors that only the device can see (an expert id outside
+ *     [0, E)) set a bit in the schedule's status word instead; the rows
+ *     concerned are skipped without any out-of-bounds access.
+ *   - Results are bitwise reproducible: the same inputs, problem, config and
+ *     device give the same output bytes on every call ([MoK clip] How-to
+ *     item 6: a fixed floating-point accumulation order).
+ *
+ * Layouts (row-major, bf16 = IEEE bfloat16 bit patterns)
+ *   topk_ids  [T][k] int32      expert of pick j of token t; flat row i = t*k + j
+ *   topk_w    [T][k] float32    combine weight of pick j (used as given)
+ *   x, y, dy, dx  [T][H] bf16
+ *   w_gate, w_up  [E][I][H]     bf16, or E4M3 codes (MXFP8)
+ *   w_down        [E][H][I]     bf16, or E4M3 codes (MXFP8)
+ *   s_gate, s_up  [E][I][H/32]  E8M0 scale bytes (MXFP8 only)
+ *   s_down        [E][H][I/32]  E8M0 scale bytes (MXFP8 only)
+ * The expert FFN is h = silu(x Wg^T) * (x Wu^T), out = h Wd^T, no biases.
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOK_OK = 0,
+  MOK_ERR_INVALID_ARG = -1,      /* null pointer, bad size or shape            */
+  MOK_ERR_UNSUPPORTED = -2,      /* valid but not supported by this build      */
+  MOK_ERR_BUFFER_TOO_SMALL = -3, /* a caller buffer is below mok_buffer_sizes  */
+  MOK_ERR_DEVICE = -4            /* no gfx950 device, or a launch failed       */
+} mok_status;
+
+typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
+
+/* Status word bits written by mok_build_schedule (read it whenever you like). */
+#define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
+#define MOK_STATUS_WATCHDOG      0x2   /* a persistent-driver wait timed out      */
+
+/* Problem shape. Supported: T >= 1, 1 <= topk <= E <= 512, T*topk < 2^31,
+ * H and I multiples of 128. dtype MOK_MXFP8 is forward-only. */
+typedef struct {
+  int64_t T, H, I;
+  int32_t E, topk;
+  int32_t dtype;                 /* mok_dtype */
+} mok_problem;
+
+/* Tuning knobs ([MoK card] "Core concepts": minibatch granularity,
+ * macrobatch size, schedule capacity multiplier; the communication-CU count
+ * has no meaning on one GPU and is not present). Zero selects the default. */
+typedef struct {
+  int32_t minibatch_rows;        /* M, routed rows per minibatch. Default:
+                                    [MoK clip] How-to item 3 asks for M >= 4*S*H/I
+                                    rows so each grouped GEMM fills two waves;
+                                    M = round_up(ceil(4*S*H/I), 256).            */
+  int32_t ring_slots;            /* N_s, slots of the ring token buffer (the
+                                    "macrobatch" is N_s*M rows). Default 4,
+                                    capped at the minibatch count.               */
+  float capacity_multiplier;     /* accepted (0 or >= 1); on one GPU the exact
+                                    row count T*topk is always used.              */
+  int32_t num_cus;               /* S for the default M; 0 = 256 (MI355X).        */
+  int32_t driver;                /* 0 = persistent minibatch kernel (default),
+                                    1 = one launch per minibatch stage.           */
+} mok_config;
+
+typedef struct {
+  const void* w_gate;            /* [E][I][H] */
+  const void* w_up;              /* [E][I][H] */
+  const void* w_down;            /* [E][H][I] */
+  const uint8_t* s_gate;         /* MXFP8 only, else NULL */
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+} mok_weights;
+
+/* Byte offsets of the arrays inside the schedule buffer (each 256-aligned). */
+typedef struct {
+  size_t status;                 /* int32 status word                              */
+  size_t counts;                 /* int32 [E]   rows routed to each expert         */
+  size_t offsets;                /* int32 [E+1] exclusive prefix sum of counts;
+                                    offsets[E] = number of valid rows              */
+  size_t perm;                   /* int32 [R]   flat row at permuted position p    */
+  size_t dest;                   /* int32 [R]   permuted position of flat row i    */
+  size_t n_fwd_tiles;            /* int32       forward row tiles                  */
+  size_t fwd_tiles;              /* int32x4 [max_fwd_tiles] {e, p0, p1, m}          */
+  size_t mb_tile_start;          /* int32 [n_minibatches + 1]                      */
+  size_t n_bwd_tiles;            /* int32       backward row tiles                 */
+  size_t bwd_tiles;              /* int32x4 [max_bwd_tiles] {e, p0, p1, 0}          */
+  size_t total;
+  int32_t minibatch_rows;        /* resolved M   */
+  int32_t ring_slots;            /* resolved N_s */
+  int32_t n_minibatches;         /* ceil(R / M)  */
+  int32_t max_fwd_tiles, max_bwd_tiles, fwd_tile_rows, bwd_tile_rows;
+} mok_schedule_layout;
+
+/* [host] Library version, major*10000 + minor*100 + patch. */
+int32_t mok_version(void);
+
+/* [host] Static text for a status code. */
+const char* mok_status_string(int32_t status);
+
+/* [host] Sizes in bytes of the three caller-allocated buffers for `problem`
+ * under `config` (NULL = defaults). No device access. workspace: scratch for
+ * any call, reusable across layers. schedule: written by mok_build_schedule,
+ * read by forward and backward. fwd_ctx: what forward saves for backward
+ * ([MoK card] "Using the functional API": forward returns (out, fwd_ctx)). */
+mok_status mok_buffer_sizes(const mok_problem* problem, const mok_config* config,
+                            size_t* workspace_bytes, size_t* schedule_bytes,
+                            size_t* fwd_ctx_bytes);
+
+/* [host] Where each schedule array lives inside the schedule buffer. */
+mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config* config,
+                                   mok_schedule_layout* layout);
+
+/* Routing schedule ([MoK card] "Using the functional API": build_schedule
+ * from the top-k expert choices; [MoK clip] Key points, bullet 4: built
+ * entirely on the GPU; How-to item 2: one schedule serves all four exchange
+ * passes of forward and backward).
+ * Computes per-expert counts, their exclusive prefix sum, and the stable
+ * permutation of the T*k routed rows into expert order (ties by flat row
+ * index), its inverse, and the row tiles of the grouped GEMMs: forward tiles
+ * never cross an expert or a minibatch boundary (minibatch m = permuted rows
+ * [m*M, (m+1)*M), held in ring slot m mod N_s). Rows whose id is outside
+ * [0, E) are placed after every valid row and set MOK_STATUS_BAD_EXPERT_ID. */
+mok_status mok_build_schedule(const mok_problem* problem, const mok_config* config,
+                              const int32_t* topk_ids,
+                              void* schedule, size_t schedule_bytes, void* stream);
+
+/* Forward ([MoK clip] Conclusion and key chart: dispatch -> expert SwiGLU
+ * FFN -> combine -> weighted sum). Per minibatch, in order: gather the rows
+ * x[perm[p] / k] into a ring slot, gate/up grouped GEMM with the SwiGLU in
+ * its epilogue, down grouped GEMM writing each expert output to its flat row
+ * i; then y[t] = sum_{j=0..k-1} topk_w[t][j] * out[t*k + j], accumulated in
+ * fp32 in ascending j and rounded once to bf16.
+ * fwd_ctx: NULL for inference; else receives what mok_backward needs
+ * (bf16 only). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
+ * mok_mxfp8_quantize): x rows are quantized along H and h along I the same
+ * way on the fly; accumulation is fp32, y is bf16. */
+mok_status mok_forward(const mok_problem* problem, const mok_config* config,
+                       const void* schedule, const void* x, const float* topk_w,
+                       const mok_weights* weights, void* y, void* fwd_ctx,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward (bf16). [MoK clip] How-to item 2: reverse-combine then
+ * reverse-dispatch with the same schedule. Outputs:
+ *   d_topk_w[t][j] = <dy[t], out[t*k+j]>           (fp32)
+ *   dx [T][H], dw_gate/dw_up [E][I][H], dw_down [E][H][I]   (bf16)
+ * Every reduction runs in a fixed order with no atomics; an expert with no
+ * rows gets exact-zero weight gradients. */
+mok_status mok_backward(const mok_problem* problem, const mok_config* config,
+                        const void* schedule, const void* fwd_ctx,
+                        const void* x, const float* topk_w, const mok_weights* weights,
+                        const void* dy, void* dx, void* dw_gate, void* dw_up,
+                        void* dw_down, float* d_topk_w,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* MXFP8 quantization ([MoK card] "Core concepts" and "Limits": MXFP8
+ * weights are pre-quantized by an op; block format from [OCP MX]).
+ * src [rows][K] bf16 -> q [rows][K] E4M3 codes and scales [rows][K/32] E8M0:
+ * per 32-element block, s = clamp(floor(log2 amax) - 8 + 127, 0, 254)
+ * (0 for an all-zero block) and q = E4M3(v * 2^(127-s)), round to nearest
+ * even, saturating at 448. K must be a multiple of 32; rows >= 0. */
+mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K,
+                              uint8_t* q, uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------- tracing
+ * Per-kernel timing for profiling ([MoK clip] How-to item 1: profile first to
+ * see where the layer's time goes). While tracing is on, every kernel the
+ * library launches is bracketed by two HIP events recorded on its launch
+ * stream (host-side calls only; nothing waits). mok_trace_collect waits for
+ * the recorded events (a host synchronisation, so never call it inside a
+ * timed or captured region), returns per-kernel totals in launch order of
+ * first appearance and clears the record. The library creates and reuses
+ * the events itself. Not thread-safe across concurrent callers. */
+typedef struct {
+  char name[40];
+  int32_t launches;
+  double total_ms;
+  double max_ms;
+} mok_trace_stat;
+
+/* [host] on != 0 starts recording, 0 stops (records are kept until collected). */
+mok_status mok_trace_enable(int32_t on);
+
+/* [host] Fill out[0 .. min(n, capacity)) and *n_out = n, the number of kernels. */
+mok_status mok_trace_collect(mok_trace_stat* out, int32_t capacity, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOK_H */

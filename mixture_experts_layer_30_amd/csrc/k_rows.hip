@@ -1,0 +1,218 @@
+// Row-wise, HBM-bound kernels of the MoE layer: token gather (dispatch),
+// weighted combine, reverse-combine, reverse-dispatch and MXFP8 quantization.
+//
+// [MoK clip] How-to item 2: forward = pull dispatch + push combine, backward =
+// pull reverse-combine + push reverse-dispatch, all four from one schedule.
+// On one GPU the exchange is a local gather/scatter through HBM; each kernel
+// moves whole rows with 16-byte accesses so a wavefront touches contiguous
+// 1 KiB spans.
+#include "mok_device.h"
+#include "mok_launch.h"
+
+namespace {
+
+MOK_DEV void unpack8(const uint4& v, float f[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(w[q] << 16);
+    f[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+}
+
+MOK_DEV uint4 pack8(const float f[8]) {
+  uint4 r;
+  r.x = pack_bf16x2(f[0], f[1]);
+  r.y = pack_bf16x2(f[2], f[3]);
+  r.z = pack_bf16x2(f[4], f[5]);
+  r.w = pack_bf16x2(f[6], f[7]);
+  return r;
+}
+
+// ------------------------------------------------------------------ gather
+// One wavefront per destination row.
+__global__ __launch_bounds__(256) void gather_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets_E, int topk, int64_t row_bytes, int64_t p_begin,
+    int64_t rows, uint8_t* __restrict__ dst, const uint8_t* __restrict__ scales, int64_t sbytes,
+    uint8_t* __restrict__ dst_scales) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (r >= rows) return;
+  const int64_t p = p_begin + r;
+  if (p >= *offsets_E) return;                   // rows of invalid ids: no tile reads them
+  const int64_t t = perm[p] / topk;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * row_bytes);
+  uint4* d = reinterpret_cast<uint4*>(dst + r * row_bytes);
+  const int64_t n16 = row_bytes >> 4;
+  for (int64_t c = lane; c < n16; c += 64) d[c] = src[c];
+  if (scales) {
+    const uint32_t* ss = reinterpret_cast<const uint32_t*>(scales + t * sbytes);
+    uint32_t* ds = reinterpret_cast<uint32_t*>(dst_scales + r * sbytes);
+    for (int64_t c = lane; c < (sbytes >> 2); c += 64) ds[c] = ss[c];
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// One thread per (token, 8 columns). y = sum over j ascending of w*o in fp32.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const bf16_t* __restrict__ obuf, const float* __restrict__ w,
+    const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
+    int64_t H, bf16_t* __restrict__ y) {
+  const int64_t nch = H >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = idx / nch, c = idx - t * nch;
+  if (t >= T) return;
+  const int nvalid = *offsets_E;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const int64_t i = t * topk + j;
+    if (dest[i] >= nvalid) continue;
+    const float wj = w ? w[i] : 1.0f;
+    float o[8];
+    unpack8(reinterpret_cast<const uint4*>(obuf + i * H)[c], o);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, o[q], acc[q]);
+  }
+  reinterpret_cast<uint4*>(y + t * H)[c] = pack8(acc);
+}
+
+// ------------------------------------------------------------------ reverse-combine
+// One wavefront per token: dw[t][j] = <dy[t], obuf[t*k+j]> reduced in a fixed
+// order (each lane sums its columns in ascending order, then a xor butterfly),
+// and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order.
+__global__ __launch_bounds__(256) void reverse_combine_kernel(
+    const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
+    const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
+    int64_t H, float* __restrict__ dw, bf16_t* __restrict__ dO) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (t >= T) return;
+  const int nvalid = *offsets_E;
+  const int64_t nch = H >> 3;
+  const uint4* dyr = reinterpret_cast<const uint4*>(dy + t * H);
+  for (int j = 0; j < topk; ++j) {
+    const int64_t i = t * topk + j;
+    const int p = dest[i];
+    const bool valid = p < nvalid;
+    const float wj = w[i];
+    const uint4* orow = reinterpret_cast<const uint4*>(obuf + i * H);
+    uint4* drow = reinterpret_cast<uint4*>(dO + (int64_t)p * H);
+    float part = 0.f;
+    for (int64_t c = lane; c < nch; c += 64) {
+      float g[8], o[8], d[8];
+      unpack8(dyr[c], g);
+      if (valid) {
+        unpack8(orow[c], o);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          part = fmaf(g[q], o[q], part);
+          d[q] = wj * g[q];
+        }
+        drow[c] = pack8(d);
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) part += __shfl_xor(part, s);
+    if (lane == 0) dw[i] = valid ? part : 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------ MXFP8 quantize
+// One thread per 32-element block: amax -> E8M0 scale -> 32 E4M3 codes.
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __restrict__ src,
+                                                            int64_t nblocks, int64_t K,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ scales) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nblocks) return;
+  const int64_t nb = K >> 5;
+  const int64_t r = idx / nb, b = idx - r * nb;
+  const uint4* s = reinterpret_cast<const uint4*>(src + r * K + b * 32);
+  float v[32];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) unpack8(s[u], v + 8 * u);
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(v[u]));
+  const int sc = mx_scale_byte(amax);
+  const float inv = mx_inv_scale(sc);
+  uint32_t wds[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    wds[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
+             (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
+  }
+  uint4* d = reinterpret_cast<uint4*>(q + r * K + b * 32);
+  d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+  scales[idx] = (uint8_t)sc;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+inline unsigned grid_for(int64_t n, int64_t per_block) {
+  return (unsigned)((n + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+hipError_t mok_launch_gather(const void* x, const int32_t* perm, const int32_t* offsets_E,
+                             int topk, int64_t row_bytes, int64_t p_begin, int64_t rows,
+                             void* dst, const uint8_t* scales, int64_t sbytes,
+                             uint8_t* dst_scales, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st,
+                     (const uint8_t*)x, perm, offsets_E, topk, row_bytes, p_begin, rows,
+                     (uint8_t*)dst, scales, sbytes, dst_scales);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t* dest,
+                              const int32_t* offsets_E, int64_t T, int topk, int64_t H,
+                              bf16_t* y, hipStream_t st) {
+  const int64_t n = T * (H / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, obuf, w, dest,
+                     offsets_E, T, topk, H, y);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
+                                      const int32_t* dest, const int32_t* offsets_E, int64_t T,
+                                      int topk, int64_t H, float* dw, bf16_t* dO,
+                                      hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reverse_combine_kernel, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf, w,
+                     dest, offsets_E, T, topk, H, dw, dO);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_reverse_dispatch(const bf16_t* dxrows, const int32_t* dest,
+                                       const int32_t* offsets_E, int64_t T, int topk, int64_t H,
+                                       bf16_t* dx, hipStream_t st) {
+  const int64_t n = T * (H / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dxrows,
+                     (const float*)nullptr, dest, offsets_E, T, topk, H, dx);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K, uint8_t* q,
+                                     uint8_t* scales, hipStream_t st) {
+  const int64_t nblocks = rows * (K / 32);
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, st, src,
+                     nblocks, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_zero(void* p, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, st, (uint4*)p, n16);
+  return hipGetLastError();
+}

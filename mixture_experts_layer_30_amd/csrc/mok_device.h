@@ -1,0 +1,84 @@
+// Device-side types and helpers shared by the MoE kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOK_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;   // bfloat16 storage (bit pattern)
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+
+// ------------------------------------------------------------------ schedule layout
+// The schedule buffer: a header, then per-expert and per-row arrays, then the
+// row-tile tables the grouped GEMMs walk. All offsets are 256-byte aligned and
+// computed on the host (mok_layout.h).
+struct mok_tile {          // one row tile of one expert: permuted rows [p0, p1)
+  int32_t e, p0, p1, m;    // m = minibatch index (p0 / M) for forward tiles
+};
+
+// ------------------------------------------------------------------ bf16 helpers
+MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+MOK_DEV bf16_t f32_to_bf16(float f) {  // round to nearest even (finite inputs)
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (bf16_t)(b >> 16);
+}
+
+MOK_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+MOK_DEV float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// ------------------------------------------------------------------ MXFP8 (OCP MX v1.0)
+// E8M0 scale byte of a 32-element block from its largest magnitude:
+// s = clamp(floor(log2 amax) - 8 + 127, 0, 254); 0 for an all-zero block.
+MOK_DEV int mx_scale_byte(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  if (amax == 0.0f) return 0;
+  int field = (int)((b >> 23) & 0xFF);
+  int e;
+  if (field > 0) e = field - 127;
+  else e = (31 - __clz((int)(b & 0x7FFFFF))) - 149;   // subnormal amax
+  int s = e - 8 + 127;
+  return s < 0 ? 0 : (s > 254 ? 254 : s);
+}
+
+// E4M3 code of q (|q| < 2^9 after block scaling), round to nearest even,
+// saturating to +-448; the sign bit is copied from q (so -0 -> 0x80).
+MOK_DEV uint32_t e4m3_encode(float q) {
+  uint32_t b = __float_as_uint(q);
+  uint32_t sign = (b >> 24) & 0x80u;
+  float a = fabsf(q);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7E;
+  } else if (a < 0.015625f) {            // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // rint = ties to even; 8 -> 0x08
+  } else {
+    uint32_t ab = __float_as_uint(a);
+    int ex = (int)((ab >> 23) & 0xFF) - 127;        // -6 .. 8
+    uint32_t mant = ab & 0x7FFFFFu;
+    uint32_t keep = mant >> 20, rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+    if (keep == 8u) { keep = 0; ++ex; }
+    code = ((uint32_t)(ex + 7) << 3) | keep;
+    if (code > 0x7Eu) code = 0x7E;
+  }
+  return code | sign;
+}
+
+// 2^(127 - s) as a float multiplier (exact; s in 0..254).
+MOK_DEV float mx_inv_scale(int s) { return ldexpf(1.0f, 127 - s); }
+
+// ------------------------------------------------------------------ misc
+MOK_DEV int lane_id() { return (int)(threadIdx.x & 63); }
+
+template <typename T>
+MOK_DEV T ceil_div(T a, T b) { return (a + b - 1) / b; }

@@ -1,0 +1,442 @@
+// Host side of libmok: argument validation, buffer layouts and the launch
+// sequences behind the C ABI declared in include/mok.h. Nothing here reads
+// device memory or synchronises: every count the device computes stays there.
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mok.h"
+#include "mok_device.h"
+#include "mok_launch.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;   // 0.1.0
+constexpr int kMaxE = 512;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Resolved {
+  int64_t T, H, I, R;
+  int E, k;
+  bool mx;
+  int M, n_slots, n_mb;
+  int max_fwd_tiles, max_bwd_tiles, max_tiles_mb;
+};
+
+mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
+  if (!p) return MOK_ERR_INVALID_ARG;
+  if (p->T < 0 || p->H <= 0 || p->I <= 0 || p->E <= 0 || p->topk <= 0) return MOK_ERR_INVALID_ARG;
+  if (p->topk > p->E) return MOK_ERR_INVALID_ARG;
+  if (p->dtype != MOK_BF16 && p->dtype != MOK_MXFP8) return MOK_ERR_INVALID_ARG;
+  if (p->E > kMaxE) return MOK_ERR_UNSUPPORTED;
+  if (p->H % 128 != 0 || p->I % 128 != 0) return MOK_ERR_UNSUPPORTED;
+  if (p->H > (1 << 20) || p->I > (1 << 20)) return MOK_ERR_UNSUPPORTED;
+  const int64_t R = p->T * (int64_t)p->topk;
+  if (R >= (int64_t)1 << 31 || R * p->H >= (int64_t)1 << 46) return MOK_ERR_UNSUPPORTED;
+  mok_config d;
+  memset(&d, 0, sizeof d);
+  if (c) d = *c;
+  if (d.minibatch_rows < 0 || d.ring_slots < 0 || d.num_cus < 0) return MOK_ERR_INVALID_ARG;
+  if (!(d.capacity_multiplier == 0.0f || d.capacity_multiplier >= 1.0f)) return MOK_ERR_INVALID_ARG;
+  if (d.driver < 0 || d.driver > 1) return MOK_ERR_INVALID_ARG;
+  r->T = p->T; r->H = p->H; r->I = p->I; r->R = R;
+  r->E = p->E; r->k = p->topk; r->mx = p->dtype == MOK_MXFP8;
+  // [MoK clip] How-to item 3: minibatch rows M >= 4*S*H/I (two waves of the
+  // gate/up grouped GEMM); rounded up to a multiple of 256 rows.
+  int64_t M = d.minibatch_rows;
+  if (M == 0) {
+    const int64_t S = d.num_cus ? d.num_cus : 256;
+    M = cdiv(cdiv(4 * S * p->H, p->I), 256) * 256;
+  }
+  if (M < 1) return MOK_ERR_INVALID_ARG;
+  M = std::min<int64_t>(M, std::max<int64_t>(R, 1));
+  r->M = (int)M;
+  r->n_mb = (int)cdiv(R, M);
+  int ns = d.ring_slots ? d.ring_slots : 4;
+  ns = std::max(1, std::min(ns, std::max(r->n_mb, 1)));
+  r->n_slots = ns;
+  r->max_fwd_tiles = (int)(cdiv(R, kTileRowsFwd) + r->E + r->n_mb + 1);
+  r->max_bwd_tiles = (int)(cdiv(R, kTileRowsBwd) + r->E + 1);
+  r->max_tiles_mb = (int)std::min<int64_t>(cdiv(M, kTileRowsFwd) + r->E, r->max_fwd_tiles);
+  return MOK_OK;
+}
+
+struct SchedLayout {
+  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, total;
+};
+
+SchedLayout sched_layout(const Resolved& r) {
+  SchedLayout L;
+  size_t o = 0;
+  L.status = o;    o = align_up(o + 4);
+  L.counts = o;    o = align_up(o + 4 * (size_t)r.E);
+  L.offsets = o;   o = align_up(o + 4 * (size_t)(r.E + 1));
+  L.perm = o;      o = align_up(o + 4 * (size_t)r.R);
+  L.dest = o;      o = align_up(o + 4 * (size_t)r.R);
+  L.n_fwd = o;     o = align_up(o + 4);
+  L.fwd_tiles = o; o = align_up(o + sizeof(mok_tile) * (size_t)r.max_fwd_tiles);
+  L.mb_start = o;  o = align_up(o + 4 * (size_t)(r.n_mb + 1));
+  L.n_bwd = o;     o = align_up(o + 4);
+  L.bwd_tiles = o; o = align_up(o + sizeof(mok_tile) * (size_t)r.max_bwd_tiles);
+  L.total = o;
+  return L;
+}
+
+mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
+  const SchedLayout L = sched_layout(r);
+  uint8_t* b = static_cast<uint8_t*>(base);
+  mok_sched_ptrs s;
+  s.status = reinterpret_cast<int32_t*>(b + L.status);
+  s.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  s.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  s.perm = reinterpret_cast<int32_t*>(b + L.perm);
+  s.dest = reinterpret_cast<int32_t*>(b + L.dest);
+  s.n_fwd_tiles = reinterpret_cast<int32_t*>(b + L.n_fwd);
+  s.fwd_tiles = reinterpret_cast<mok_tile*>(b + L.fwd_tiles);
+  s.mb_tile_start = reinterpret_cast<int32_t*>(b + L.mb_start);
+  s.n_bwd_tiles = reinterpret_cast<int32_t*>(b + L.n_bwd);
+  s.bwd_tiles = reinterpret_cast<mok_tile*>(b + L.bwd_tiles);
+  return s;
+}
+
+// Workspace carve-up. Forward and backward never run inside one call, so
+// they share the same bytes.
+struct FwdWs {
+  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
+};
+struct BwdWs {
+  size_t dO, dab, hb, dxrows, xg, total;
+};
+
+FwdWs fwd_ws(const Resolved& r) {
+  FwdWs w;
+  const size_t slots = (size_t)r.n_slots * r.M;
+  size_t o = 0;
+  w.ring_x = o;  o = align_up(o + slots * (r.mx ? r.H : 2 * r.H));
+  w.ring_xs = o; o = align_up(o + (r.mx ? slots * (r.H / 32) : 0));
+  w.ring_h = o;  o = align_up(o + slots * (r.mx ? r.I : 2 * r.I));
+  w.ring_hs = o; o = align_up(o + (r.mx ? slots * (r.I / 32) : 0));
+  w.obuf = o;    o = align_up(o + (size_t)r.R * 2 * r.H);
+  w.xq = o;      o = align_up(o + (r.mx ? (size_t)r.T * r.H : 0));
+  w.xqs = o;     o = align_up(o + (r.mx ? (size_t)r.T * (r.H / 32) : 0));
+  w.total = o;
+  return w;
+}
+
+BwdWs bwd_ws(const Resolved& r) {
+  BwdWs w;
+  size_t o = 0;
+  w.dO = o;     o = align_up(o + (size_t)r.R * 2 * r.H);
+  w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
+  w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
+  w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
+  w.xg = o;     o = align_up(o + (size_t)r.R * 2 * r.H);
+  w.total = r.mx ? 0 : o;
+  return w;
+}
+
+size_t ws_bytes(const Resolved& r) { return std::max(fwd_ws(r).total, bwd_ws(r).total); }
+
+size_t ctx_bytes(const Resolved& r) {
+  if (r.mx) return 0;
+  return align_up((size_t)r.R * 2 * r.H) + align_up((size_t)r.R * 4 * r.I);
+}
+
+// gfx950 check, once per device; queries device properties only.
+mok_status check_device() {
+  static std::mutex mu;
+  static int state[64] = {0};   // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOK_ERR_DEVICE;
+  std::lock_guard<std::mutex> g(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOK_ERR_DEVICE;
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return state[dev] == 1 ? MOK_OK : MOK_ERR_DEVICE;
+}
+
+mok_status launched(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_DEVICE; }
+
+// Launch tracing: when on, each launch is bracketed by two events recorded on
+// its stream. Events come from a pool that is reused across collections.
+struct Tracer {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    hipEvent_t e = nullptr;
+    if (!pool.empty()) {
+      e = pool.back();
+      pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+    }
+    return e;
+  }
+};
+Tracer g_tr;
+
+struct TraceScope {
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  TraceScope(const char* n, hipStream_t s) : name(n), st(s) {
+    if (!g_tr.on) return;
+    std::lock_guard<std::mutex> g(g_tr.mu);
+    a = g_tr.get();
+    if (a) (void)hipEventRecord(a, st);
+  }
+  ~TraceScope() {
+    if (!a) return;
+    std::lock_guard<std::mutex> g(g_tr.mu);
+    hipEvent_t b = g_tr.get();
+    if (!b) return;
+    (void)hipEventRecord(b, st);
+    g_tr.recs.push_back({name, a, b});
+  }
+};
+
+#define MOK_TRY(expr)                               \
+  do {                                              \
+    const mok_status _s = launched(expr);           \
+    if (_s != MOK_OK) return _s;                    \
+  } while (0)
+
+// Launch `expr` (which enqueues one kernel on `st`) under the tracer.
+#define MOK_RUN(name, expr)                         \
+  do {                                              \
+    TraceScope _ts(name, st);                       \
+    MOK_TRY(expr);                                  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t mok_version(void) { return kVersion; }
+
+const char* mok_status_string(int32_t s) {
+  switch (s) {
+    case MOK_OK: return "ok";
+    case MOK_ERR_INVALID_ARG: return "invalid argument";
+    case MOK_ERR_UNSUPPORTED: return "unsupported problem or configuration";
+    case MOK_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case MOK_ERR_DEVICE: return "device error (no gfx950 device or launch failure)";
+    default: return "unknown status";
+  }
+}
+
+mok_status mok_buffer_sizes(const mok_problem* problem, const mok_config* config,
+                            size_t* workspace_bytes, size_t* schedule_bytes,
+                            size_t* fwd_ctx_bytes) {
+  Resolved r;
+  const mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (workspace_bytes) *workspace_bytes = ws_bytes(r);
+  if (schedule_bytes) *schedule_bytes = sched_layout(r).total;
+  if (fwd_ctx_bytes) *fwd_ctx_bytes = ctx_bytes(r);
+  return MOK_OK;
+}
+
+mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config* config,
+                                   mok_schedule_layout* out) {
+  if (!out) return MOK_ERR_INVALID_ARG;
+  Resolved r;
+  const mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  const SchedLayout L = sched_layout(r);
+  out->status = L.status; out->counts = L.counts; out->offsets = L.offsets;
+  out->perm = L.perm; out->dest = L.dest; out->n_fwd_tiles = L.n_fwd;
+  out->fwd_tiles = L.fwd_tiles; out->mb_tile_start = L.mb_start; out->n_bwd_tiles = L.n_bwd;
+  out->bwd_tiles = L.bwd_tiles; out->total = L.total;
+  out->minibatch_rows = r.M; out->ring_slots = r.n_slots; out->n_minibatches = r.n_mb;
+  out->max_fwd_tiles = r.max_fwd_tiles; out->max_bwd_tiles = r.max_bwd_tiles;
+  out->fwd_tile_rows = kTileRowsFwd; out->bwd_tile_rows = kTileRowsBwd;
+  return MOK_OK;
+}
+
+mok_status mok_build_schedule(const mok_problem* problem, const mok_config* config,
+                              const int32_t* topk_ids, void* schedule, size_t schedule_bytes,
+                              void* stream) {
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || (r.R > 0 && !topk_ids)) return MOK_ERR_INVALID_ARG;
+  if (schedule_bytes < sched_layout(r).total) return MOK_ERR_BUFFER_TOO_SMALL;
+  if ((s = check_device()) != MOK_OK) return s;
+  const mok_sched_ptrs p = sched_ptrs(r, schedule);
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN("schedule", mok_launch_schedule(topk_ids, p, (int)r.R, r.E, r.M, kTileRowsFwd,
+                                          kTileRowsBwd, r.n_mb, r.max_fwd_tiles,
+                                          r.max_bwd_tiles, st));
+  return MOK_OK;
+}
+
+mok_status mok_forward(const mok_problem* problem, const mok_config* config, const void* schedule,
+                       const void* x, const float* topk_w, const mok_weights* weights, void* y,
+                       void* fwd_ctx, void* workspace, size_t workspace_bytes, void* stream) {
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
+  if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
+  if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
+  if (r.mx && fwd_ctx) return MOK_ERR_UNSUPPORTED;
+  const FwdWs W = fwd_ws(r);
+  if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
+  if ((s = check_device()) != MOK_OK) return s;
+  if (r.T == 0) return MOK_OK;
+  if (r.mx) return MOK_ERR_UNSUPPORTED;   // MXFP8 GEMM path not built yet
+  hipStream_t st = (hipStream_t)stream;
+  const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+
+  mok_fwd_args a;
+  memset(&a, 0, sizeof a);
+  a.T = r.T; a.H = r.H; a.I = r.I; a.E = r.E; a.topk = r.k;
+  a.M = r.M; a.n_slots = r.n_slots; a.n_mb = r.n_mb;
+  a.perm = sp.perm; a.tiles = sp.fwd_tiles; a.n_tiles = sp.n_fwd_tiles;
+  a.mb_tile_start = sp.mb_tile_start;
+  a.wg = weights->w_gate; a.wu = weights->w_up; a.wd = weights->w_down;
+  a.sg = weights->s_gate; a.su = weights->s_up; a.sd = weights->s_down;
+  a.ring_x = ws + W.ring_x; a.ring_xs = ws + W.ring_xs;
+  a.ring_h = ws + W.ring_h; a.ring_hs = ws + W.ring_hs;
+  uint8_t* ctx = static_cast<uint8_t*>(fwd_ctx);
+  a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx : ws + W.obuf);
+  a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + align_up((size_t)r.R * 2 * r.H)) : nullptr;
+
+  const int64_t xrow = 2 * r.H;
+  for (int m = 0; m < r.n_mb; ++m) {
+    const int64_t p0 = (int64_t)m * r.M;
+    const int64_t rows = std::min<int64_t>(r.M, r.R - p0);
+    uint8_t* slot = a.ring_x + (size_t)(m % r.n_slots) * r.M * xrow;
+    MOK_RUN("gather", mok_launch_gather(x, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows, slot,
+                                        nullptr, 0, nullptr, st));
+    MOK_RUN("gateup_gemm", mok_launch_gateup(a, m, r.max_tiles_mb, false, st));
+    MOK_RUN("down_gemm", mok_launch_down(a, m, r.max_tiles_mb, false, st));
+  }
+  MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
+                             static_cast<bf16_t*>(y), st));
+  return MOK_OK;
+}
+
+mok_status mok_backward(const mok_problem* problem, const mok_config* config,
+                        const void* schedule, const void* fwd_ctx, const void* x,
+                        const float* topk_w, const mok_weights* weights, const void* dy, void* dx,
+                        void* dw_gate, void* dw_up, void* dw_down, float* d_topk_w,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (r.mx) return MOK_ERR_UNSUPPORTED;
+  if (!schedule || !fwd_ctx || !weights || !dw_gate || !dw_up || !dw_down) return MOK_ERR_INVALID_ARG;
+  if (r.T > 0 && (!x || !topk_w || !dy || !dx || !d_topk_w)) return MOK_ERR_INVALID_ARG;
+  if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
+  const BwdWs W = bwd_ws(r);
+  if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
+  if ((s = check_device()) != MOK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const uint8_t* ctx = static_cast<const uint8_t*>(fwd_ctx);
+
+  mok_bwd_args a;
+  memset(&a, 0, sizeof a);
+  a.T = r.T; a.H = r.H; a.I = r.I; a.E = r.E; a.topk = r.k;
+  a.perm = sp.perm; a.offsets = sp.offsets; a.tiles = sp.bwd_tiles; a.n_tiles = sp.n_bwd_tiles;
+  a.max_tiles = r.max_bwd_tiles;
+  a.wg = static_cast<const bf16_t*>(weights->w_gate);
+  a.wu = static_cast<const bf16_t*>(weights->w_up);
+  a.wd = static_cast<const bf16_t*>(weights->w_down);
+  const bf16_t* obuf = reinterpret_cast<const bf16_t*>(ctx);
+  a.ab = reinterpret_cast<const bf16_t*>(ctx + align_up((size_t)r.R * 2 * r.H));
+  a.dO = reinterpret_cast<bf16_t*>(ws + W.dO);
+  a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
+  a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
+  a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
+  a.xg = reinterpret_cast<bf16_t*>(ws + W.xg);
+  a.dwg = static_cast<bf16_t*>(dw_gate);
+  a.dwu = static_cast<bf16_t*>(dw_up);
+  a.dwd = static_cast<bf16_t*>(dw_down);
+
+  if (r.T > 0) {
+    MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
+                                       sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
+                                       const_cast<bf16_t*>(a.dO), st));
+    MOK_RUN("bwd_gather", mok_launch_gather(x, sp.perm, sp.offsets + r.E, r.k, 2 * r.H, 0, r.R,
+                                            const_cast<bf16_t*>(a.xg), nullptr, 0, nullptr, st));
+    MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
+  }
+  MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));
+  MOK_RUN("bwd_dwgu_gemm", mok_launch_bwd_dwgu(a, st));
+  if (r.T > 0) {
+    MOK_RUN("bwd_dx_gemm", mok_launch_bwd_dx(a, st));
+    MOK_RUN("reverse_dispatch", mok_launch_reverse_dispatch(a.dxrows, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
+                                        static_cast<bf16_t*>(dx), st));
+  }
+  return MOK_OK;
+}
+
+mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K, uint8_t* q,
+                              uint8_t* scales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_ERR_INVALID_ARG;
+  if (rows > 0 && (!src || !q || !scales)) return MOK_ERR_INVALID_ARG;
+  mok_status s = check_device();
+  if (s != MOK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN("mxfp8_quantize", mok_launch_mxfp8_quantize(static_cast<const bf16_t*>(src), rows, K, q,
+                                                      scales, st));
+  return MOK_OK;
+}
+
+mok_status mok_trace_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_tr.mu);
+  g_tr.on = on != 0;
+  return MOK_OK;
+}
+
+mok_status mok_trace_collect(mok_trace_stat* out, int32_t capacity, int32_t* n_out) {
+  if (capacity < 0 || (capacity > 0 && !out) || !n_out) return MOK_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> g(g_tr.mu);
+  std::vector<std::string> names;
+  std::vector<mok_trace_stat> stats;
+  mok_status st = MOK_OK;
+  for (const auto& rec : g_tr.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(rec.b) != hipSuccess || hipEventElapsedTime(&ms, rec.a, rec.b) != hipSuccess)
+      st = MOK_ERR_DEVICE;
+    size_t k = 0;
+    while (k < names.size() && names[k] != rec.name) ++k;
+    if (k == names.size()) {
+      names.emplace_back(rec.name);
+      mok_trace_stat z;
+      memset(&z, 0, sizeof z);
+      strncpy(z.name, rec.name, sizeof z.name - 1);
+      stats.push_back(z);
+    }
+    stats[k].launches += 1;
+    stats[k].total_ms += ms;
+    stats[k].max_ms = std::max(stats[k].max_ms, (double)ms);
+    g_tr.pool.push_back(rec.a);
+    g_tr.pool.push_back(rec.b);
+  }
+  g_tr.recs.clear();
+  *n_out = (int32_t)stats.size();
+  for (int32_t i = 0; i < capacity && i < (int32_t)stats.size(); ++i) out[i] = stats[i];
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Host-side launch entry points of the device kernels (internal to libmok).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mok_device.h"
+
+struct mok_sched_ptrs {
+  int32_t* status;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* dest;
+  int32_t* n_fwd_tiles;
+  mok_tile* fwd_tiles;
+  int32_t* mb_tile_start;
+  int32_t* n_bwd_tiles;
+  mok_tile* bwd_tiles;
+};
+
+// Row-tile sizes of the grouped GEMMs.
+constexpr int kTileRowsFwd = 128;
+constexpr int kTileRowsBwd = 128;
+
+hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E, int M,
+                               int bm_f, int bm_b, int n_mb, int max_f, int max_b, hipStream_t st);
+
+// Gather: for permuted rows p in [p_begin, p_begin + rows) that are valid
+// (p < offsets[E]), copy x[perm[p] / topk] to dst row (p - p_begin).
+// row_bytes = bytes per row (2H for bf16, H for E4M3 codes); if scales != NULL
+// the E8M0 rows (sbytes each) are gathered to dst_scales the same way.
+hipError_t mok_launch_gather(const void* x, const int32_t* perm, const int32_t* offsets_E,
+                             int topk, int64_t row_bytes, int64_t p_begin, int64_t rows,
+                             void* dst, const uint8_t* scales, int64_t sbytes,
+                             uint8_t* dst_scales, hipStream_t st);
+
+// y[t] = sum_j w[t][j] * obuf[t*k+j] (valid rows only), fp32, j ascending.
+hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t* dest,
+                              const int32_t* offsets_E, int64_t T, int topk, int64_t H,
+                              bf16_t* y, hipStream_t st);
+
+// dw[t][j] = <dy[t], obuf[t*k+j]>; dO[dest[t*k+j]] = bf16(w[t][j] * dy[t]).
+hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
+                                      const int32_t* dest, const int32_t* offsets_E, int64_t T,
+                                      int topk, int64_t H, float* dw, bf16_t* dO, hipStream_t st);
+
+// dx[t] = sum_j dxrows[t*k+j] (valid rows only), fp32, j ascending.
+hipError_t mok_launch_reverse_dispatch(const bf16_t* dxrows, const int32_t* dest,
+                                       const int32_t* offsets_E, int64_t T, int topk, int64_t H,
+                                       bf16_t* dx, hipStream_t st);
+
+hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K, uint8_t* q,
+                                     uint8_t* scales, hipStream_t st);
+
+hipError_t mok_launch_zero(void* p, int64_t bytes, hipStream_t st);
+
+// ---------------------------------------------------------------- grouped GEMMs
+struct mok_fwd_args {
+  // problem
+  int64_t T, H, I;
+  int E, topk, M, n_slots, n_mb;
+  // schedule
+  const int32_t* perm;
+  const mok_tile* tiles;
+  const int32_t* n_tiles;
+  const int32_t* mb_tile_start;
+  // weights
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const uint8_t* sg;
+  const uint8_t* su;
+  const uint8_t* sd;
+  // ring: slot s holds X rows at ring_x + s*M*xrow_bytes, h rows at ring_h + ...
+  uint8_t* ring_x;
+  uint8_t* ring_xs;      // MXFP8 scales of ring_x rows
+  uint8_t* ring_h;
+  uint8_t* ring_hs;      // MXFP8 scales of ring_h rows
+  // outputs
+  bf16_t* obuf;          // [R][H], flat row order
+  bf16_t* ab;            // [R][2I] saved pre-activations (NULL = none)
+};
+
+// gate/up GEMM + SwiGLU epilogue over the row tiles of minibatch m.
+hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+                             hipStream_t st);
+// down GEMM over the row tiles of minibatch m; writes obuf[perm[p]].
+hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+                           hipStream_t st);
+
+struct mok_bwd_args {
+  int64_t T, H, I;
+  int E, topk;
+  const int32_t* perm;
+  const int32_t* offsets;
+  const mok_tile* tiles;
+  const int32_t* n_tiles;
+  int max_tiles;
+  const bf16_t* wg;
+  const bf16_t* wu;
+  const bf16_t* wd;
+  const bf16_t* dO;      // [R][H] permuted
+  const bf16_t* ab;      // [R][2I] permuted (saved by forward)
+  const bf16_t* xg;      // [R][H] gathered x, permuted
+  bf16_t* dab;           // [R][2I] permuted: dA | dB
+  bf16_t* hb;            // [R][I] permuted: recomputed h
+  bf16_t* dxrows;        // [R][H] flat row order
+  bf16_t* dwg;
+  bf16_t* dwu;
+  bf16_t* dwd;
+};
+
+hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st);     // dh, SwiGLU bwd
+hipError_t mok_launch_bwd_dwd(const mok_bwd_args& a, hipStream_t st);    // dWd
+hipError_t mok_launch_bwd_dwgu(const mok_bwd_args& a, hipStream_t st);   // dWg, dWu
+hipError_t mok_launch_bwd_dx(const mok_bwd_args& a, hipStream_t st);     // dX rows

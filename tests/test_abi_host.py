@@ -1,0 +1,123 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/mok.h declares, sizes and layouts are consistent, and
+every argument error is caught on the host before anything touches a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_30_amd as mok
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mok.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mok_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(mok.EXPORTS), names
+    L = mok.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert mok.version() == 100
+    assert mok.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert mok.status_string(s) and mok.status_string(s) != "unknown status"
+    assert mok.status_string(7) == "unknown status"
+
+
+def P(T=256, H=256, I=512, E=8, k=2, dtype=0):
+    return mok.make_problem(T, H, I, E, k, dtype)
+
+
+def test_buffer_sizes_and_layout():
+    ws, sb, cb = mok.buffer_sizes(P())
+    R = 512
+    assert cb >= R * 2 * 256 + R * 4 * 512
+    assert ws >= R * 2 * 256 * 4          # backward keeps four [R][H]-sized buffers
+    L = mok.schedule_layout(P())
+    assert L.total == sb
+    offs = [L.status, L.counts, L.offsets, L.perm, L.dest, L.n_fwd_tiles, L.fwd_tiles,
+            L.mb_tile_start, L.n_bwd_tiles, L.bwd_tiles]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.perm - L.offsets >= 4 * 9 and L.dest - L.perm >= 4 * R
+    # default minibatch: round_up(ceil(4*256*H/I), 256) capped at R
+    assert L.minibatch_rows == 512 and L.n_minibatches == 1 and L.ring_slots == 1
+
+
+def test_default_minibatch_rule_large_shapes():
+    # T=16384, H=4096, I=1536: 4*256*4096/1536 = 2730.67 -> 2816 rows, 47 minibatches
+    L = mok.schedule_layout(mok.make_problem(16384, 4096, 1536, 128, 8))
+    assert L.minibatch_rows == 2816 and L.n_minibatches == 47 and L.ring_slots == 4
+    L = mok.schedule_layout(mok.make_problem(16384, 7168, 2048, 32, 4))
+    assert L.minibatch_rows == 3584 and L.n_minibatches == 19
+    L = mok.schedule_layout(mok.make_problem(4096, 2048, 768, 64, 8), mok.make_config(num_cus=128))
+    assert L.minibatch_rows == 1536
+    L = mok.schedule_layout(mok.make_problem(100, 256, 256, 4, 2),
+                            mok.make_config(minibatch_rows=64, ring_slots=9))
+    assert L.minibatch_rows == 64 and L.n_minibatches == 4 and L.ring_slots == 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), mok.MOK_ERR_INVALID_ARG),
+    (dict(k=0), mok.MOK_ERR_INVALID_ARG),
+    (dict(k=9), mok.MOK_ERR_INVALID_ARG),
+    (dict(E=0), mok.MOK_ERR_INVALID_ARG),
+    (dict(H=200), mok.MOK_ERR_UNSUPPORTED),
+    (dict(I=96), mok.MOK_ERR_UNSUPPORTED),
+    (dict(E=513, k=2), mok.MOK_ERR_UNSUPPORTED),
+    (dict(dtype=5), mok.MOK_ERR_INVALID_ARG),
+    (dict(T=1 << 29, k=8, E=8), mok.MOK_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_rejected(kw, status):
+    with pytest.raises(mok.MokError) as ei:
+        mok.buffer_sizes(P(**kw))
+    assert ei.value.status == status
+
+
+@pytest.mark.parametrize("cfg", [dict(minibatch_rows=-1), dict(ring_slots=-2),
+                                 dict(capacity_multiplier=0.5), dict(driver=3)])
+def test_invalid_configs_rejected(cfg):
+    with pytest.raises(mok.MokError) as ei:
+        mok.buffer_sizes(P(), mok.make_config(**cfg))
+    assert ei.value.status == mok.MOK_ERR_INVALID_ARG
+
+
+def test_calls_reject_bad_arguments_before_any_launch():
+    L = mok.lib()
+    prob = P()
+    _, sb, _ = mok.buffer_sizes(prob)
+    fake = ctypes.c_void_p(0x1000)
+    # null pointers
+    assert L.mok_build_schedule(ctypes.byref(prob), None, None, fake, sb, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_build_schedule(ctypes.byref(prob), None, fake, None, sb, None) == mok.MOK_ERR_INVALID_ARG
+    # schedule buffer too small
+    assert L.mok_build_schedule(ctypes.byref(prob), None, fake, fake, sb - 1, None) == mok.MOK_ERR_BUFFER_TOO_SMALL
+    w = mok.Weights(0x1000, 0x1000, 0x1000, None, None, None)
+    ws, _, _ = mok.buffer_sizes(prob)
+    assert L.mok_forward(ctypes.byref(prob), None, fake, fake, fake, ctypes.byref(w), fake, None,
+                         fake, ws - 1, None) == mok.MOK_ERR_BUFFER_TOO_SMALL
+    w0 = mok.Weights(0x1000, None, 0x1000, None, None, None)
+    assert L.mok_forward(ctypes.byref(prob), None, fake, fake, fake, ctypes.byref(w0), fake, None,
+                         fake, ws, None) == mok.MOK_ERR_INVALID_ARG
+    # MXFP8 forward needs scales; its backward is not provided
+    pm = P(dtype=mok.MOK_MXFP8)
+    wsm, _, cbm = mok.buffer_sizes(pm)
+    assert cbm == 0
+    assert L.mok_forward(ctypes.byref(pm), None, fake, fake, fake, ctypes.byref(w), fake, None,
+                         fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(w), fake,
+                          fake, fake, fake, fake, fake, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED
+    # quantize: K must be a multiple of 32
+    assert L.mok_mxfp8_quantize(fake, 4, 48, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_mxfp8_quantize(fake, -1, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_mxfp8_quantize(None, 4, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
