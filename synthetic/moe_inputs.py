@@ -72,8 +72,9 @@ CONFIGS = {
 }
 
 
-def problem(T, H, E, k, I, seed=0, zipf_s=0.0, empty_den=0, dtype="bf16", backward=False,
+def problem(T, H, I, E, k, seed=0, zipf_s=0.0, empty_den=0, dtype="bf16", backward=False,
             name=None) -> Problem:
+    """A workload of T tokens, hidden H, expert size I, E experts, top-k."""
     return Problem(name or f"T{T} H{H} E{E} k{k} I{I}", T, H, E, k, I, seed=seed,
                    zipf_s=zipf_s, empty_den=empty_den, dtype=dtype, backward=backward)
 

@@ -143,7 +143,7 @@ def test_invalid_expert_rows_contribute_zero():
 @pytest.mark.parametrize("seed", [0, 1])
 def test_generator_routing_weights_are_softmax(seed):
     from synthetic import make_routing, make_x, problem
-    p = problem(64, 32, 8, 2, 16, seed=seed)
+    p = problem(64, 32, 16, 8, 2, seed=seed)
     ids, w = make_routing(p, make_x(p))
     np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-6)
     assert np.all(w[:, 0] >= w[:, 1])    # picks come in descending score order
