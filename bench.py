@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="reference workload id (0-4)")
-    ap.add_argument("--cpu-tokens", type=int, default=1024,
+    ap.add_argument("--cpu-tokens", type=int, default=3072,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip)")
     ap.add_argument("--driver", type=int, default=0)
     ap.add_argument("--minibatch-rows", type=int, default=0)
