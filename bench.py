@@ -191,7 +191,8 @@ def main():
                    "E": p.E, "topk": p.k, "routed_rows": R, "minibatch_rows": ws.config.minibatch_rows
                    or mok.schedule_layout(ws.problem, ws.config).minibatch_rows,
                    "ring_slots": mok.schedule_layout(ws.problem, ws.config).ring_slots,
-                   "driver": "persistent" if args.driver == 0 else "launch-per-minibatch"},
+                   "driver": {0: "default (launch-per-minibatch)", 1: "launch-per-minibatch",
+                              2: "persistent"}[args.driver]},
         "tokens_per_s": round(p.T / (ms_step * 1e-3), 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,

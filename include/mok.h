@@ -80,17 +80,22 @@ typedef struct {
  * has no meaning on one GPU and is not present). Zero selects the default. */
 typedef struct {
   int32_t minibatch_rows;        /* M, routed rows per minibatch. Default:
-                                    [MoK clip] How-to item 3 asks for M >= 4*S*H/I
-                                    rows so each grouped GEMM fills two waves;
-                                    M = round_up(ceil(4*S*H/I), 256).            */
+                                    [MoK clip] How-to item 3 asks that each
+                                    grouped GEMM fill two waves (M >= 4*S*H/I for
+                                    its tiles); for this library's 256x256 tiles
+                                    that is M >= S*65536/I. Default
+                                    M = round_up(max(4*S*H/I, S*65536/I), 256),
+                                    capped at T*topk.                            */
   int32_t ring_slots;            /* N_s, slots of the ring token buffer (the
                                     "macrobatch" is N_s*M rows). Default 4,
                                     capped at the minibatch count.               */
   float capacity_multiplier;     /* accepted (0 or >= 1); on one GPU the exact
                                     row count T*topk is always used.              */
   int32_t num_cus;               /* S for the default M; 0 = 256 (MI355X).        */
-  int32_t driver;                /* 0 = persistent minibatch kernel (default),
-                                    1 = one launch per minibatch stage.           */
+  int32_t driver;                /* 0 = default (= 1), 1 = one launch per
+                                    minibatch stage (gather, gate/up, down),
+                                    2 = one persistent launch for all minibatches
+                                    (currently returns MOK_ERR_UNSUPPORTED).      */
 } mok_config;
 
 typedef struct {

@@ -25,6 +25,7 @@ struct Resolved {
   int64_t T, H, I, R;
   int E, k;
   bool mx;
+  int driver;
   int M, n_slots, n_mb;
   int max_fwd_tiles, max_bwd_tiles, max_tiles_mb;
 };
@@ -44,15 +45,23 @@ mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
   if (c) d = *c;
   if (d.minibatch_rows < 0 || d.ring_slots < 0 || d.num_cus < 0) return MOK_ERR_INVALID_ARG;
   if (!(d.capacity_multiplier == 0.0f || d.capacity_multiplier >= 1.0f)) return MOK_ERR_INVALID_ARG;
-  if (d.driver < 0 || d.driver > 1) return MOK_ERR_INVALID_ARG;
+  if (d.driver < 0 || d.driver > 2) return MOK_ERR_INVALID_ARG;
   r->T = p->T; r->H = p->H; r->I = p->I; r->R = R;
   r->E = p->E; r->k = p->topk; r->mx = p->dtype == MOK_MXFP8;
-  // [MoK clip] How-to item 3: minibatch rows M >= 4*S*H/I (two waves of the
-  // gate/up grouped GEMM); rounded up to a multiple of 256 rows.
+  r->driver = d.driver;
+  // [MoK clip] How-to item 3: size the minibatch so that each expert grouped
+  // GEMM fills at least two waves of the machine, written there as
+  // M >= 4*S*H/I for the pages' tiles. For this library's gate/up tiles
+  // (256 rows x 256 columns of the 2I-wide gate|up output, one workgroup per
+  // CU) two waves of S workgroups need M*2I/(256*256) >= 2*S, i.e.
+  // M >= S*65536/I. The default takes the larger of the two bounds, rounded up
+  // to a multiple of 256 rows.
   int64_t M = d.minibatch_rows;
   if (M == 0) {
     const int64_t S = d.num_cus ? d.num_cus : 256;
-    M = cdiv(cdiv(4 * S * p->H, p->I), 256) * 256;
+    const int64_t m_pages = cdiv(4 * S * p->H, p->I);
+    const int64_t m_tiles = cdiv(S * 65536, p->I);
+    M = cdiv(std::max(m_pages, m_tiles), 256) * 256;
   }
   if (M < 1) return MOK_ERR_INVALID_ARG;
   M = std::min<int64_t>(M, std::max<int64_t>(R, 1));
@@ -108,7 +117,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
 // Workspace carve-up. Forward and backward never run inside one call, so
 // they share the same bytes.
 struct FwdWs {
-  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
+  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, ctr, ctr_bytes, total;
 };
 struct BwdWs {
   size_t dO, dab, hb, dxrows, xg, total;
@@ -125,6 +134,10 @@ FwdWs fwd_ws(const Resolved& r) {
   w.obuf = o;    o = align_up(o + (size_t)r.R * 2 * r.H);
   w.xq = o;      o = align_up(o + (r.mx ? (size_t)r.T * r.H : 0));
   w.xqs = o;     o = align_up(o + (r.mx ? (size_t)r.T * (r.H / 32) : 0));
+  // persistent-driver counters: ticket, gather-done and down-done per
+  // minibatch, gate/up-done per forward row tile
+  w.ctr_bytes = (4 * (size_t)(1 + 2 * r.n_mb + r.max_fwd_tiles) + 15) / 16 * 16;
+  w.ctr = o;     o = align_up(o + w.ctr_bytes);
   w.total = o;
   return w;
 }
@@ -148,8 +161,11 @@ size_t ctx_bytes(const Resolved& r) {
   return align_up((size_t)r.R * 2 * r.H) + align_up((size_t)r.R * 4 * r.I);
 }
 
-// gfx950 check, once per device; queries device properties only.
-mok_status check_device() {
+// gfx950 check and compute-unit count, once per device (device properties
+// only; no device memory is touched).
+int g_cus[64] = {0};
+
+mok_status check_device(int* cus = nullptr) {
   static std::mutex mu;
   static int state[64] = {0};   // 0 unknown, 1 ok, 2 bad
   int dev = 0;
@@ -159,7 +175,9 @@ mok_status check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOK_ERR_DEVICE;
     state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev] = prop.multiProcessorCount;
   }
+  if (cus) *cus = g_cus[dev];
   return state[dev] == 1 ? MOK_OK : MOK_ERR_DEVICE;
 }
 
@@ -295,11 +313,14 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
   if (r.mx && fwd_ctx) return MOK_ERR_UNSUPPORTED;
+  // The persistent minibatch kernel (driver 2) is switched off: its first run
+  // on the device did not complete and the cause is not yet established.
+  if (r.driver == 2) return MOK_ERR_UNSUPPORTED;
   const FwdWs W = fwd_ws(r);
   if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
-  if ((s = check_device()) != MOK_OK) return s;
+  int cus = 0;
+  if ((s = check_device(&cus)) != MOK_OK) return s;
   if (r.T == 0) return MOK_OK;
-  if (r.mx) return MOK_ERR_UNSUPPORTED;   // MXFP8 GEMM path not built yet
   hipStream_t st = (hipStream_t)stream;
   const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -318,15 +339,30 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx : ws + W.obuf);
   a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + align_up((size_t)r.R * 2 * r.H)) : nullptr;
 
-  const int64_t xrow = 2 * r.H;
-  for (int m = 0; m < r.n_mb; ++m) {
-    const int64_t p0 = (int64_t)m * r.M;
-    const int64_t rows = std::min<int64_t>(r.M, r.R - p0);
-    uint8_t* slot = a.ring_x + (size_t)(m % r.n_slots) * r.M * xrow;
-    MOK_RUN("gather", mok_launch_gather(x, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows, slot,
-                                        nullptr, 0, nullptr, st));
-    MOK_RUN("gateup_gemm", mok_launch_gateup(a, m, r.max_tiles_mb, false, st));
-    MOK_RUN("down_gemm", mok_launch_down(a, m, r.max_tiles_mb, false, st));
+  // MXFP8: x is quantized once per token (blocks lie inside a row, so this is
+  // bitwise the same as quantizing each gathered row), then fp8 rows and their
+  // scale rows are gathered like bf16 rows.
+  const void* xsrc = x;
+  const uint8_t* xscales = nullptr;
+  const int64_t xrow = r.mx ? r.H : 2 * r.H;
+  const int64_t srow = r.H / 32;
+  if (r.mx) {
+    MOK_RUN("mxfp8_quantize_x", mok_launch_mxfp8_quantize(static_cast<const bf16_t*>(x), r.T, r.H,
+                                                          ws + W.xq, ws + W.xqs, st));
+    xsrc = ws + W.xq;
+    xscales = ws + W.xqs;
+  }
+  {
+    for (int m = 0; m < r.n_mb; ++m) {
+      const int64_t p0 = (int64_t)m * r.M;
+      const int64_t rows = std::min<int64_t>(r.M, r.R - p0);
+      const size_t slot_row = (size_t)(m % r.n_slots) * r.M;
+      MOK_RUN("gather", mok_launch_gather(xsrc, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows,
+                                          a.ring_x + slot_row * xrow, xscales, srow,
+                                          r.mx ? a.ring_xs + slot_row * srow : nullptr, st));
+      MOK_RUN("gateup_gemm", mok_launch_gateup(a, m, r.max_tiles_mb, r.mx, st));
+      MOK_RUN("down_gemm", mok_launch_down(a, m, r.max_tiles_mb, r.mx, st));
+    }
   }
   MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
                              static_cast<bf16_t*>(y), st));

@@ -19,8 +19,8 @@ struct mok_sched_ptrs {
 };
 
 // Row-tile sizes of the grouped GEMMs.
-constexpr int kTileRowsFwd = 128;
-constexpr int kTileRowsBwd = 128;
+constexpr int kTileRowsFwd = 256;
+constexpr int kTileRowsBwd = 256;
 
 hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E, int M,
                                int bm_f, int bm_b, int n_mb, int max_f, int max_b, hipStream_t st);
@@ -87,6 +87,12 @@ hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, boo
 // down GEMM over the row tiles of minibatch m; writes obuf[perm[p]].
 hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
                            hipStream_t st);
+
+// Persistent forward: gather + gate/up + down of every minibatch in one
+// launch; counters = 1 + 2*n_mb + max_fwd_tiles ints, zeroed beforehand.
+hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, int* counters, int32_t* status,
+                                     const void* xsrc, const uint8_t* xscales,
+                                     const int32_t* offsets_E, int grid, bool mxfp8, hipStream_t st);
 
 struct mok_bwd_args {
   int64_t T, H, I;

@@ -50,18 +50,22 @@ def test_buffer_sizes_and_layout():
             L.mb_tile_start, L.n_bwd_tiles, L.bwd_tiles]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L.perm - L.offsets >= 4 * 9 and L.dest - L.perm >= 4 * R
-    # default minibatch: round_up(ceil(4*256*H/I), 256) capped at R
+    # default minibatch: round_up(max(4*S*H/I, S*65536/I), 256) capped at R
     assert L.minibatch_rows == 512 and L.n_minibatches == 1 and L.ring_slots == 1
 
 
 def test_default_minibatch_rule_large_shapes():
-    # T=16384, H=4096, I=1536: 4*256*4096/1536 = 2730.67 -> 2816 rows, 47 minibatches
+    # T=16384, H=4096, I=1536: 4*256*4096/1536 = 2731 (pages' form) and
+    # 256*65536/1536 = 10923 (two waves of 256x256 gate|up tiles) -> 11008 rows
     L = mok.schedule_layout(mok.make_problem(16384, 4096, 1536, 128, 8))
-    assert L.minibatch_rows == 2816 and L.n_minibatches == 47 and L.ring_slots == 4
-    L = mok.schedule_layout(mok.make_problem(16384, 7168, 2048, 32, 4))
-    assert L.minibatch_rows == 3584 and L.n_minibatches == 19
+    assert L.minibatch_rows == 11008 and L.n_minibatches == 12 and L.ring_slots == 4
+    L = mok.schedule_layout(mok.make_problem(16384, 7168, 2048, 32, 4))   # max(3584, 8192)
+    assert L.minibatch_rows == 8192 and L.n_minibatches == 8
     L = mok.schedule_layout(mok.make_problem(4096, 2048, 768, 64, 8), mok.make_config(num_cus=128))
-    assert L.minibatch_rows == 1536
+    assert L.minibatch_rows == 11008                                      # max(1366, 10923)
+    # the pages' bound 4*S*H/I wins once H > 16384
+    L = mok.schedule_layout(mok.make_problem(65536, 32768, 256, 8, 1), mok.make_config(num_cus=16))
+    assert L.minibatch_rows == 8192                                        # max(8192, 4096)
     L = mok.schedule_layout(mok.make_problem(100, 256, 256, 4, 2),
                             mok.make_config(minibatch_rows=64, ring_slots=9))
     assert L.minibatch_rows == 64 and L.n_minibatches == 4 and L.ring_slots == 4
@@ -117,6 +121,9 @@ def test_calls_reject_bad_arguments_before_any_launch():
                          fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(w), fake,
                           fake, fake, fake, fake, fake, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED
+    # the persistent minibatch driver is switched off
+    assert L.mok_forward(ctypes.byref(prob), ctypes.byref(mok.make_config(driver=2)), fake, fake,
+                         fake, ctypes.byref(w), fake, None, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED
     # quantize: K must be a multiple of 32
     assert L.mok_mxfp8_quantize(fake, 4, 48, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_mxfp8_quantize(fake, -1, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG

@@ -64,3 +64,64 @@ def test_quantize_bit_exact_special_values():
 def test_quantize_empty_rows():
     q, s = gpu_quantize(np.zeros((0, 64), np.uint16))
     assert q.shape == (0, 64)
+
+
+# ------------------------------------------------------------------ MXFP8 forward
+def gpu_mx_forward(p, d, **cfg):
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=False, **cfg)
+    qw = F.quantize_weights(*d["weights"])
+    F.run_schedule(ws, d["ids"])
+    y = F.run_forward(ws, d["x"], d["w"], qw)
+    torch.cuda.synchronize()
+    return y, qw
+
+
+SMALL_MX = [problem(37, 256, 256, 5, 2, seed=51), problem(300, 512, 384, 16, 4, seed=52)]
+
+
+@pytest.mark.parametrize("p", SMALL_MX, ids=lambda p: p.name)
+@pytest.mark.parametrize("cfg", [dict(), dict(minibatch_rows=64, ring_slots=2)], ids=["default", "M64-ring2"])
+def test_mxfp8_forward_small(p, cfg):
+    from test_gpu_forward import device_inputs, host_inputs
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    d = device_inputs(p)
+    y, qw = gpu_mx_forward(p, d, **cfg)
+    # the library's weight quantization equals the oracle's, bit for bit
+    rq, rs = oracle.mxfp8_quantize(f64(wg[0]))
+    np.testing.assert_array_equal(qw[0][0].cpu().numpy(), rq)
+    np.testing.assert_array_equal(qw[3][0].cpu().numpy(), rs)
+    ref, _ = oracle.forward_mxfp8(f64(x), ids, w.astype(np.float64), ExpertsF64(wg, wu, wd))
+    got = from_dev_bf16(y)
+    assert np.all(np.isfinite(got))
+    r = rel_fro(got, ref)
+    assert r <= REL_FRO_MXFP8, f"relative Frobenius error {r:.3e}"
+
+
+@pytest.mark.timeout(900)
+def test_mxfp8_forward_full_size_sampled():
+    """T=16384, H=4096, E=128, top-8, I=1536, Zipf(1.2) routing, MXFP8."""
+    from test_gpu_forward import device_inputs, host_inputs, sampled_tokens
+    p = CONFIGS[3]
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    d = device_inputs(p)
+    y, _ = gpu_mx_forward(p, d)
+    toks = sampled_tokens(p.T, 16, 3)
+    ref, _ = oracle.forward_mxfp8_tokens(f64(x[toks]), ids[toks], w[toks].astype(np.float64),
+                                         ExpertsF64(wg, wu, wd))
+    got = from_dev_bf16(y)[toks]
+    r = rel_fro(got, ref)
+    assert r <= REL_FRO_MXFP8, f"relative Frobenius error {r:.3e}"
+
+
+def test_mxfp8_forward_bitwise_deterministic():
+    import torch
+    from test_gpu_forward import device_inputs
+    p = problem(1024, 512, 256, 16, 4, seed=53)
+    d = device_inputs(p)
+    y0, _ = gpu_mx_forward(p, d)
+    for _ in range(4):
+        y, _ = gpu_mx_forward(p, d)
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
