@@ -44,15 +44,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="reference workload id (0-4)")
-    ap.add_argument("--cpu-tokens", type=int, default=3072,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-reps", type=int, default=4,
+                    help="repetitions of the CPU-baseline sample (best is reported)")
     ap.add_argument("--driver", type=int, default=0)
     ap.add_argument("--minibatch-rows", type=int, default=0)
     ap.add_argument("--ring-slots", type=int, default=0)
     return ap.parse_args()
 
 
-def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok):
+def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok, reps=1):
     """The fp64 oracle (as it stands) on the first n_tok tokens of the same
     workload: forward + backward, reported in the same unit."""
     import numpy as np
@@ -73,12 +75,16 @@ def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok):
 
     xs = bf16_to_f32(x[:n_tok]).astype(np.float64)
     dys = bf16_to_f32(dy[:n_tok]).astype(np.float64)
-    t0 = time.perf_counter()
-    oracle.backward(xs, ids[:n_tok], w[:n_tok].astype(np.float64), Ex(), dys)   # runs forward too
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(max(1, reps)):
+        t0 = time.perf_counter()
+        oracle.backward(xs, ids[:n_tok], w[:n_tok].astype(np.float64), Ex(), dys)   # runs forward too
+        times.append(time.perf_counter() - t0)
+    dt = min(times)
     flops = 18.0 * n_tok * p.k * p.H * p.I
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n_tok} of {p.T} tokens (forward+backward, fp64 NumPy), {dt:.1f} s",
+            "sample": f"first {n_tok} of {p.T} tokens, forward+backward in fp64 NumPy, best of "
+                      f"{len(times)} runs ({sum(times):.1f} s of CPU work in total)",
             "seconds": dt}
 
 
@@ -155,6 +161,23 @@ def main():
     log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
     ms_fwd, fstats = timed(fwd_only, args.steps, trace=True)
 
+    # MXFP8 forward on the same workload: weights pre-quantized once (outside
+    # the timed region), x quantized on the fly inside mok_forward.
+    log("[bench] MXFP8 forward timing")
+    wsm = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=False, **cfg)
+    qweights = F.quantize_weights(*weights)
+    ymx = torch.empty_like(dx_)
+
+    def fwd_mx():
+        mok.build_schedule(wsm.problem, dids, wsm.schedule, wsm.config, stream)
+        mok.forward(wsm.problem, wsm.schedule, dx_, dw_, qweights, ymx, wsm.workspace, None,
+                    wsm.config, stream)
+
+    for _ in range(2):
+        fwd_mx()
+    ms_mx, mxstats = timed(fwd_mx, args.steps, trace=True)
+    del wsm
+
     R, H, I = p.R, p.H, p.I
     flops_step = p.fwd_flops() + p.bwd_flops()
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -202,10 +225,18 @@ def main():
                     "tokens_per_s": round(p.T / (ms_fwd * 1e-3), 1)},
         "kernels": kernels,
         "roofline": roofline,
+        "mxfp8_forward": {
+            "ms": round(ms_mx, 4), "tflops": round(fwd_flops / (ms_mx * 1e-3) / 1e12, 2),
+            "pct_fp8_peak": round(100 * fwd_flops / (ms_mx * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+            "tokens_per_s": round(p.T / (ms_mx * 1e-3), 1),
+            "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
+                            for k, v in mxstats.items() if k in GEMM_FLOPS_PER_ROW},
+        },
     }
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(p, x, ids, w, wg, wu, wd, dy, min(args.cpu_tokens, p.T))
+        out["cpu_baseline"] = cpu_baseline(p, x, ids, w, wg, wu, wd, dy, min(args.cpu_tokens, p.T),
+                                           args.cpu_reps)
     print(json.dumps(out), flush=True)
 
 

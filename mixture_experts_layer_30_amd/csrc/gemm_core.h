@@ -1,13 +1,24 @@
 // Tile machinery shared by the grouped-GEMM kernels (gfx950 matrix cores).
 //
 // A workgroup of 256 threads (4 wavefronts in a WM x WN grid) computes a
-// BM x BN tile of C = A . B^T, where row m of A and row n of B are read as K
-// vectors. K advances in stages of 128 bytes per row (64 bf16 or 128 fp8),
-// double-buffered through LDS. Each LDS tile is [rows][128 B]; its 16-byte
-// chunks are XOR-swizzled with (row ^ row >> 3) & 7, which keeps three access
-// patterns free of bank conflicts: 8 lanes writing the 8 chunks of one row
-// (row loader), 8 lanes writing one chunk of rows 8 apart (transposing
-// loader), and 8 consecutive rows read by the MFMA lanes.
+// BM x BN tile of C = A . B^T over K. K advances in stages of 64 bytes per
+// operand row (32 bf16 or 64 fp8) through a ring of 4 LDS buffers; every
+// operand reaches LDS by direct global->LDS copies (global_load_lds), up to 3
+// stages ahead of the MFMAs that read it.
+//
+// Two LDS tile layouts, both 16 KiB per stage for 256 rows or columns:
+//  * K-contiguous operands (row r = K vector in memory): [256 rows][64 B].
+//    LDS reads of 16 bytes serve 8 lanes per bank half; conflict-free when,
+//    in every group of 8 lanes, address bit 7 equals lane bit 3 and the
+//    16-byte slots (address bits 4-6) differ (measured on gfx950: 64 banks,
+//    256 bytes per clock). MFMA lanes 0-31 read 32 consecutive rows, so row
+//    r is stored at physical row swap13(r) (row bits 1 and 3 exchanged) and
+//    its 16-byte chunk c at c ^ ((r >> 1) & 3).
+//  * K-outer operands (element (k, n) at k*ld + n in memory): [32 k][512 B],
+//    16-byte chunk c of k-row k stored at c ^ ((k & 3) << 2). Fragments are
+//    read with ds_read_b64_tr_b16, which hands a 16-lane group the transpose
+//    of the 4 x 16 block its lanes address (lane 4q + p addresses k-row q,
+//    columns 4p .. 4p+3; lane i receives column i, k-rows 0 .. 3).
 //
 // bf16: v_mfma_f32_32x32x16_bf16; lane l supplies row l%32, K elements
 //       8*(l/32) .. +8 of a 16-wide K step.
@@ -18,15 +29,61 @@
 // Accumulator element q of a 32x32 fragment sits at row 8*(q/4) + 4*(l/32) +
 // q%4, column l%32.
 #pragma once
+#include <type_traits>
+
 #include "mok_device.h"
 
 namespace mok {
 
 constexpr int kThreads = 256;
-constexpr int kStage = 128;                       // K bytes per row per stage
+constexpr int kStage = 64;                        // K bytes per row per stage
+constexpr int kNbuf = 4;                          // LDS ring depth
 
-MOK_DEV int swz_chunk(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
-MOK_DEV int lds_at(int row, int chunk) { return row * kStage + (swz_chunk(row, chunk) << 4); }
+MOK_DEV int swap13(int r) { return (r & ~0xA) | ((r >> 2) & 2) | ((r << 2) & 8); }
+// byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile
+MOK_DEV int lds_at(int row, int chunk) { return swap13(row) * kStage + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// byte offset of byte `byte` of k-row k in a K-outer tile
+MOK_DEV int lds_ko(int k, int byte) { return k * 512 + ((((byte >> 4) ^ ((k & 3) << 2))) << 4) + (byte & 15); }
+
+typedef const __attribute__((address_space(3))) uint8_t* lds_cptr;
+typedef __attribute__((ext_vector_type(4))) short v4i16_t;
+
+// 512 zero bytes: the source of K-outer rows past the end of K.
+__device__ __attribute__((aligned(16))) uint8_t kZeroRow[512];
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding and all of its LDS operations are done (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+MOK_DEV void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Direct copy of 16 (or 4) bytes per lane from global memory into LDS:
+// lane l's bytes land at LDS byte address lds + 16*l (4*l). Written as inline
+// assembly so that the compiler does not track these LDS writes: its
+// conservative tracking would add a full vmcnt wait before LDS reads that it
+// cannot prove disjoint from every copy in flight, draining the copy
+// pipeline. The main loop orders copies and reads with explicit waits and
+// barriers instead. The compiler does not count these operations in its own
+// vmcnt bookkeeping either; that only makes its waits for ordinary loads
+// stricter, never weaker.
+MOK_DEV void copy16_to_lds(const void* g, const uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_cptr)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(m0) : "memory");
+}
+MOK_DEV void copy4_to_lds(const void* g, const uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_cptr)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads: a workgroup-
+// scope release there waits for every outstanding global->LDS copy, which
+// would drain the copy pipeline at each stage. Callers issue the waits that
+// make their own LDS writes visible (wait_vm_lds) first; the memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+MOK_DEV void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------------ row sources
 // Byte address of element k = 0 of operand row r (rows past the end clamp).
@@ -39,147 +96,118 @@ struct RowsStrided {
 
 // gate/up B operand: LDS rows come in 32-row groups alternating Wg and Wu, so
 // that a wavefront column holds gate and up of the same 32 h-columns.
+// (The Wg/Wu choice is address arithmetic, not a select between two fields:
+// a select of field addresses keeps the loader object in scratch memory.)
 struct RowsGateUp {
-  const uint8_t* wg;
-  const uint8_t* wu;
+  uintptr_t wg;            // address of Wg row 0
+  intptr_t du;             // Wu address minus Wg address
   int64_t stride;
   int n0;                  // first h column of the tile
   int ncols;               // I
+  MOK_DEV RowsGateUp(const uint8_t* g, const uint8_t* u, int64_t stride_, int n0_, int ncols_)
+      : wg((uintptr_t)g), du((intptr_t)((uintptr_t)u - (uintptr_t)g)), stride(stride_), n0(n0_),
+        ncols(ncols_) {}
   MOK_DEV const uint8_t* row(int r) const {
     const int col = min(n0 + (r >> 6) * 32 + (r & 31), ncols - 1);
-    return (((r >> 5) & 1) ? wu : wg) + (int64_t)col * stride;
+    return reinterpret_cast<const uint8_t*>(wg + (intptr_t)((r >> 5) & 1) * du + (int64_t)col * stride);
   }
 };
 
 // ------------------------------------------------------------------ loaders
-// K-contiguous operand: R rows x 8 chunks, R*8/256 chunks per thread.
-template <int R, class Rows>
-struct LoadK {
-  static constexpr int N = R * 8 / kThreads;
-  Rows src;
-  uint4 v[N];
-  MOK_DEV static int my_row(int q) { return (int)(threadIdx.x >> 3) + 32 * q; }
-  MOK_DEV void fetch(int kt) {
-    const int off = kt * kStage + (threadIdx.x & 7) * 16;
-#pragma unroll
-    for (int q = 0; q < N; ++q) v[q] = *reinterpret_cast<const uint4*>(src.row(my_row(q)) + off);
-  }
-  MOK_DEV void put(uint8_t* t) const {
-    const int c = threadIdx.x & 7;
-#pragma unroll
-    for (int q = 0; q < N; ++q) *reinterpret_cast<uint4*>(t + lds_at(my_row(q), c)) = v[q];
-  }
-  MOK_DEV void begin(int kt, uint8_t*) { fetch(kt); }
-  MOK_DEV void end(uint8_t* t) const { put(t); }
-};
+// Every loader moves its operand with kDma direct copies per wavefront per
+// stage (dma(kt, t): stage kt into LDS tile t) and supplies this lane's MFMA
+// fragment of 32 rows/columns starting at r0 for a 16-wide bf16 K step kk
+// (frag). Every wavefront issues exactly kDma copies per stage (positions
+// past the end are clamped, never skipped), which the main loop's vmcnt
+// accounting relies on.
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// K-contiguous operand copied straight from global memory into LDS
-// (global_load_lds_dwordx4: lane l of an instruction fills bytes 16*l .. +16
-// of a 1 KiB LDS window = 8 tile rows). Each lane fetches the global chunk
-// that the swizzle places at its LDS position, so no registers are used.
+// K-contiguous operand. One copy instruction fills a 1 KiB window (16
+// physical rows); lane l writes bytes 16*l .. +16 of it, so each lane fetches
+// the global chunk that the layout places at its LDS position.
 template <int R, class Rows>
 struct LoadKD {
+  static constexpr int kDma = R / 64;
+  static constexpr int kReads = 1;               // LDS reads per fragment
   Rows src;
-  MOK_DEV void begin(int kt, uint8_t* t) {
+  MOK_DEV void dma(int kt, uint8_t* t) const {
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
 #pragma unroll
-    for (int q = 0; q < R / 32; ++q) {
-      const int g = w + 4 * q;                   // 1 KiB window = rows 8g .. 8g+7
-      const int row = 8 * g + (l >> 3);
-      const int lc = swz_chunk(row, l & 7);      // logical chunk stored at physical chunk l&7
+    for (int q = 0; q < kDma; ++q) {
+      const int g = w + 4 * q;                   // window g = physical rows 16g .. 16g+15
+      const int row = swap13(16 * g + (l >> 2)); // logical row stored there
+      const int lc = (l & 3) ^ ((row >> 1) & 3); // logical chunk at physical chunk l&3
       const uint8_t* gp = src.row(row) + kt * kStage + lc * 16;
-      __builtin_amdgcn_global_load_lds(gp, (lds_void_ptr)(t + g * 1024), 16, 0, 0);
+      copy16_to_lds(gp, t + g * 1024);
     }
   }
-  MOK_DEV void end(uint8_t*) const {}
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int kk) {
+    const int l = lane_id();
+    return *reinterpret_cast<const bf16x8_t*>(t + lds_at(r0 + (l & 31), 2 * kk + (l >> 5)));
+  }
 };
 
-// K-outer bf16 operand: element (m, k) at base + k*ld + m (elements). The tile
-// has R rows (m) and 64 k. Each thread loads KR = R/32 k-rows of 8 consecutive
-// m and writes them transposed (8 rows of KR k each).
+// K-outer bf16 operand: element (k, n) at src0 + k*ld + 2n bytes for k <
+// ksplit and src1 + (k - ksplit)*ld + 2n beyond; k-rows >= K read as zero,
+// columns past ncols are clamped (their products land in unstored output).
+// A stage is 32 k-rows of 256 columns; one copy fills 2 k-rows.
 template <int R>
-struct LoadT {
-  static constexpr int KR = R / 32;
-  static constexpr int MC = R / 8;               // m chunks
-  const bf16_t* base0;                           // k < ksplit
-  const bf16_t* base1;                           // k >= ksplit
+struct LoadKO {
+  static_assert(R == 256, "K-outer tiles have 256 columns");
+  static constexpr int kDma = 4;
+  static constexpr int kReads = 2;               // LDS reads per fragment
+  const uint8_t* src0;
+  const uint8_t* src1;
   int ksplit;
-  int64_t ld;
-  int K;                                         // k >= K reads as zero
-  int mlimit;                                    // m >= mlimit reads as zero
-  uint4 v[KR];
-  MOK_DEV void fetch(int kt) {
-    const int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
-    const bool mok = 8 * mc < mlimit;
+  int64_t ld;              // bytes between k-rows
+  int K;
+  int ncols;               // valid columns (multiple of 8, >= 8)
+  MOK_DEV void dma(int kt, uint8_t* t) const {
+    const int w = (int)(threadIdx.x >> 6), l = lane_id();
 #pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const int k = kt * 64 + kg * KR + i;
-      if (k < K && mok) {
-        const bf16_t* b = k < ksplit ? base0 : base1;
-        v[i] = *reinterpret_cast<const uint4*>(b + (int64_t)k * ld + 8 * mc);
-      } else {
-        v[i] = make_uint4(0, 0, 0, 0);
-      }
+    for (int q = 0; q < kDma; ++q) {
+      const int g = w + 4 * q;                   // window g = k-rows 2g, 2g+1
+      const int kl = 2 * g + (l >> 5);
+      const int c = (l & 31) ^ ((kl & 3) << 2);  // logical chunk at physical chunk l&31
+      const int k = kt * 32 + kl;
+      const int cc = min(c, (ncols >> 3) - 1);
+      const uint8_t* gp = k >= K ? kZeroRow + c * 16
+                        : (k < ksplit ? src0 + (int64_t)k * ld : src1 + (int64_t)(k - ksplit) * ld) + cc * 16;
+      copy16_to_lds(gp, t + g * 1024);
     }
   }
-  MOK_DEV void put(uint8_t* t) const {
-    const int mc = threadIdx.x % MC, kg = threadIdx.x / MC;
-    uint32_t w[KR][4];
-#pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      w[i][0] = v[i].x; w[i][1] = v[i].y; w[i][2] = v[i].z; w[i][3] = v[i].w;
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t o[KR / 2];
-#pragma unroll
-      for (int i = 0; i < KR / 2; ++i) o[i] = __builtin_amdgcn_perm(w[2 * i + 1][m >> 1], w[2 * i][m >> 1], sel);
-      const int r = 8 * mc + m;
-      // this thread's KR k values are bytes [kg*KR*2, +KR*2) of the row
-      uint8_t* dst = t + lds_at(r, (kg * KR * 2) >> 4) + ((kg * KR * 2) & 15);
-      if constexpr (KR == 8) {
-        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-      } else {
-        static_assert(KR == 4, "LoadT supports 128 or 256 rows");
-        *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
-      }
-    }
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int kk) {
+    const int l = lane_id(), g = l >> 4, L = l & 15;
+    const int n = r0 + 16 * (g & 1) + 4 * (L & 3);
+    const int k = 16 * kk + 8 * (g >> 1) + (L >> 2);
+    typedef __attribute__((address_space(3))) v4i16_t* lds_v4_ptr;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k, 2 * n)));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k + 4, 2 * n)));
+    const v4i16_t x = lo, y = hi;
+    typedef __attribute__((ext_vector_type(8))) short v8i16_t;
+    const v8i16_t v = v8i16_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
   }
-  MOK_DEV void begin(int kt, uint8_t*) { fetch(kt); }
-  MOK_DEV void end(uint8_t* t) const { put(t); }
 };
 
-// E8M0 scales of an fp8 operand: 4 bytes (blocks) per row per stage.
-template <int R>
-struct LoadScales {
-  const uint8_t* base;     // scale bytes of row 0, block 0
-  int64_t stride;          // bytes between rows
-  int nrows;
-  bool gateup;             // rows follow the RowsGateUp interleave
-  const uint8_t* base_u;
-  int n0, ncols;
-  uint32_t v;
-  MOK_DEV void fetch(int kt) {
-    const int r = threadIdx.x;
-    if (r < R) {
-      const uint8_t* p;
-      if (gateup) {
-        const int col = min(n0 + (r >> 6) * 32 + (r & 31), ncols - 1);
-        p = (((r >> 5) & 1) ? base_u : base) + (int64_t)col * stride;
-      } else {
-        p = base + (int64_t)min(r, nrows - 1) * stride;
-      }
-      v = *reinterpret_cast<const uint32_t*>(p + kt * 4);
-    }
+// E8M0 block scales of a 256-row fp8 operand, copied into LDS as one 32-bit
+// word per row holding the scales of K blocks 4j .. 4j+3 (stages 2j and
+// 2j+1; K is a multiple of 128, so the word never runs past the row). Lane l
+// of wavefront w copies the word of row 64w + l.
+template <int R, class Rows>
+struct LoadScalesD {
+  static_assert(R == 256, "scale tiles have 256 rows");
+  static constexpr int kDma = 1;
+  Rows src;                                      // byte address of each row's scale 0
+  MOK_DEV void dma(int kt, uint8_t* t) const {
+    const int w = (int)(threadIdx.x >> 6), l = lane_id();
+    const uint8_t* gp = src.row(64 * w + l) + (kt >> 1) * 4;
+    copy4_to_lds(gp, t + 256 * w);
   }
-  MOK_DEV void put(uint32_t* t) const {
-    if ((int)threadIdx.x < R) t[threadIdx.x] = v;
-  }
-  MOK_DEV void begin(int kt, uint32_t*) { fetch(kt); }
-  MOK_DEV void end(uint32_t* t) const { put(t); }
+};
+
+struct NoScales {
+  static constexpr int kDma = 0;
+  MOK_DEV void dma(int, uint8_t*) const {}
 };
 
 // ------------------------------------------------------------------ accumulators
@@ -214,138 +242,247 @@ struct Geo {
 
 template <class G>
 struct Smem {
-  uint8_t a[2][G::BM * kStage];
-  uint8_t b[2][G::BN * kStage];
-  uint32_t sa[2][G::BM];
-  uint32_t sb[2][G::BN];
+  uint8_t a[kNbuf][G::BM * kStage];
+  uint8_t b[kNbuf][G::BN * kStage];
+  uint32_t sa[kNbuf][G::BM];
+  uint32_t sb[kNbuf][G::BN];
 };
 
-// One stage of MFMAs from LDS.
-template <class G, bool F8>
-MOK_DEV void mma_stage(const uint8_t* ta, const uint8_t* tb, const uint32_t* sa,
-                       const uint32_t* sb, Acc<G::FM, G::FN>& acc) {
-  const int lane = lane_id(), lr = lane & 31, lk = lane >> 5;
+// ------------------------------------------------------------------ fragments
+// bf16: fragments of one 16-wide K step (kk = 0, 1 within a stage).
+template <class G>
+struct FragsB16 {
+  bf16x8_t a[G::FM], b[G::FN];
+};
+
+template <class G, class LA, class LB>
+MOK_DEV void read_b16(const uint8_t* ta, const uint8_t* tb, int kk, FragsB16<G>& f) {
   const int r0 = G::wm() * G::WTM, c0 = G::wn() * G::WTN;
-  if constexpr (!F8) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t a[G::FM], b[G::FN];
+  for (int i = 0; i < G::FM; ++i) f.a[i] = LA::frag(ta, r0 + i * 32, kk);
 #pragma unroll
-      for (int i = 0; i < G::FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(ta + lds_at(r0 + i * 32 + lr, 2 * kk + lk));
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(tb + lds_at(c0 + j * 32 + lr, 2 * kk + lk));
-#pragma unroll
-      for (int i = 0; i < G::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);   // keep one K step's fragments live at a time
-    }
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      i32x8_t b[G::FN];
-      int bs[G::FN];
-#pragma unroll
-      for (int j = 0; j < G::FN; ++j) {
-        const int r = c0 + j * 32 + lr;
-        const uint4 lo = *reinterpret_cast<const uint4*>(tb + lds_at(r, 4 * kk + lk));
-        const uint4 hi = *reinterpret_cast<const uint4*>(tb + lds_at(r, 4 * kk + 2 + lk));
-        b[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bs[j] = (int)((sb[r] >> (8 * (2 * kk + lk))) & 0xFFu);
-      }
-#pragma unroll
-      for (int i = 0; i < G::FM; ++i) {
-        const int r = r0 + i * 32 + lr;
-        const uint4 lo = *reinterpret_cast<const uint4*>(ta + lds_at(r, 4 * kk + lk));
-        const uint4 hi = *reinterpret_cast<const uint4*>(ta + lds_at(r, 4 * kk + 2 + lk));
-        const i32x8_t a = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const int as = (int)((sa[r] >> (8 * (2 * kk + lk))) & 0xFFu);
-#pragma unroll
-        for (int j = 0; j < G::FN; ++j)
-          acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], acc.c[i][j], 0, 0, 0,
-                                                                        as, 0, bs[j]);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // keep one K step's fragments live at a time
-    }
-  }
+  for (int j = 0; j < G::FN; ++j) f.b[j] = LB::frag(tb, c0 + j * 32, kk);
 }
 
-struct NoScales {
-  MOK_DEV void begin(int, uint32_t*) {}
-  MOK_DEV void end(uint32_t*) const {}
+// LDS read instructions per fragment, averaged over the two operands
+template <class LA, class LB>
+struct RdPerFrag {
+  static constexpr int kAvg = (LA::kReads + LB::kReads + 1) / 2;
 };
 
-// Wait for this thread's outstanding global->LDS copies and global loads.
-MOK_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <class G>
+MOK_DEV void mfma_b16(const FragsB16<G>& f, Acc<G::FM, G::FN>& acc) {
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+}
 
-// Double-buffered main loop over nk stages. Loaders start stage kt+1 (direct
-// copies into the idle LDS buffer, or loads into registers) before the MFMAs
-// of stage kt and finish it (register loaders write LDS) after them.
+// fp8: the fragments of one whole stage (one 64-wide scaled K step) and the
+// scale words of their rows.
+template <class G>
+struct FragsF8 {
+  i32x8_t a[G::FM], b[G::FN];
+  uint32_t as[G::FM], bs[G::FN];
+};
+
+MOK_DEV i32x8_t cat8(const bf16x8_t& lo8, const bf16x8_t& hi8) {
+  const i32x4_t lo = __builtin_bit_cast(i32x4_t, lo8), hi = __builtin_bit_cast(i32x4_t, hi8);
+  return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <class G>
+MOK_DEV void read_f8_a(const uint8_t* ta, const uint32_t* sa, int i, FragsF8<G>& f) {
+  const int lane = lane_id(), lr = lane & 31, lk = lane >> 5;
+  const int r = G::wm() * G::WTM + i * 32 + lr;
+  f.a[i] = cat8(*reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, lk)),
+                *reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, 2 + lk)));
+  f.as[i] = sa[r];
+}
+
+template <class G>
+MOK_DEV void read_f8_b(const uint8_t* tb, const uint32_t* sb, int j, FragsF8<G>& f) {
+  const int lane = lane_id(), lr = lane & 31, lk = lane >> 5;
+  const int r = G::wn() * G::WTN + j * 32 + lr;
+  f.b[j] = cat8(*reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, lk)),
+                *reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, 2 + lk)));
+  f.bs[j] = sb[r];
+}
+
+// one scaled MFMA of fragment (i, j); sh selects the scale byte of this
+// lane's block (stage parity and lane half)
+template <class G>
+MOK_DEV void mfma_f8(const FragsF8<G>& f, int i, int j, int sh, Acc<G::FM, G::FN>& acc) {
+  acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+      f.a[i], f.b[j], acc.c[i][j], 0, 0, 0, (int)((f.as[i] >> sh) & 0xFFu), 0,
+      (int)((f.bs[j] >> sh) & 0xFFu));
+}
+
+// ------------------------------------------------------------------ main loop
+// nk stages through the 4-buffer LDS ring; one workgroup barrier per stage,
+// placed in the middle of the stage's MFMAs:
+//
+//   region A   first half of stage kt's MFMAs, while fragments of the second
+//              half are read from LDS
+//   barrier    each wavefront first waits for its copies of stage kt+1 and
+//              its LDS reads; afterwards stage kt+1 is visible and no
+//              wavefront reads buffer kt%4 any more
+//   region B   second half of stage kt's MFMAs, while the copies of stage
+//              kt+4 into buffer kt%4 are issued and the first fragments of
+//              stage kt+1 are read
+//
+// bf16 halves are the two 16-wide K steps of a stage; fp8 halves are
+// fragment rows 0-1 and 2-3 of the one 64-wide K step, with the B fragments
+// of stage kt+1 read into each B register as soon as its last MFMA of stage
+// kt has issued. Copies complete in issue order, so "stage kt+1 has landed"
+// is a bound on this wavefront's outstanding vector-memory operations: 2
+// stages of copies may still be in flight in the steady state. The main loop
+// runs while stage kt+4 exists; the last (up to 4) stages issue no copies.
+template <class G, class LA, class LB, class SA, class SB>
+struct Pipe {
+  static constexpr int kD = LA::kDma + LB::kDma + SA::kDma + SB::kDma;
+  Smem<G>& sm;
+  const LA& la;
+  const LB& lb;
+  const SA& sa;
+  const SB& sb;
+  MOK_DEV void dma(int s) const {
+    const int b = s & (kNbuf - 1);
+    la.dma(s, sm.a[b]);
+    lb.dma(s, sm.b[b]);
+    sa.dma(s, reinterpret_cast<uint8_t*>(sm.sa[b]));
+    sb.dma(s, reinterpret_cast<uint8_t*>(sm.sb[b]));
+  }
+  // wait until stage s+1 has landed, given that `left` later stages of
+  // copies (0, 1 or 2) have been issued since, then barrier
+  MOK_DEV void publish(int left) const {
+    if (left >= 2) wait_vm_lds<2 * kD>();
+    else if (left == 1) wait_vm_lds<kD>();
+    else wait_vm_lds<0>();
+    barrier_lds();
+  }
+};
+
+// scheduling-group masks (llvm.amdgcn.sched.group.barrier)
+constexpr int kSgMfma = 0x008, kSgVmem = 0x020, kSgDsRead = 0x100;
+
 template <class G, bool F8, class LA, class LB, class SA, class SB>
-MOK_DEV void mainloop(Smem<G>& sm, LA& la, LB& lb, SA& sa, SB& sb, int nk,
+MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
                       Acc<G::FM, G::FN>& acc) {
+  using P = Pipe<G, LA, LB, SA, SB>;
+  constexpr int kD = P::kD;
+  static_assert(3 * kD < 64, "vmcnt range");
+  const P p{sm, la, lb, sa, sb};
   acc.zero();
-  __syncthreads();                       // previous users of the LDS buffers are done
+  __syncthreads();                               // previous users of the LDS buffers are done
   if (nk <= 0) return;
-  la.begin(0, sm.a[0]);
-  lb.begin(0, sm.b[0]);
-  sa.begin(0, sm.sa[0]);
-  sb.begin(0, sm.sb[0]);
-  la.end(sm.a[0]);
-  lb.end(sm.b[0]);
-  sa.end(sm.sa[0]);
-  sb.end(sm.sb[0]);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.begin(kt + 1, sm.a[nxt]);
-      lb.begin(kt + 1, sm.b[nxt]);
-      sa.begin(kt + 1, sm.sa[nxt]);
-      sb.begin(kt + 1, sm.sb[nxt]);
-    }
-    mma_stage<G, F8>(sm.a[cur], sm.b[cur], sm.sa[cur], sm.sb[cur], acc);
-    if (more) {
-      la.end(sm.a[nxt]);
-      lb.end(sm.b[nxt]);
-      sa.end(sm.sa[nxt]);
-      sb.end(sm.sb[nxt]);
-    }
-    wait_vmem();
-    __syncthreads();
+
+  // prologue: copies of stages 0..3, wait for stage 0
+  p.dma(0);
+  if (nk > 1) p.dma(1);
+  if (nk > 2) p.dma(2);
+  if (nk > 3) p.dma(3);
+  if (nk > 3) wait_vm_lds<3 * kD>();
+  else if (nk == 3) wait_vm_lds<2 * kD>();
+  else if (nk == 2) wait_vm_lds<kD>();
+  else wait_vm_lds<0>();
+  barrier_lds();
+
+  if constexpr (!F8) {
+    static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
+    FragsB16<G> f0, f1;
+    read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, f0);
+    auto stage = [&](int kt, auto dma_tag, int left) {
+      constexpr bool DMA = decltype(dma_tag)::value;
+      const int cur = kt & (kNbuf - 1), nxt = (kt + 1) & (kNbuf - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b16<G, LA, LB>(sm.a[cur], sm.b[cur], 1, f1);
+      mfma_b16<G>(f0, acc);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      p.publish(left);
+      if constexpr (DMA) p.dma(kt + 4);
+      read_b16<G, LA, LB>(sm.a[nxt], sm.b[nxt], 0, f0);
+      mfma_b16<G>(f1, acc);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 4 < nk; ++kt) stage(kt, std::true_type{}, 2);
+    for (; kt < nk; ++kt) stage(kt, std::false_type{}, min(nk - 2 - kt, 2));
+  } else {
+    static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
+    const int sh_lane = 8 * (lane_id() >> 5);
+    FragsF8<G> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_f8_a<G>(sm.a[0], sm.sa[0], i, f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) read_f8_b<G>(sm.b[0], sm.sb[0], j, f);
+    auto stage = [&](int kt, auto dma_tag, int left) {
+      constexpr bool DMA = decltype(dma_tag)::value;
+      const int cur = kt & (kNbuf - 1), nxt = (kt + 1) & (kNbuf - 1);
+      const int sh = 16 * (kt & 1) + sh_lane;
+      // region A: rows 0-1; read rows 2-3 of this stage (rows 0-1 and all B
+      // fragments were read during the previous stage)
+      __builtin_amdgcn_sched_barrier(0);
+      read_f8_a<G>(sm.a[cur], sm.sa[cur], 2, f);
+      read_f8_a<G>(sm.a[cur], sm.sa[cur], 3, f);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_f8<G>(f, i, j, sh, acc);
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      p.publish(left);
+      if constexpr (DMA) p.dma(kt + 4);
+      // region B: rows 2-3, column block by column block; each B fragment of
+      // stage kt+1 is read once its last MFMA here has issued, rows 0-1 of
+      // stage kt+1 go into the registers region A freed
+      const FragsF8<G> g = f;
+      read_f8_a<G>(sm.a[nxt], sm.sa[nxt], 0, f);
+      read_f8_a<G>(sm.a[nxt], sm.sa[nxt], 1, f);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mfma_f8<G>(g, 2, j, sh, acc);
+        mfma_f8<G>(g, 3, j, sh, acc);
+        read_f8_b<G>(sm.b[nxt], sm.sb[nxt], j, f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmem, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 4 < nk; ++kt) stage(kt, std::true_type{}, 2);
+    for (; kt < nk; ++kt) stage(kt, std::false_type{}, min(nk - 2 - kt, 2));
   }
 }
 
 // ------------------------------------------------------------------ epilogue staging
-// Output tile staged in LDS as bf16 [BM][W] (row pitch W*2 + 16 bytes), then
-// written out as 16-byte row chunks to per-row destinations.
-template <int BM, int W>
-struct OutStage {
-  static constexpr int PITCH = W * 2 + 16;
-  MOK_DEV static void put(uint8_t* lds, int r, int c, float v) {
-    *reinterpret_cast<bf16_t*>(lds + r * PITCH + c * 2) = f32_to_bf16(v);
-  }
-  MOK_DEV static void put_bits(uint8_t* lds, int r, int c, bf16_t v) {
-    *reinterpret_cast<bf16_t*>(lds + r * PITCH + c * 2) = v;
-  }
-  // dst(r) = byte address of output row r (column 0 of the tile); rows >= nrows
-  // and columns >= ncols are skipped.
-  template <class Dst>
-  MOK_DEV static void store(const uint8_t* lds, int nrows, int ncols, Dst dst) {
-    constexpr int CPR = W / 8;                       // 16-byte chunks per row
-    for (int idx = threadIdx.x; idx < BM * CPR; idx += kThreads) {
-      const int r = idx / CPR, c = idx % CPR;
-      if (r < nrows && c * 8 < ncols)
-        *reinterpret_cast<uint4*>(dst(r) + c * 16) = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 16);
-    }
-  }
-};
-
 // fp32 staging of one 128-row half of a 256-row tile (the rows owned by the
 // wavefronts with wm() == half), pitch BN*4 + 16 bytes.
 template <class G>
@@ -405,6 +542,19 @@ MOK_DEV void store_tile_bf16(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nro
       *reinterpret_cast<uint4*>(dst(128 * half + r) + c) = pack_bf16x8(v);
     }
   }
+}
+
+// Logical tile of this workgroup for a 1-D grid over `total` tiles.
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs (each
+// with its own L2); this gives each XCD one contiguous range of logical
+// tiles, so tiles that share operands (same row tile, same expert weights)
+// run on the same L2. Returns -1 for workgroups past the end.
+constexpr int kXcds = 8;
+MOK_DEV int xcd_tile(int total) {
+  const int wg = (int)blockIdx.x;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int t = (wg % kXcds) * per + wg / kXcds;
+  return (wg / kXcds < per && t < total) ? t : -1;
 }
 
 }  // namespace mok

@@ -20,8 +20,7 @@ namespace {
 using G256 = Geo<256, 256, 2, 2>;
 
 // ================================================================== forward
-// Forward tiles of minibatch m: blockIdx.x walks the minibatch's row tiles,
-// blockIdx.y the column tiles.
+// A forward tile: row tile ti of minibatch m (rows in ring slot m mod N_s).
 struct FwdTile {
   mok_tile t;
   int nrows;
@@ -53,13 +52,13 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti,
   Acc<G::FM, G::FN> acc;
   if constexpr (F8) {
     const int64_t sx = H / 32;
-    LoadScales<G::BM> lsa{a.ring_xs + ft.slot_row0 * sx, sx, ft.nrows, false, nullptr, 0, 0};
+    LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_xs + ft.slot_row0 * sx, sx, ft.nrows}};
     const int64_t se = (int64_t)ft.t.e * I * sx;
-    LoadScales<G::BN> lsb{a.sg + se, sx, 0, true, a.su + se, n0, (int)I};
-    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 128), acc);
+    LoadScalesD<G::BN, RowsGateUp> lsb{{a.sg + se, a.su + se, sx, n0, (int)I}};
+    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);
   } else {
     NoScales ns;
-    mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 64), acc);
+    mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
   }
 
   // SwiGLU on the accumulators; h (and a, b) staged in LDS for row-wise stores.
@@ -159,33 +158,38 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int* rows, int m
   Acc<G::FM, G::FN> acc;
   if constexpr (F8) {
     const int64_t sx = I / 32;
-    LoadScales<G::BM> lsa{a.ring_hs + ft.slot_row0 * sx, sx, ft.nrows, false, nullptr, 0, 0};
-    LoadScales<G::BN> lsb{a.sd + ((int64_t)ft.t.e * H + n0) * sx, sx, (int)(H - n0), false, nullptr, 0, 0};
-    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(I / 128), acc);
+    LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_hs + ft.slot_row0 * sx, sx, ft.nrows}};
+    LoadScalesD<G::BN, RowsStrided> lsb{{a.sd + ((int64_t)ft.t.e * H + n0) * sx, sx, (int)(H - n0)}};
+    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(I / 64), acc);
   } else {
     NoScales ns;
-    mainloop<G, false>(sm, la, lb, ns, ns, (int)(I / 64), acc);
+    mainloop<G, false>(sm, la, lb, ns, ns, (int)(I / 32), acc);
   }
   bf16_t* ob = a.obuf + n0;
   store_tile_bf16<G>(lds_raw, acc, ft.nrows, (int)(H - n0),
                      [&](int r) { return ob + (int64_t)rows[r] * H; });
 }
 
+// Launch grids are 1-D upper bounds; the tile count of minibatch m is read
+// on the device and the logical tile order is XCD-aware (xcd_tile), row-major
+// over (row tile, column tile).
 template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m) {
+__global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G256>)];
-  const int ti = a.mb_tile_start[m] + (int)blockIdx.x;
-  if (ti >= a.mb_tile_start[m + 1]) return;
-  gateup_tile<F8>(a, lds_raw, m, ti, (int)blockIdx.y);
+  const int t0 = a.mb_tile_start[m];
+  const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
+  if (L < 0) return;
+  gateup_tile<F8>(a, lds_raw, m, t0 + L / ncol, L % ncol);
 }
 
 template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m) {
+__global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G256>)];
   __shared__ int rows[G256::BM];
-  const int ti = a.mb_tile_start[m] + (int)blockIdx.x;
-  if (ti >= a.mb_tile_start[m + 1]) return;
-  down_tile<F8>(a, lds_raw, rows, m, ti, (int)blockIdx.y);
+  const int t0 = a.mb_tile_start[m];
+  const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
+  if (L < 0) return;
+  down_tile<F8>(a, lds_raw, rows, m, t0 + L / ncol, L % ncol);
 }
 
 // ================================================================== persistent driver
@@ -343,33 +347,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
 }
 
 // ================================================================== backward
-MOK_DEV bool bwd_tile(const mok_bwd_args& a, mok_tile& t) {
-  if ((int)blockIdx.x >= *a.n_tiles) return false;
-  t = a.tiles[blockIdx.x];
+// Backward row-tile kernels: 1-D grid, logical tile L = (row tile, column
+// tile) row-major in XCD-aware order; ny receives the column tile.
+MOK_DEV bool bwd_tile(const mok_bwd_args& a, int ncol, mok_tile& t, int& ny) {
+  const int L = xcd_tile(*a.n_tiles * ncol);
+  if (L < 0) return false;
+  t = a.tiles[L / ncol];
+  ny = L % ncol;
   return true;
 }
 
 // dh = dO . Wd[e] (K = H), then the SwiGLU backward from the saved a, b:
 // dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s, h = a*s*b with s = sigmoid(a).
-__global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
   Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
   mok_tile t;
-  if (!bwd_tile(a, t)) return;
+  int ny;
+  if (!bwd_tile(a, ncol, t, ny)) return;
   const int nrows = t.p1 - t.p0;
   const int64_t H = a.H, I = a.I;
-  const int n0 = blockIdx.y * G::BN;
+  const int n0 = ny * G::BN;
   LoadKD<G::BM, RowsStrided> la{{reinterpret_cast<const uint8_t*>(a.dO + (int64_t)t.p0 * H), 2 * H, nrows}};
-  LoadT<G::BN> lb;
-  lb.base0 = lb.base1 = a.wd + (int64_t)t.e * H * I + n0;
-  lb.ksplit = 0x7FFFFFFF;
-  lb.ld = I;
-  lb.K = (int)H;
-  lb.mlimit = (int)(I - n0);
+  const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(a.wd + (int64_t)t.e * H * I + n0),
+                        reinterpret_cast<const uint8_t*>(a.wd + (int64_t)t.e * H * I + n0), 0x7FFFFFFF,
+                        2 * I, (int)H, (int)min<int64_t>(G::BN, I - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 64), acc);
+  mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
   // dA, dB and h per element from an fp32 half-tile of dh in LDS and the
   // saved a, b (16-byte loads and stores along the row).
   using HS = HalfF32<G>;
@@ -402,78 +408,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a) {
 }
 
 // dX rows = [dA | dB] . [Wg[e]; Wu[e]] (K = 2I); row p goes to flat row perm[p].
-__global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
   __shared__ int rows[G::BM];
   Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
   mok_tile t;
-  if (!bwd_tile(a, t)) return;
+  int ny;
+  if (!bwd_tile(a, ncol, t, ny)) return;
   const int nrows = t.p1 - t.p0;
   const int64_t H = a.H, I = a.I;
-  const int n0 = blockIdx.y * G::BN;
+  const int n0 = ny * G::BN;
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   LoadKD<G::BM, RowsStrided> la{{reinterpret_cast<const uint8_t*>(a.dab + (int64_t)t.p0 * 2 * I), 4 * I, nrows}};
-  LoadT<G::BN> lb;
-  lb.base0 = a.wg + (int64_t)t.e * I * H + n0;
-  lb.base1 = a.wu + (int64_t)t.e * I * H + n0 - I * H;   // row k of [Wg; Wu] for k >= I
-  lb.ksplit = (int)I;
-  lb.ld = H;
-  lb.K = (int)(2 * I);
-  lb.mlimit = (int)(H - n0);
+  // row k of [Wg[e]; Wu[e]]: Wg row k for k < I, Wu row k - I beyond
+  const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(a.wg + (int64_t)t.e * I * H + n0),
+                        reinterpret_cast<const uint8_t*>(a.wu + (int64_t)t.e * I * H + n0), (int)I,
+                        2 * H, (int)(2 * I), (int)min<int64_t>(G::BN, H - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (int)(2 * I / 64), acc);
+  mainloop<G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), acc);
   bf16_t* d = a.dxrows + n0;
   store_tile_bf16<G>(lds_raw, acc, nrows, (int)(H - n0),
                      [&](int r) { return d + (int64_t)rows[r] * H; });
 }
 
 // Weight gradients out[m][n] = sum over the expert's rows p (ascending) of
-// A[p][m] * B[p][n]; both operands K-outer. blockIdx.y = expert.
+// A[p][m] * B[p][n]; both operands K-outer.
 MOK_DEV void dw_tile(uint8_t* lds_raw, const bf16_t* A, int64_t lda, int mlimit, const bf16_t* B,
                      int64_t ldb, int nlimit, int K, bf16_t* out, int64_t ldo) {
   using G = G256;
   Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
-  LoadT<G::BM> la;
-  la.base0 = la.base1 = A;
-  la.ksplit = 0x7FFFFFFF;
-  la.ld = lda;
-  la.K = K;
-  la.mlimit = mlimit;
-  LoadT<G::BN> lb;
-  lb.base0 = lb.base1 = B;
-  lb.ksplit = 0x7FFFFFFF;
-  lb.ld = ldb;
-  lb.K = K;
-  lb.mlimit = nlimit;
+  const LoadKO<G::BM> la{reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(A),
+                        0x7FFFFFFF, 2 * lda, K, mlimit};
+  const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(B), reinterpret_cast<const uint8_t*>(B),
+                        0x7FFFFFFF, 2 * ldb, K, nlimit};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (K + 63) / 64, acc);
+  mainloop<G, false>(sm, la, lb, ns, ns, (K + 31) / 32, acc);
   store_tile_bf16<G>(lds_raw, acc, mlimit, nlimit, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
-  const int e = blockIdx.y;
+  const int L = xcd_tile(a.E * tiles_per_e);
+  if (L < 0) return;
+  const int e = L / tiles_per_e, tl = L % tiles_per_e;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((I + G::BN - 1) / G::BN);
-  const int m0 = (blockIdx.x / ntn) * G::BM, n0 = (blockIdx.x % ntn) * G::BN;
+  const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
   const int o = a.offsets[e], c = a.offsets[e + 1] - o;
   dw_tile(lds_raw, a.dO + (int64_t)o * H + m0, H, (int)min<int64_t>(G::BM, H - m0),
           a.hb + (int64_t)o * I + n0, I, (int)min<int64_t>(G::BN, I - n0), c,
           a.dwd + (int64_t)e * H * I + (int64_t)m0 * I + n0, I);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
-  const int e = blockIdx.y;
+  const int L = xcd_tile(a.E * tiles_per_e);
+  if (L < 0) return;
+  const int e = L / tiles_per_e, tl = L % tiles_per_e;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((H + G::BN - 1) / G::BN);
-  const int mt = blockIdx.x / ntn;
-  const int n0 = (blockIdx.x % ntn) * G::BN;
+  const int mt = tl / ntn;
+  const int n0 = (tl % ntn) * G::BN;
   // rows [0, I) of the stacked [dWg; dWu] are dWg, [I, 2I) dWu; a tile never
   // straddles the two because I is a multiple of 128 and tiles of 256 rows are
   // split at I.
@@ -491,19 +491,23 @@ unsigned cdivu(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
+unsigned grid8(int64_t n) { return (unsigned)((n + kXcds - 1) / kXcds * kXcds); }
+
 hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
                              hipStream_t st) {
-  const dim3 grid(max_tiles_mb, cdivu(a.I, G256::BN / 2));
-  if (mxfp8) hipLaunchKernelGGL(gateup_kernel<true>, grid, dim3(kThreads), 0, st, a, m);
-  else hipLaunchKernelGGL(gateup_kernel<false>, grid, dim3(kThreads), 0, st, a, m);
+  const int ncol = (int)cdivu(a.I, G256::BN / 2);
+  const dim3 grid(grid8((int64_t)max_tiles_mb * ncol));
+  if (mxfp8) hipLaunchKernelGGL(gateup_kernel<true>, grid, dim3(kThreads), 0, st, a, m, ncol);
+  else hipLaunchKernelGGL(gateup_kernel<false>, grid, dim3(kThreads), 0, st, a, m, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
                            hipStream_t st) {
-  const dim3 grid(max_tiles_mb, cdivu(a.H, G256::BN));
-  if (mxfp8) hipLaunchKernelGGL(down_kernel<true>, grid, dim3(kThreads), 0, st, a, m);
-  else hipLaunchKernelGGL(down_kernel<false>, grid, dim3(kThreads), 0, st, a, m);
+  const int ncol = (int)cdivu(a.H, G256::BN);
+  const dim3 grid(grid8((int64_t)max_tiles_mb * ncol));
+  if (mxfp8) hipLaunchKernelGGL(down_kernel<true>, grid, dim3(kThreads), 0, st, a, m, ncol);
+  else hipLaunchKernelGGL(down_kernel<false>, grid, dim3(kThreads), 0, st, a, m, ncol);
   return hipGetLastError();
 }
 
@@ -522,23 +526,25 @@ hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, int* counters, int32
 }
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_dh_kernel, dim3(a.max_tiles, cdivu(a.I, G256::BN)), dim3(kThreads), 0, st, a);
+  const int ncol = (int)cdivu(a.I, G256::BN);
+  hipLaunchKernelGGL(bwd_dh_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dx(const mok_bwd_args& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3(a.max_tiles, cdivu(a.H, G256::BN)), dim3(kThreads), 0, st, a);
+  const int ncol = (int)cdivu(a.H, G256::BN);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwd(const mok_bwd_args& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_dwd_kernel, dim3(cdivu(a.H, G256::BM) * cdivu(a.I, G256::BN), a.E),
-                     dim3(kThreads), 0, st, a);
+  const int tpe = (int)(cdivu(a.H, G256::BM) * cdivu(a.I, G256::BN));
+  hipLaunchKernelGGL(bwd_dwd_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwgu(const mok_bwd_args& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_dwgu_kernel, dim3(2 * cdivu(a.I, G256::BM) * cdivu(a.H, G256::BN), a.E),
-                     dim3(kThreads), 0, st, a);
+  const int tpe = (int)(2 * cdivu(a.I, G256::BM) * cdivu(a.H, G256::BN));
+  hipLaunchKernelGGL(bwd_dwgu_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
   return hipGetLastError();
 }
