@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 # algorithmic FLOPs per routed row of each GEMM kernel, in units of H*I
 GEMM_FLOPS_PER_ROW = {
     "gateup_gemm": 4, "down_gemm": 2, "bwd_dh_gemm": 2, "bwd_dwd_gemm": 2,
-    "bwd_dwgu_gemm": 4, "bwd_dx_gemm": 4, "fwd_persistent": 6,
+    "bwd_dwgu_gemm": 4, "bwd_dx_gemm": 4,
 }
 
 

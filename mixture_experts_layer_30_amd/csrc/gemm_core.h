@@ -37,7 +37,6 @@ namespace mok {
 
 constexpr int kThreads = 256;
 constexpr int kStage = 64;                        // K bytes per row per stage
-constexpr int kNbuf = 4;                          // LDS ring depth
 
 MOK_DEV int swap13(int r) { return (r & ~0xA) | ((r >> 2) & 2) | ((r << 2) & 8); }
 // byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile
@@ -240,13 +239,37 @@ struct Geo {
   MOK_DEV static int col(int j) { return wn() * WTN + j * 32 + (lane_id() & 31); }
 };
 
-template <class G>
-struct Smem {
-  uint8_t a[kNbuf][G::BM * kStage];
-  uint8_t b[kNbuf][G::BN * kStage];
-  uint32_t sa[kNbuf][G::BM];
-  uint32_t sb[kNbuf][G::BN];
+// LDS ring of one tile: NBUF stage buffers per operand, plus per-stage scale
+// words for fp8.
+template <class G, int NBUF, bool SCALES>
+struct SmemT {
+  static constexpr int kNbuf = NBUF;
+  uint8_t a[NBUF][G::BM * kStage];
+  uint8_t b[NBUF][G::BN * kStage];
 };
+template <class G, int NBUF>
+struct SmemT<G, NBUF, true> {
+  static constexpr int kNbuf = NBUF;
+  uint8_t a[NBUF][G::BM * kStage];
+  uint8_t b[NBUF][G::BN * kStage];
+  uint32_t sa[NBUF][G::BM];
+  uint32_t sb[NBUF][G::BN];
+};
+// 4 buffers (bf16: 128 KiB; fp8: 136 KiB with the scale words)
+template <class G, bool F8>
+using Smem = SmemT<G, 4, F8>;
+
+// LDS bytes of a tile kernel: the ring, or the epilogue's fp32 half-tile
+// (128 rows of BN*4 + 16 bytes) plus a 256-entry row table, if larger.
+template <class SM>
+constexpr int tile_lds_bytes() {
+  return (int)sizeof(SM) > 128 * (256 * 4 + 16) + 1024 ? (int)sizeof(SM) : 128 * (256 * 4 + 16) + 1024;
+}
+// the row table: the top 1 KiB of a tile's LDS, free once the main loop ends
+template <class SM>
+MOK_DEV int* tile_rows(uint8_t* lds_raw) {
+  return reinterpret_cast<int*>(lds_raw + tile_lds_bytes<SM>() - 1024);
+}
 
 // ------------------------------------------------------------------ fragments
 // bf16: fragments of one 16-wide K step (kk = 0, 1 within a stage).
@@ -320,60 +343,70 @@ MOK_DEV void mfma_f8(const FragsF8<G>& f, int i, int j, int sh, Acc<G::FM, G::FN
 }
 
 // ------------------------------------------------------------------ main loop
-// nk stages through the 4-buffer LDS ring; one workgroup barrier per stage,
-// placed in the middle of the stage's MFMAs:
+// nk stages through the LDS ring; one workgroup barrier per stage, placed in
+// the middle of the stage's MFMAs:
 //
 //   region A   first half of stage kt's MFMAs, while fragments of the second
 //              half are read from LDS
 //   barrier    each wavefront first waits for its copies of stage kt+1 and
 //              its LDS reads; afterwards stage kt+1 is visible and no
-//              wavefront reads buffer kt%4 any more
-//   region B   second half of stage kt's MFMAs, while the copies of stage
-//              kt+4 into buffer kt%4 are issued and the first fragments of
-//              stage kt+1 are read
+//              wavefront reads the buffer of stage kt any more
+//   copies     into buffers whose stages have been read completely
+//   region B   second half of stage kt's MFMAs, while the first fragments
+//              of stage kt+1 are read
 //
-// bf16 halves are the two 16-wide K steps of a stage; fp8 halves are
-// fragment rows 0-1 and 2-3 of the one 64-wide K step, with the B fragments
-// of stage kt+1 read into each B register as soon as its last MFMA of stage
-// kt has issued. Copies complete in issue order, so "stage kt+1 has landed"
-// is a bound on this wavefront's outstanding vector-memory operations: 2
-// stages of copies may still be in flight in the steady state. The main loop
-// runs while stage kt+4 exists; the last (up to 4) stages issue no copies.
-template <class G, class LA, class LB, class SA, class SB>
+// Stage kt+4 is copied on every kt, into the buffer of stage kt. (Copying
+// stages in 128-byte-line pairs, which streams HBM better in isolation, was
+// measured slower here.) bf16 halves are the two 16-wide K steps of a stage.
+// fp8 halves are fragment rows 0-1 and 2-3 of the one 64-wide K step; the B
+// fragments of stage kt+1 are read into each B register as soon as its last
+// MFMA of stage kt has issued.
+//
+// Copies complete in issue order, so "stage kt+1 has landed" is a bound on
+// this wavefront's outstanding vector-memory operations: the number of stages
+// issued after it. The last stages issue no copies.
+template <class SM, class LA, class LB, class SA, class SB>
 struct Pipe {
   static constexpr int kD = LA::kDma + LB::kDma + SA::kDma + SB::kDma;
-  Smem<G>& sm;
+  SM& sm;
   const LA& la;
   const LB& lb;
   const SA& sa;
   const SB& sb;
   MOK_DEV void dma(int s) const {
-    const int b = s & (kNbuf - 1);
+    const int b = s % SM::kNbuf;
     la.dma(s, sm.a[b]);
     lb.dma(s, sm.b[b]);
-    sa.dma(s, reinterpret_cast<uint8_t*>(sm.sa[b]));
-    sb.dma(s, reinterpret_cast<uint8_t*>(sm.sb[b]));
+    if constexpr (SA::kDma > 0) sa.dma(s, reinterpret_cast<uint8_t*>(sm.sa[b]));
+    if constexpr (SB::kDma > 0) sb.dma(s, reinterpret_cast<uint8_t*>(sm.sb[b]));
   }
-  // wait until stage s+1 has landed, given that `left` later stages of
-  // copies (0, 1 or 2) have been issued since, then barrier
+  // wait until stage kt+1 has landed, given that `left` later stages of
+  // copies (0 .. 3) have been issued since, then barrier
   MOK_DEV void publish(int left) const {
-    if (left >= 2) wait_vm_lds<2 * kD>();
+    if (left >= 3) wait_vm_lds<3 * kD>();
+    else if (left == 2) wait_vm_lds<2 * kD>();
     else if (left == 1) wait_vm_lds<kD>();
     else wait_vm_lds<0>();
     barrier_lds();
   }
 };
 
+// copy issue of a stage iteration: none, or stage kt+4
+constexpr int kNoCopy = 0, kCopy = 1;
+
 // scheduling-group masks (llvm.amdgcn.sched.group.barrier)
 constexpr int kSgMfma = 0x008, kSgVmem = 0x020, kSgDsRead = 0x100;
 
 template <class G, bool F8, class LA, class LB, class SA, class SB>
-MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
+MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
                       Acc<G::FM, G::FN>& acc) {
-  using P = Pipe<G, LA, LB, SA, SB>;
+  using SM = Smem<G, F8>;
+  constexpr int NB = SM::kNbuf;
+  using P = Pipe<SM, LA, LB, SA, SB>;
   constexpr int kD = P::kD;
   static_assert(3 * kD < 64, "vmcnt range");
   const P p{sm, la, lb, sa, sb};
+  auto buf = [](int st) { return st % NB; };
   acc.zero();
   __syncthreads();                               // previous users of the LDS buffers are done
   if (nk <= 0) return;
@@ -394,8 +427,8 @@ MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, con
     FragsB16<G> f0, f1;
     read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, f0);
     auto stage = [&](int kt, auto dma_tag, int left) {
-      constexpr bool DMA = decltype(dma_tag)::value;
-      const int cur = kt & (kNbuf - 1), nxt = (kt + 1) & (kNbuf - 1);
+      constexpr int DMA = decltype(dma_tag)::value;
+      const int cur = buf(kt), nxt = buf(kt + 1);
       __builtin_amdgcn_sched_barrier(0);
       read_b16<G, LA, LB>(sm.a[cur], sm.b[cur], 1, f1);
       mfma_b16<G>(f0, acc);
@@ -407,23 +440,20 @@ MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, con
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
       p.publish(left);
-      if constexpr (DMA) p.dma(kt + 4);
+      if constexpr (DMA == kCopy) p.dma(kt + 4);
       read_b16<G, LA, LB>(sm.a[nxt], sm.b[nxt], 0, f0);
       mfma_b16<G>(f1, acc);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 4 < nk; ++kt) stage(kt, std::true_type{}, 2);
-    for (; kt < nk; ++kt) stage(kt, std::false_type{}, min(nk - 2 - kt, 2));
+    for (; kt + 4 < nk; ++kt) stage(kt, std::integral_constant<int, kCopy>{}, 2);
+    for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, kNoCopy>{}, min(nk - 2 - kt, 2));
   } else {
     static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
     const int sh_lane = 8 * (lane_id() >> 5);
@@ -433,8 +463,8 @@ MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, con
 #pragma unroll
     for (int j = 0; j < 4; ++j) read_f8_b<G>(sm.b[0], sm.sb[0], j, f);
     auto stage = [&](int kt, auto dma_tag, int left) {
-      constexpr bool DMA = decltype(dma_tag)::value;
-      const int cur = kt & (kNbuf - 1), nxt = (kt + 1) & (kNbuf - 1);
+      constexpr int DMA = decltype(dma_tag)::value;
+      const int cur = buf(kt), nxt = buf(kt + 1);
       const int sh = 16 * (kt & 1) + sh_lane;
       // region A: rows 0-1; read rows 2-3 of this stage (rows 0-1 and all B
       // fragments were read during the previous stage)
@@ -453,7 +483,7 @@ MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, con
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
       p.publish(left);
-      if constexpr (DMA) p.dma(kt + 4);
+      if constexpr (DMA == kCopy) p.dma(kt + 4);
       // region B: rows 2-3, column block by column block; each B fragment of
       // stage kt+1 is read once its last MFMA here has issued, rows 0-1 of
       // stage kt+1 go into the registers region A freed
@@ -477,8 +507,8 @@ MOK_DEV void mainloop(Smem<G>& sm, const LA& la, const LB& lb, const SA& sa, con
       __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 4 < nk; ++kt) stage(kt, std::true_type{}, 2);
-    for (; kt < nk; ++kt) stage(kt, std::false_type{}, min(nk - 2 - kt, 2));
+    for (; kt + 4 < nk; ++kt) stage(kt, std::integral_constant<int, kCopy>{}, 2);
+    for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, kNoCopy>{}, min(nk - 2 - kt, 2));
   }
 }
 

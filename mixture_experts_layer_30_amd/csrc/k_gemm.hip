@@ -39,7 +39,7 @@ MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int m, int ti, FwdTile& ft) {
 template <bool F8>
 MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti, int ny) {
   using G = G256;
-  Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
+  Smem<G, F8>& sm = *reinterpret_cast<Smem<G, F8>*>(lds_raw);
   FwdTile ft;
   fwd_tile_at(a, m, ti, ft);
   const int64_t H = a.H, I = a.I;
@@ -143,15 +143,14 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti,
 // down GEMM of one row tile x 256 output columns; each row is pushed to its
 // flat position perm[p] of obuf (unique destinations, no atomics).
 template <bool F8>
-MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int* rows, int m, int ti, int ny) {
+MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti, int ny) {
   using G = G256;
-  Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
+  Smem<G, F8>& sm = *reinterpret_cast<Smem<G, F8>*>(lds_raw);
   FwdTile ft;
   fwd_tile_at(a, m, ti, ft);
   const int64_t H = a.H, I = a.I;
   const int n0 = ny * G::BN;
   const int64_t hrow = F8 ? I : 2 * I;
-  for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < ft.nrows ? a.perm[ft.t.p0 + r] : 0;
   LoadKD<G::BM, RowsStrided> la{{a.ring_h + ft.slot_row0 * hrow, hrow, ft.nrows}};
   LoadKD<G::BN, RowsStrided> lb{{(const uint8_t*)a.wd + ((int64_t)ft.t.e * H + n0) * hrow, hrow,
                                 (int)(H - n0)}};
@@ -165,6 +164,9 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int* rows, int m
     NoScales ns;
     mainloop<G, false>(sm, la, lb, ns, ns, (int)(I / 32), acc);
   }
+  // destination rows, staged above the epilogue's fp32 half-tile
+  int* rows = tile_rows<Smem<G, F8>>(lds_raw);
+  for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < ft.nrows ? a.perm[ft.t.p0 + r] : 0;
   bf16_t* ob = a.obuf + n0;
   store_tile_bf16<G>(lds_raw, acc, ft.nrows, (int)(H - n0),
                      [&](int r) { return ob + (int64_t)rows[r] * H; });
@@ -175,7 +177,7 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int* rows, int m
 // over (row tile, column tile).
 template <bool F8>
 __global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m, int ncol) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G256>)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
   const int t0 = a.mb_tile_start[m];
   const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
   if (L < 0) return;
@@ -184,166 +186,11 @@ __global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int
 
 template <bool F8>
 __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m, int ncol) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G256>)];
-  __shared__ int rows[G256::BM];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
   const int t0 = a.mb_tile_start[m];
   const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
   if (L < 0) return;
-  down_tile<F8>(a, lds_raw, rows, m, t0 + L / ncol, L % ncol);
-}
-
-// ================================================================== persistent driver
-// [MoK clip] Key points, bullets 3-5, and How-to items 3-4: minibatches of
-// routed rows flow through a fixed ring of token slots on the device; a slot
-// is refilled as soon as the work that read it has retired, and completion
-// is signalled through counters in memory rather than by kernel boundaries.
-//
-// One persistent launch runs every work item of the forward's expert stage:
-//   G(m, c)  gather rows [m*M + c*GR, +GR) into ring slot m mod N_s
-//   U(m, r, n) gate/up tile (row tile r of minibatch m, h-column tile n)
-//   D(m, r, n) down tile
-// Items are numbered in one global order, stage by stage: stage s holds
-// D(s - dl), then G(s), then U(s - ul), with (dl, ul) = (2, 1) when N_s >= 2
-// and (1, 0) when N_s = 1. Every item depends only on items numbered before
-// it (G(m) on all D(m - N_s), U on G of its minibatch, D on all U of its row
-// tile). Workgroups take item numbers from an atomic ticket in increasing
-// order, so every item an item waits for is held by a workgroup that is
-// already running: the waits always end. A wait that exceeds about two
-// seconds sets MOK_STATUS_WATCHDOG and gives up instead of hanging.
-// Which workgroup runs an item never changes what it computes, so the result
-// is bitwise the same as with one launch per stage.
-constexpr int kGatherRows = 64;
-
-struct FwdPlan {
-  int n_mb, M, R, dl, ul, ntu, ntd, gi_full, n_stages;
-  const int* mbs;                      // mb_tile_start
-  MOK_DEV int tiles_before(int m) const { return mbs[m < 0 ? 0 : (m > n_mb ? n_mb : m)]; }
-  MOK_DEV int gi(int m) const {        // gather items of minibatch m
-    if (m < 0 || m >= n_mb) return 0;
-    return (min(M, R - m * M) + kGatherRows - 1) / kGatherRows;
-  }
-  MOK_DEV int64_t gsum(int m) const {  // gather items of minibatches < m
-    if (m <= 0) return 0;
-    if (m >= n_mb) return (int64_t)(n_mb - 1) * gi_full + gi(n_mb - 1);
-    return (int64_t)m * gi_full;
-  }
-  MOK_DEV int64_t cum(int s) const {   // items in stages < s
-    return (int64_t)ntd * tiles_before(s - dl) + gsum(s) + (int64_t)ntu * tiles_before(s - ul);
-  }
-};
-
-struct mok_persist_args {
-  int* ctr;          // [0] ticket, [1 .. n_mb] gather done, [1+n_mb .. 2 n_mb] down done,
-                     // [1 + 2 n_mb ..] gate/up tiles done per forward row tile
-  int32_t* status;   // schedule status word (watchdog bit)
-  const uint8_t* xsrc;
-  const uint8_t* xscales;
-  const int32_t* offsets_E;
-};
-
-MOK_DEV void signal_done(int* c) {
-  __threadfence();                     // this thread's results are visible device-wide
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-MOK_DEV void wait_for(const int* c, int target, int32_t* status) {
-  if (threadIdx.x == 0 && target > 0) {
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
-      // once any wait has timed out, no later wait blocks: the launch drains
-      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 2) break;
-      if (__builtin_amdgcn_s_memrealtime() - t0 > 200000000ull) {   // 2 s at 100 MHz
-        __hip_atomic_fetch_or(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-MOK_DEV void gather_item(const mok_fwd_args& a, const mok_persist_args& ps, bool f8, int m, int c) {
-  const int64_t xrow = f8 ? a.H : 2 * a.H, srow = a.H / 32;
-  const int64_t mb0 = (int64_t)m * a.M;
-  const int64_t rows_m = min((int64_t)a.M, (int64_t)a.T * a.topk - mb0);
-  const int nvalid = *ps.offsets_E;
-  const int64_t slot0 = (int64_t)(m % a.n_slots) * a.M;
-  const int w = threadIdx.x >> 6, l = lane_id();
-  for (int rr = w; rr < kGatherRows; rr += 4) {
-    const int64_t r = (int64_t)c * kGatherRows + rr;
-    if (r >= rows_m || mb0 + r >= nvalid) break;
-    const int64_t tok = a.perm[mb0 + r] / a.topk;
-    const uint4* src = reinterpret_cast<const uint4*>(ps.xsrc + tok * xrow);
-    uint4* dst = reinterpret_cast<uint4*>(a.ring_x + (slot0 + r) * xrow);
-    for (int64_t q = l; q < xrow / 16; q += 64) dst[q] = src[q];
-    if (f8) {
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(ps.xscales + tok * srow);
-      uint32_t* ds = reinterpret_cast<uint32_t*>(a.ring_xs + (slot0 + r) * srow);
-      for (int64_t q = l; q < srow / 4; q += 64) ds[q] = ss[q];
-    }
-  }
-}
-
-template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_args a, mok_persist_args ps) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G256>)];
-  __shared__ int rows[G256::BM];
-  __shared__ int s_ticket;
-  FwdPlan P;
-  P.n_mb = a.n_mb;
-  P.M = a.M;
-  P.R = (int)(a.T * a.topk);
-  P.dl = a.n_slots >= 2 ? 2 : 1;
-  P.ul = P.dl - 1;
-  P.ntu = (int)((a.I + G256::BN / 2 - 1) / (G256::BN / 2));
-  P.ntd = (int)((a.H + G256::BN - 1) / G256::BN);
-  P.gi_full = (a.M + kGatherRows - 1) / kGatherRows;
-  P.n_stages = a.n_mb + P.dl;
-  P.mbs = a.mb_tile_start;
-  int* gdone = ps.ctr + 1;
-  int* ddone = ps.ctr + 1 + a.n_mb;
-  int* udone = ps.ctr + 1 + 2 * a.n_mb;
-  const int64_t total = P.cum(P.n_stages);
-  for (;;) {
-    if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(ps.ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t t = s_ticket;
-    if (t >= total) break;
-    // stage s with cum(s) <= t < cum(s + 1)
-    int lo = 0, hi = P.n_stages - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (P.cum(mid) <= t) lo = mid; else hi = mid - 1;
-    }
-    const int s = lo;
-    int64_t o = t - P.cum(s);
-    const int md = s - P.dl;
-    const int64_t nd = (md >= 0 && md < P.n_mb) ? (int64_t)P.ntd * (P.tiles_before(md + 1) - P.tiles_before(md)) : 0;
-    if (o < nd) {                                                  // D(md, r, n)
-      const int ti = P.tiles_before(md) + (int)(o / P.ntd);
-      wait_for(udone + ti, P.ntu, ps.status);
-      down_tile<F8>(a, lds_raw, rows, md, ti, (int)(o % P.ntd));
-      signal_done(ddone + md);
-      continue;
-    }
-    o -= nd;
-    const int ng = P.gi(s);
-    if (o < ng) {                                                  // G(s, c)
-      const int mp = s - a.n_slots;
-      if (mp >= 0) wait_for(ddone + mp, P.ntd * (P.tiles_before(mp + 1) - P.tiles_before(mp)), ps.status);
-      gather_item(a, ps, F8, s, (int)o);
-      signal_done(gdone + s);
-      continue;
-    }
-    o -= ng;                                                       // U(mu, r, n)
-    const int mu = s - P.ul;
-    const int ti = P.tiles_before(mu) + (int)(o / P.ntu);
-    wait_for(gdone + mu, P.gi(mu), ps.status);
-    gateup_tile<F8>(a, lds_raw, mu, ti, (int)(o % P.ntu));
-    signal_done(udone + ti);
-  }
+  down_tile<F8>(a, lds_raw, m, t0 + L / ncol, L % ncol);
 }
 
 // ================================================================== backward
@@ -361,8 +208,8 @@ MOK_DEV bool bwd_tile(const mok_bwd_args& a, int ncol, mok_tile& t, int& ny) {
 // dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s, h = a*s*b with s = sigmoid(a).
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
-  Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
+  Smem<G, false>& sm = *reinterpret_cast<Smem<G, false>*>(lds_raw);
   mok_tile t;
   int ny;
   if (!bwd_tile(a, ncol, t, ny)) return;
@@ -410,16 +257,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
 // dX rows = [dA | dB] . [Wg[e]; Wu[e]] (K = 2I); row p goes to flat row perm[p].
 __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
-  __shared__ int rows[G::BM];
-  Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
+  Smem<G, false>& sm = *reinterpret_cast<Smem<G, false>*>(lds_raw);
   mok_tile t;
   int ny;
   if (!bwd_tile(a, ncol, t, ny)) return;
   const int nrows = t.p1 - t.p0;
   const int64_t H = a.H, I = a.I;
   const int n0 = ny * G::BN;
-  for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   LoadKD<G::BM, RowsStrided> la{{reinterpret_cast<const uint8_t*>(a.dab + (int64_t)t.p0 * 2 * I), 4 * I, nrows}};
   // row k of [Wg[e]; Wu[e]]: Wg row k for k < I, Wu row k - I beyond
   const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(a.wg + (int64_t)t.e * I * H + n0),
@@ -428,6 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
   NoScales ns;
   Acc<G::FM, G::FN> acc;
   mainloop<G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), acc);
+  int* rows = tile_rows<Smem<G, false>>(lds_raw);
+  for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   bf16_t* d = a.dxrows + n0;
   store_tile_bf16<G>(lds_raw, acc, nrows, (int)(H - n0),
                      [&](int r) { return d + (int64_t)rows[r] * H; });
@@ -438,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
 MOK_DEV void dw_tile(uint8_t* lds_raw, const bf16_t* A, int64_t lda, int mlimit, const bf16_t* B,
                      int64_t ldb, int nlimit, int K, bf16_t* out, int64_t ldo) {
   using G = G256;
-  Smem<G>& sm = *reinterpret_cast<Smem<G>*>(lds_raw);
+  Smem<G, false>& sm = *reinterpret_cast<Smem<G, false>*>(lds_raw);
   const LoadKO<G::BM> la{reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(A),
                         0x7FFFFFFF, 2 * lda, K, mlimit};
   const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(B), reinterpret_cast<const uint8_t*>(B),
@@ -451,7 +298,7 @@ MOK_DEV void dw_tile(uint8_t* lds_raw, const bf16_t* A, int64_t lda, int mlimit,
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
   const int L = xcd_tile(a.E * tiles_per_e);
   if (L < 0) return;
   const int e = L / tiles_per_e, tl = L % tiles_per_e;
@@ -466,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, in
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[sizeof(Smem<G>)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
   const int L = xcd_tile(a.E * tiles_per_e);
   if (L < 0) return;
   const int e = L / tiles_per_e, tl = L % tiles_per_e;
@@ -511,19 +358,6 @@ hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool 
   return hipGetLastError();
 }
 
-hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, int* counters, int32_t* status,
-                                     const void* xsrc, const uint8_t* xscales,
-                                     const int32_t* offsets_E, int grid, bool mxfp8, hipStream_t st) {
-  mok_persist_args ps;
-  ps.ctr = counters;
-  ps.status = status;
-  ps.xsrc = static_cast<const uint8_t*>(xsrc);
-  ps.xscales = xscales;
-  ps.offsets_E = offsets_E;
-  if (mxfp8) hipLaunchKernelGGL(fwd_persistent_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, ps);
-  else hipLaunchKernelGGL(fwd_persistent_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a, ps);
-  return hipGetLastError();
-}
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN);

@@ -117,7 +117,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
 // Workspace carve-up. Forward and backward never run inside one call, so
 // they share the same bytes.
 struct FwdWs {
-  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, ctr, ctr_bytes, total;
+  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
 };
 struct BwdWs {
   size_t dO, dab, hb, dxrows, xg, total;
@@ -134,10 +134,6 @@ FwdWs fwd_ws(const Resolved& r) {
   w.obuf = o;    o = align_up(o + (size_t)r.R * 2 * r.H);
   w.xq = o;      o = align_up(o + (r.mx ? (size_t)r.T * r.H : 0));
   w.xqs = o;     o = align_up(o + (r.mx ? (size_t)r.T * (r.H / 32) : 0));
-  // persistent-driver counters: ticket, gather-done and down-done per
-  // minibatch, gate/up-done per forward row tile
-  w.ctr_bytes = (4 * (size_t)(1 + 2 * r.n_mb + r.max_fwd_tiles) + 15) / 16 * 16;
-  w.ctr = o;     o = align_up(o + w.ctr_bytes);
   w.total = o;
   return w;
 }
@@ -313,8 +309,8 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
   if (r.mx && fwd_ctx) return MOK_ERR_UNSUPPORTED;
-  // The persistent minibatch kernel (driver 2) is switched off: its first run
-  // on the device did not complete and the cause is not yet established.
+  // The persistent minibatch kernel (driver 2) is not provided: its first
+  // version did not complete on the device and the cause was not established.
   if (r.driver == 2) return MOK_ERR_UNSUPPORTED;
   const FwdWs W = fwd_ws(r);
   if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;

@@ -88,12 +88,6 @@ hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, boo
 hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
                            hipStream_t st);
 
-// Persistent forward: gather + gate/up + down of every minibatch in one
-// launch; counters = 1 + 2*n_mb + max_fwd_tiles ints, zeroed beforehand.
-hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, int* counters, int32_t* status,
-                                     const void* xsrc, const uint8_t* xscales,
-                                     const int32_t* offsets_E, int grid, bool mxfp8, hipStream_t st);
-
 struct mok_bwd_args {
   int64_t T, H, I;
   int E, topk;
