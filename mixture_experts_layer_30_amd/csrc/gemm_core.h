@@ -2,19 +2,26 @@
 //
 // A workgroup of 256 threads (4 wavefronts in a WM x WN grid) computes a
 // BM x BN tile of C = A . B^T over K. K advances in stages of 64 bytes per
-// operand row (32 bf16 or 64 fp8) through a ring of 4 LDS buffers; every
-// operand reaches LDS by direct global->LDS copies (global_load_lds), up to 3
-// stages ahead of the MFMAs that read it.
+// operand row (32 bf16 or 64 fp8); LDS holds two slots, each a pair of
+// consecutive stages (128 bytes of K per row). Every operand reaches LDS by
+// direct global->LDS copies (global_load_lds); a slot is refilled with the
+// pair after next while the other slot's pair is being multiplied.
 //
-// Two LDS tile layouts, both 16 KiB per stage for 256 rows or columns:
-//  * K-contiguous operands (row r = K vector in memory): [256 rows][64 B].
-//    LDS reads of 16 bytes serve 8 lanes per bank half; conflict-free when,
-//    in every group of 8 lanes, address bit 7 equals lane bit 3 and the
+// Why pairs of stages: every copy instruction then reads whole 128-byte lines
+// (8 rows x 128 B for K-contiguous operands). On gfx950 a copy costs the
+// address unit about one cache line per two clocks, and HBM delivers whole
+// lines at full rate; 64-byte half-line reads measured half the L2 rate and
+// about 70% of the HBM rate.
+//
+// Two LDS tile layouts, both 32 KiB per slot for 256 rows or columns:
+//  * K-contiguous operands (row r = K vector in memory): [256 rows][128 B].
+//    16-byte LDS reads serve 8 lanes per bank half; they are conflict-free
+//    when, in every group of 8 lanes, address bit 7 equals lane bit 3 and the
 //    16-byte slots (address bits 4-6) differ (measured on gfx950: 64 banks,
 //    256 bytes per clock). MFMA lanes 0-31 read 32 consecutive rows, so row
-//    r is stored at physical row swap13(r) (row bits 1 and 3 exchanged) and
-//    its 16-byte chunk c at c ^ ((r >> 1) & 3).
-//  * K-outer operands (element (k, n) at k*ld + n in memory): [32 k][512 B],
+//    r is stored at physical row swap03(r) (row bits 0 and 3 exchanged) and
+//    its 16-byte chunk c at c ^ (r & 7).
+//  * K-outer operands (element (k, n) at k*ld + n in memory): [64 k][512 B],
 //    16-byte chunk c of k-row k stored at c ^ ((k & 3) << 2). Fragments are
 //    read with ds_read_b64_tr_b16, which hands a 16-lane group the transpose
 //    of the 4 x 16 block its lanes address (lane 4q + p addresses k-row q,
@@ -37,11 +44,12 @@ namespace mok {
 
 constexpr int kThreads = 256;
 constexpr int kStage = 64;                        // K bytes per row per stage
+constexpr int kSlotRow = 128;                     // K bytes per row per LDS slot (2 stages)
 
-MOK_DEV int swap13(int r) { return (r & ~0xA) | ((r >> 2) & 2) | ((r << 2) & 8); }
-// byte offset of 16-byte chunk `chunk` of row `row` in a K-contiguous tile
-MOK_DEV int lds_at(int row, int chunk) { return swap13(row) * kStage + ((chunk ^ ((row >> 1) & 3)) << 4); }
-// byte offset of byte `byte` of k-row k in a K-outer tile
+MOK_DEV int swap03(int r) { return (r & ~0x9) | ((r >> 3) & 1) | ((r & 1) << 3); }
+// byte offset of 16-byte chunk `chunk` (0..7) of row `row` in a K-contiguous slot
+MOK_DEV int lds_at(int row, int chunk) { return swap03(row) * kSlotRow + ((chunk ^ (row & 7)) << 4); }
+// byte offset of byte `byte` of k-row k (0..63) in a K-outer slot
 MOK_DEV int lds_ko(int k, int byte) { return k * 512 + ((((byte >> 4) ^ ((k & 3) << 2))) << 4) + (byte & 15); }
 
 typedef const __attribute__((address_space(3))) uint8_t* lds_cptr;
@@ -113,46 +121,45 @@ struct RowsGateUp {
 };
 
 // ------------------------------------------------------------------ loaders
-// Every loader moves its operand with kDma direct copies per wavefront per
-// stage (dma(kt, t): stage kt into LDS tile t) and supplies this lane's MFMA
-// fragment of 32 rows/columns starting at r0 for a 16-wide bf16 K step kk
-// (frag). Every wavefront issues exactly kDma copies per stage (positions
-// past the end are clamped, never skipped), which the main loop's vmcnt
-// accounting relies on.
+// Every loader copies one pair of stages (slot j = stages 2j, 2j+1) with kDma
+// direct copies per wavefront (dma(j, t)), and supplies this lane's MFMA
+// fragment of 32 rows/columns starting at r0 for half h (stage parity) and
+// 16-wide bf16 K step kk (frag). Every wavefront issues exactly kDma copies
+// per pair (positions past the end are clamped, never skipped).
 
-// K-contiguous operand. One copy instruction fills a 1 KiB window (16
-// physical rows); lane l writes bytes 16*l .. +16 of it, so each lane fetches
-// the global chunk that the layout places at its LDS position.
+// K-contiguous operand. One copy instruction fills a 1 KiB window (8
+// physical rows x 128 B); lane l writes bytes 16*l .. +16 of it, so each lane
+// fetches the global chunk that the layout places at its LDS position.
 template <int R, class Rows>
 struct LoadKD {
-  static constexpr int kDma = R / 64;
+  static constexpr int kDma = R / 32;
   static constexpr int kReads = 1;               // LDS reads per fragment
   Rows src;
-  MOK_DEV void dma(int kt, uint8_t* t) const {
+  MOK_DEV void dma(int j, uint8_t* t) const {
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
 #pragma unroll
     for (int q = 0; q < kDma; ++q) {
-      const int g = w + 4 * q;                   // window g = physical rows 16g .. 16g+15
-      const int row = swap13(16 * g + (l >> 2)); // logical row stored there
-      const int lc = (l & 3) ^ ((row >> 1) & 3); // logical chunk at physical chunk l&3
-      const uint8_t* gp = src.row(row) + kt * kStage + lc * 16;
+      const int g = w + 4 * q;                   // window g = physical rows 8g .. 8g+7
+      const int row = swap03(8 * g + (l >> 3));  // logical row stored there
+      const int lc = (l & 7) ^ (row & 7);        // logical chunk at physical chunk l&7
+      const uint8_t* gp = src.row(row) + j * kSlotRow + lc * 16;
       copy16_to_lds(gp, t + g * 1024);
     }
   }
-  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int kk) {
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id();
-    return *reinterpret_cast<const bf16x8_t*>(t + lds_at(r0 + (l & 31), 2 * kk + (l >> 5)));
+    return *reinterpret_cast<const bf16x8_t*>(t + lds_at(r0 + (l & 31), 4 * h + 2 * kk + (l >> 5)));
   }
 };
 
 // K-outer bf16 operand: element (k, n) at src0 + k*ld + 2n bytes for k <
 // ksplit and src1 + (k - ksplit)*ld + 2n beyond; k-rows >= K read as zero,
 // columns past ncols are clamped (their products land in unstored output).
-// A stage is 32 k-rows of 256 columns; one copy fills 2 k-rows.
+// A slot is 64 k-rows of 256 columns; one copy fills 2 k-rows.
 template <int R>
 struct LoadKO {
   static_assert(R == 256, "K-outer tiles have 256 columns");
-  static constexpr int kDma = 4;
+  static constexpr int kDma = 8;
   static constexpr int kReads = 2;               // LDS reads per fragment
   const uint8_t* src0;
   const uint8_t* src1;
@@ -160,28 +167,27 @@ struct LoadKO {
   int64_t ld;              // bytes between k-rows
   int K;
   int ncols;               // valid columns (multiple of 8, >= 8)
-  MOK_DEV void dma(int kt, uint8_t* t) const {
+  MOK_DEV void dma(int j, uint8_t* t) const {
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
 #pragma unroll
     for (int q = 0; q < kDma; ++q) {
       const int g = w + 4 * q;                   // window g = k-rows 2g, 2g+1
       const int kl = 2 * g + (l >> 5);
       const int c = (l & 31) ^ ((kl & 3) << 2);  // logical chunk at physical chunk l&31
-      const int k = kt * 32 + kl;
+      const int k = j * 64 + kl;
       const int cc = min(c, (ncols >> 3) - 1);
       const uint8_t* gp = k >= K ? kZeroRow + c * 16
                         : (k < ksplit ? src0 + (int64_t)k * ld : src1 + (int64_t)(k - ksplit) * ld) + cc * 16;
       copy16_to_lds(gp, t + g * 1024);
     }
   }
-  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int kk) {
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id(), g = l >> 4, L = l & 15;
     const int n = r0 + 16 * (g & 1) + 4 * (L & 3);
-    const int k = 16 * kk + 8 * (g >> 1) + (L >> 2);
+    const int k = 32 * h + 16 * kk + 8 * (g >> 1) + (L >> 2);
     typedef __attribute__((address_space(3))) v4i16_t* lds_v4_ptr;
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k, 2 * n)));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k + 4, 2 * n)));
-    const v4i16_t x = lo, y = hi;
+    const v4i16_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k, 2 * n)));
+    const v4i16_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4_ptr)(t + lds_ko(k + 4, 2 * n)));
     typedef __attribute__((ext_vector_type(8))) short v8i16_t;
     const v8i16_t v = v8i16_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8_t, v);
@@ -189,17 +195,17 @@ struct LoadKO {
 };
 
 // E8M0 block scales of a 256-row fp8 operand, copied into LDS as one 32-bit
-// word per row holding the scales of K blocks 4j .. 4j+3 (stages 2j and
-// 2j+1; K is a multiple of 128, so the word never runs past the row). Lane l
-// of wavefront w copies the word of row 64w + l.
+// word per row holding the scales of K blocks 4j .. 4j+3 (the two stages of
+// slot j; K is a multiple of 128, so the word never runs past the row). Lane
+// l of wavefront w copies the word of row 64w + l.
 template <int R, class Rows>
 struct LoadScalesD {
   static_assert(R == 256, "scale tiles have 256 rows");
   static constexpr int kDma = 1;
   Rows src;                                      // byte address of each row's scale 0
-  MOK_DEV void dma(int kt, uint8_t* t) const {
+  MOK_DEV void dma(int j, uint8_t* t) const {
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
-    const uint8_t* gp = src.row(64 * w + l) + (kt >> 1) * 4;
+    const uint8_t* gp = src.row(64 * w + l) + j * 4;
     copy4_to_lds(gp, t + 256 * w);
   }
 };
@@ -239,25 +245,22 @@ struct Geo {
   MOK_DEV static int col(int j) { return wn() * WTN + j * 32 + (lane_id() & 31); }
 };
 
-// LDS ring of one tile: NBUF stage buffers per operand, plus per-stage scale
-// words for fp8.
-template <class G, int NBUF, bool SCALES>
+// LDS of one tile: two slots per operand (a pair of stages each), plus the
+// per-row scale words of each slot for fp8.
+template <class G, bool SCALES>
 struct SmemT {
-  static constexpr int kNbuf = NBUF;
-  uint8_t a[NBUF][G::BM * kStage];
-  uint8_t b[NBUF][G::BN * kStage];
+  uint8_t a[2][G::BM * kSlotRow];
+  uint8_t b[2][G::BN * kSlotRow];
 };
-template <class G, int NBUF>
-struct SmemT<G, NBUF, true> {
-  static constexpr int kNbuf = NBUF;
-  uint8_t a[NBUF][G::BM * kStage];
-  uint8_t b[NBUF][G::BN * kStage];
-  uint32_t sa[NBUF][G::BM];
-  uint32_t sb[NBUF][G::BN];
+template <class G>
+struct SmemT<G, true> {
+  uint8_t a[2][G::BM * kSlotRow];
+  uint8_t b[2][G::BN * kSlotRow];
+  uint32_t sa[2][G::BM];
+  uint32_t sb[2][G::BN];
 };
-// 4 buffers (bf16: 128 KiB; fp8: 136 KiB with the scale words)
 template <class G, bool F8>
-using Smem = SmemT<G, 4, F8>;
+using Smem = SmemT<G, F8>;
 
 // LDS bytes of a tile kernel: the ring, or the epilogue's fp32 half-tile
 // (128 rows of BN*4 + 16 bytes) plus a 256-entry row table, if larger.
@@ -272,19 +275,19 @@ MOK_DEV int* tile_rows(uint8_t* lds_raw) {
 }
 
 // ------------------------------------------------------------------ fragments
-// bf16: fragments of one 16-wide K step (kk = 0, 1 within a stage).
+// bf16: fragments of one 16-wide K step (kk = 0, 1 within stage half h).
 template <class G>
 struct FragsB16 {
   bf16x8_t a[G::FM], b[G::FN];
 };
 
 template <class G, class LA, class LB>
-MOK_DEV void read_b16(const uint8_t* ta, const uint8_t* tb, int kk, FragsB16<G>& f) {
+MOK_DEV void read_b16(const uint8_t* ta, const uint8_t* tb, int h, int kk, FragsB16<G>& f) {
   const int r0 = G::wm() * G::WTM, c0 = G::wn() * G::WTN;
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i) f.a[i] = LA::frag(ta, r0 + i * 32, kk);
+  for (int i = 0; i < G::FM; ++i) f.a[i] = LA::frag(ta, r0 + i * 32, h, kk);
 #pragma unroll
-  for (int j = 0; j < G::FN; ++j) f.b[j] = LB::frag(tb, c0 + j * 32, kk);
+  for (int j = 0; j < G::FN; ++j) f.b[j] = LB::frag(tb, c0 + j * 32, h, kk);
 }
 
 // LDS read instructions per fragment, averaged over the two operands
@@ -316,20 +319,20 @@ MOK_DEV i32x8_t cat8(const bf16x8_t& lo8, const bf16x8_t& hi8) {
 }
 
 template <class G>
-MOK_DEV void read_f8_a(const uint8_t* ta, const uint32_t* sa, int i, FragsF8<G>& f) {
+MOK_DEV void read_f8_a(const uint8_t* ta, const uint32_t* sa, int h, int i, FragsF8<G>& f) {
   const int lane = lane_id(), lr = lane & 31, lk = lane >> 5;
   const int r = G::wm() * G::WTM + i * 32 + lr;
-  f.a[i] = cat8(*reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, lk)),
-                *reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, 2 + lk)));
+  f.a[i] = cat8(*reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, 4 * h + lk)),
+                *reinterpret_cast<const bf16x8_t*>(ta + lds_at(r, 4 * h + 2 + lk)));
   f.as[i] = sa[r];
 }
 
 template <class G>
-MOK_DEV void read_f8_b(const uint8_t* tb, const uint32_t* sb, int j, FragsF8<G>& f) {
+MOK_DEV void read_f8_b(const uint8_t* tb, const uint32_t* sb, int h, int j, FragsF8<G>& f) {
   const int lane = lane_id(), lr = lane & 31, lk = lane >> 5;
   const int r = G::wn() * G::WTN + j * 32 + lr;
-  f.b[j] = cat8(*reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, lk)),
-                *reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, 2 + lk)));
+  f.b[j] = cat8(*reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, 4 * h + lk)),
+                *reinterpret_cast<const bf16x8_t*>(tb + lds_at(r, 4 * h + 2 + lk)));
   f.bs[j] = sb[r];
 }
 
@@ -343,28 +346,24 @@ MOK_DEV void mfma_f8(const FragsF8<G>& f, int i, int j, int sh, Acc<G::FM, G::FN
 }
 
 // ------------------------------------------------------------------ main loop
-// nk stages through the LDS ring; one workgroup barrier per stage, placed in
-// the middle of the stage's MFMAs:
+// nk stages, consumed in pairs from the two LDS slots (pair j in slot j%2).
+// Within each stage the MFMAs come in two regions, and the next fragments
+// are read from LDS while a region's MFMAs issue:
 //
-//   region A   first half of stage kt's MFMAs, while fragments of the second
-//              half are read from LDS
-//   barrier    each wavefront first waits for its copies of stage kt+1 and
-//              its LDS reads; afterwards stage kt+1 is visible and no
-//              wavefront reads the buffer of stage kt any more
-//   copies     into buffers whose stages have been read completely
-//   region B   second half of stage kt's MFMAs, while the first fragments
-//              of stage kt+1 are read
+//   stage 2j     region A, region B (no barrier)
+//   stage 2j+1   region A; then every wavefront waits for all its copies
+//                (pair j+1) and LDS reads, and the workgroup barrier makes
+//                pair j+1 visible and guarantees that nobody reads slot j%2
+//                any more; the copies of pair j+2 into slot j%2 are issued;
+//                region B, reading the first fragments of pair j+1
 //
-// Stage kt+4 is copied on every kt, into the buffer of stage kt. (Copying
-// stages in 128-byte-line pairs, which streams HBM better in isolation, was
-// measured slower here.) bf16 halves are the two 16-wide K steps of a stage.
-// fp8 halves are fragment rows 0-1 and 2-3 of the one 64-wide K step; the B
-// fragments of stage kt+1 are read into each B register as soon as its last
-// MFMA of stage kt has issued.
+// So each pair has two stages of MFMAs to arrive, and there is one barrier
+// per pair.
 //
-// Copies complete in issue order, so "stage kt+1 has landed" is a bound on
-// this wavefront's outstanding vector-memory operations: the number of stages
-// issued after it. The last stages issue no copies.
+// bf16 regions are the two 16-wide K steps of a stage. fp8 regions are
+// fragment rows 0-1 and 2-3 of the one 64-wide K step; the B fragments of the
+// next stage are read into each B register as soon as its last MFMA of the
+// current stage has issued.
 template <class SM, class LA, class LB, class SA, class SB>
 struct Pipe {
   static constexpr int kD = LA::kDma + LB::kDma + SA::kDma + SB::kDma;
@@ -373,64 +372,56 @@ struct Pipe {
   const LB& lb;
   const SA& sa;
   const SB& sb;
-  MOK_DEV void dma(int s) const {
-    const int b = s % SM::kNbuf;
-    la.dma(s, sm.a[b]);
-    lb.dma(s, sm.b[b]);
-    if constexpr (SA::kDma > 0) sa.dma(s, reinterpret_cast<uint8_t*>(sm.sa[b]));
-    if constexpr (SB::kDma > 0) sb.dma(s, reinterpret_cast<uint8_t*>(sm.sb[b]));
+  MOK_DEV void dma(int j) const {                // pair j into slot j%2
+    const int b = j & 1;
+    la.dma(j, sm.a[b]);
+    lb.dma(j, sm.b[b]);
+    if constexpr (SA::kDma > 0) sa.dma(j, reinterpret_cast<uint8_t*>(sm.sa[b]));
+    if constexpr (SB::kDma > 0) sb.dma(j, reinterpret_cast<uint8_t*>(sm.sb[b]));
   }
-  // wait until stage kt+1 has landed, given that `left` later stages of
-  // copies (0 .. 3) have been issued since, then barrier
-  MOK_DEV void publish(int left) const {
-    if (left >= 3) wait_vm_lds<3 * kD>();
-    else if (left == 2) wait_vm_lds<2 * kD>();
-    else if (left == 1) wait_vm_lds<kD>();
-    else wait_vm_lds<0>();
+  MOK_DEV void publish() const {                 // all copies landed, all LDS reads done
+    wait_vm_lds<0>();
     barrier_lds();
   }
 };
 
-// copy issue of a stage iteration: none, or stage kt+4
-constexpr int kNoCopy = 0, kCopy = 1;
-
 // scheduling-group masks (llvm.amdgcn.sched.group.barrier)
-constexpr int kSgMfma = 0x008, kSgVmem = 0x020, kSgDsRead = 0x100;
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 template <class G, bool F8, class LA, class LB, class SA, class SB>
 MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
                       Acc<G::FM, G::FN>& acc) {
   using SM = Smem<G, F8>;
-  constexpr int NB = SM::kNbuf;
   using P = Pipe<SM, LA, LB, SA, SB>;
   constexpr int kD = P::kD;
-  static_assert(3 * kD < 64, "vmcnt range");
+  static_assert(kD < 64, "vmcnt range");
+  static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
   const P p{sm, la, lb, sa, sb};
-  auto buf = [](int st) { return st % NB; };
   acc.zero();
   __syncthreads();                               // previous users of the LDS buffers are done
   if (nk <= 0) return;
+  const int np = (nk + 1) >> 1;                  // pairs
 
-  // prologue: copies of stages 0..3, wait for stage 0
+  // prologue: pairs 0 and 1, wait for pair 0
   p.dma(0);
-  if (nk > 1) p.dma(1);
-  if (nk > 2) p.dma(2);
-  if (nk > 3) p.dma(3);
-  if (nk > 3) wait_vm_lds<3 * kD>();
-  else if (nk == 3) wait_vm_lds<2 * kD>();
-  else if (nk == 2) wait_vm_lds<kD>();
-  else wait_vm_lds<0>();
+  if (np > 1) {
+    p.dma(1);
+    wait_vm_lds<kD>();
+  } else {
+    wait_vm_lds<0>();
+  }
   barrier_lds();
 
   if constexpr (!F8) {
-    static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
     FragsB16<G> f0, f1;
-    read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, f0);
-    auto stage = [&](int kt, auto dma_tag, int left) {
-      constexpr int DMA = decltype(dma_tag)::value;
-      const int cur = buf(kt), nxt = buf(kt + 1);
+    read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, 0, f0);
+    // stage kt: K steps 0 (f0, read before) and 1 (f1); reads the first
+    // fragments of stage kt+1 into f0. Odd kt ends its pair: barrier and,
+    // with COPY, the copies of pair kt/2 + 2.
+    auto stage = [&](int kt, bool ODD, bool COPY) {
+      const int j = kt >> 1, slot = j & 1;
       __builtin_amdgcn_sched_barrier(0);
-      read_b16<G, LA, LB>(sm.a[cur], sm.b[cur], 1, f1);
+      read_b16<G, LA, LB>(sm.a[slot], sm.b[slot], ODD ? 1 : 0, 1, f1);
       mfma_b16<G>(f0, acc);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -439,9 +430,12 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       }
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
       __builtin_amdgcn_sched_barrier(0);
-      p.publish(left);
-      if constexpr (DMA == kCopy) p.dma(kt + 4);
-      read_b16<G, LA, LB>(sm.a[nxt], sm.b[nxt], 0, f0);
+      if (ODD) {
+        p.publish();
+        if (COPY) p.dma(j + 2);
+      }
+      const int nslot = ODD ? (slot ^ 1) : slot;
+      read_b16<G, LA, LB>(sm.a[nslot], sm.b[nslot], ODD ? 0 : 1, 0, f0);
       mfma_b16<G>(f1, acc);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -452,29 +446,30 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 4 < nk; ++kt) stage(kt, std::integral_constant<int, kCopy>{}, 2);
-    for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, kNoCopy>{}, min(nk - 2 - kt, 2));
+    for (; kt + 5 < nk; kt += 2) {               // pair kt/2 + 2 exists
+      stage(kt, false, false);
+      stage(kt + 1, true, true);
+    }
+    for (; kt < nk; ++kt) stage(kt, (kt & 1) != 0, (kt & 1) != 0 && kt + 3 < nk);
   } else {
-    static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
     const int sh_lane = 8 * (lane_id() >> 5);
     FragsF8<G> f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) read_f8_a<G>(sm.a[0], sm.sa[0], i, f);
+    for (int i = 0; i < 4; ++i) read_f8_a<G>(sm.a[0], sm.sa[0], 0, i, f);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) read_f8_b<G>(sm.b[0], sm.sb[0], j, f);
-    auto stage = [&](int kt, auto dma_tag, int left) {
-      constexpr int DMA = decltype(dma_tag)::value;
-      const int cur = buf(kt), nxt = buf(kt + 1);
-      const int sh = 16 * (kt & 1) + sh_lane;
+    for (int jj = 0; jj < 4; ++jj) read_f8_b<G>(sm.b[0], sm.sb[0], 0, jj, f);
+    auto stage = [&](int kt, bool ODD, bool COPY) {
+      const int j = kt >> 1, slot = j & 1, h = ODD ? 1 : 0;
+      const int sh = 16 * h + sh_lane;
       // region A: rows 0-1; read rows 2-3 of this stage (rows 0-1 and all B
       // fragments were read during the previous stage)
       __builtin_amdgcn_sched_barrier(0);
-      read_f8_a<G>(sm.a[cur], sm.sa[cur], 2, f);
-      read_f8_a<G>(sm.a[cur], sm.sa[cur], 3, f);
+      read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 2, f);
+      read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 3, f);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_f8<G>(f, i, j, sh, acc);
+        for (int jj = 0; jj < 4; ++jj) mfma_f8<G>(f, i, jj, sh, acc);
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -482,33 +477,37 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       }
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      p.publish(left);
-      if constexpr (DMA == kCopy) p.dma(kt + 4);
+      if (ODD) {
+        p.publish();
+        if (COPY) p.dma(j + 2);
+      }
       // region B: rows 2-3, column block by column block; each B fragment of
-      // stage kt+1 is read once its last MFMA here has issued, rows 0-1 of
-      // stage kt+1 go into the registers region A freed
+      // the next stage is read once its last MFMA here has issued, rows 0-1
+      // of the next stage go into the registers region A freed
+      const int nslot = ODD ? (slot ^ 1) : slot, nh = ODD ? 0 : 1;
       const FragsF8<G> g = f;
-      read_f8_a<G>(sm.a[nxt], sm.sa[nxt], 0, f);
-      read_f8_a<G>(sm.a[nxt], sm.sa[nxt], 1, f);
+      read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 0, f);
+      read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 1, f);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mfma_f8<G>(g, 2, j, sh, acc);
-        mfma_f8<G>(g, 3, j, sh, acc);
-        read_f8_b<G>(sm.b[nxt], sm.sb[nxt], j, f);
+      for (int jj = 0; jj < 4; ++jj) {
+        mfma_f8<G>(g, 2, jj, sh, acc);
+        mfma_f8<G>(g, 3, jj, sh, acc);
+        read_f8_b<G>(sm.b[nslot], sm.sb[nslot], nh, jj, f);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmem, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 4 < nk; ++kt) stage(kt, std::integral_constant<int, kCopy>{}, 2);
-    for (; kt < nk; ++kt) stage(kt, std::integral_constant<int, kNoCopy>{}, min(nk - 2 - kt, 2));
+    for (; kt + 5 < nk; kt += 2) {
+      stage(kt, false, false);
+      stage(kt + 1, true, true);
+    }
+    for (; kt < nk; ++kt) stage(kt, (kt & 1) != 0, (kt & 1) != 0 && kt + 3 < nk);
   }
 }
 
