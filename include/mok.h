@@ -120,7 +120,8 @@ typedef struct {
   size_t mb_tile_start;          /* int32 [n_minibatches + 1]                      */
   size_t n_bwd_tiles;            /* int32       backward row tiles                 */
   size_t bwd_tiles;              /* int32x4 [max_bwd_tiles] {e, p0, p1, 0}          */
-  size_t total;
+  size_t total;                  /* buffer size; the bytes after bwd_tiles are
+                                    scratch of mok_build_schedule              */
   int32_t minibatch_rows;        /* resolved M   */
   int32_t ring_slots;            /* resolved N_s */
   int32_t n_minibatches;         /* ceil(R / M)  */

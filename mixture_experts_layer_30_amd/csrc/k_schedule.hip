@@ -4,24 +4,30 @@
 // the GPU and routed-token counts never travel to the CPU. [MoK card] "Using
 // the functional API": the schedule is built from the top-k expert choices.
 //
-// One workgroup of 16 wavefronts does the whole job:
-//   1. each wave owns a contiguous chunk of flat rows and builds a histogram
-//      of expert ids in LDS; ties inside a 64-row step are ranked with
-//      wavefront ballots (no atomics, so ranks are stable by row index);
-//   2. per-expert totals, their exclusive scan (offsets) and each wave's base
-//      position inside every expert segment;
-//   3. the ranking is replayed to scatter perm[p] = i and dest[i] = p;
-//   4. the row-tile tables for the grouped GEMMs.
+// Three launches, each deterministic (no atomics; ties ranked by row index):
+//   1. hist:    the rows are cut into chunks of equal size; each workgroup
+//               counts the expert ids of its chunk (wavefront ballots group
+//               equal ids inside a 64-row step);
+//   2. scan:    one workgroup turns the chunk counts into per-expert totals,
+//               their exclusive scan (offsets) and the base position of every
+//               chunk inside every expert segment, then writes the row-tile
+//               tables for the grouped GEMMs;
+//   3. scatter: each workgroup replays the ranking of its chunk and writes
+//               perm[p] = i and dest[i] = p.
 // Rows whose id lies outside [0, E) go to an extra bucket E placed after all
 // valid rows; they set status bit 0.
 #include "mok_device.h"
 #include "mok_launch.h"
 
+#include <algorithm>
+
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = kWaves * 64;
-constexpr int kMaxBuckets = 513;   // E <= 512 plus the invalid bucket
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kChunkThreads = 256;               // 4 wavefronts per chunk
+constexpr int kChunkWaves = kChunkThreads / 64;
+constexpr int kMaxBuckets = 513;                 // E <= 512 plus the invalid bucket
 
 MOK_DEV uint64_t lanemask_lt() {
   const int l = lane_id();
@@ -39,7 +45,7 @@ MOK_DEV uint64_t match_mask(int v, bool active, int nbits) {
   return m;
 }
 
-// Exclusive scan of one int per thread over the whole 1024-thread block.
+// Exclusive scan of one int per thread over a 1024-thread block.
 MOK_DEV int block_exclusive_scan(int v, int* sums, int* total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   int incl = v;
@@ -50,18 +56,18 @@ MOK_DEV int block_exclusive_scan(int v, int* sums, int* total) {
   if (lane == 63) sums[wave] = incl;
   __syncthreads();
   if (wave == 0) {
-    int s = lane < kWaves ? sums[lane] : 0;
+    int s = lane < kScanWaves ? sums[lane] : 0;
     int si = s;
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(si, d);
       if (lane >= d) si += o;
     }
-    if (lane < kWaves) sums[kWaves + lane] = si - s;
-    if (lane == kWaves - 1) sums[2 * kWaves] = si;
+    if (lane < kScanWaves) sums[kScanWaves + lane] = si - s;
+    if (lane == kScanWaves - 1) sums[2 * kScanWaves] = si;
   }
   __syncthreads();
-  const int r = incl - v + sums[kWaves + wave];
-  if (total) *total = sums[2 * kWaves];
+  const int r = incl - v + sums[kScanWaves + wave];
+  if (total) *total = sums[2 * kScanWaves];
   __syncthreads();
   return r;
 }
@@ -91,81 +97,89 @@ MOK_DEV void write_tiles(mok_tile* out, int room, int e, int lo, int hi, int cut
   }
 }
 
-__global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __restrict__ ids,
-                                                          mok_sched_ptrs s, int R, int E,
-                                                          int M, int bm_f, int bm_b, int n_mb,
-                                                          int max_f, int max_b) {
-  __shared__ int hist[kWaves][kMaxBuckets];
-  __shared__ int sums[2 * kWaves + 1];
+MOK_DEV int bucket_of(int id, int E) { return (id >= 0 && id < E) ? id : E; }
+
+// Rows of chunk c handled by wavefront w: [lo, hi), contiguous, in order.
+MOK_DEV void wave_rows(int c, int w, int R, int chunk, int& lo, int& hi) {
+  const int per = chunk / kChunkWaves;           // chunk is a multiple of 256
+  lo = min(R, c * chunk + w * per);
+  hi = min(R, lo + per);
+}
+
+// Per-wavefront histograms of one chunk in LDS: h[w][v] += count.
+MOK_DEV void chunk_histogram(const int32_t* ids, int R, int E, int chunk, int nbits,
+                             int (*h)[kMaxBuckets]) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int lo, hi;
+  wave_rows(blockIdx.x, w, R, chunk, lo, hi);
+  for (int base = lo; base < hi; base += 256) {
+    int v[4];
+    bool act[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {                // loads of 4 steps first
+      const int i = base + 64 * u + lane;
+      act[u] = i < hi;
+      v[u] = act[u] ? bucket_of(ids[i], E) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t m = match_mask(v[u], act[u], nbits);
+      if (act[u] && (m & lanemask_lt()) == 0) h[w][v[u]] += __popcll(m);
+    }
+  }
+}
+
+// 1. chunk counts: bh[c * nb + v] = rows of chunk c in bucket v
+__global__ __launch_bounds__(kChunkThreads) void sched_hist_kernel(const int32_t* __restrict__ ids,
+                                                                 int R, int E, int chunk,
+                                                                 int32_t* __restrict__ bh) {
+  __shared__ int h[kChunkWaves][kMaxBuckets];
+  const int nb = E + 1, nbits = 32 - __clz(E);
+  for (int v = threadIdx.x; v < kChunkWaves * kMaxBuckets; v += kChunkThreads) (&h[0][0])[v] = 0;
+  __syncthreads();
+  chunk_histogram(ids, R, E, chunk, nbits, h);
+  __syncthreads();
+  for (int v = threadIdx.x; v < nb; v += kChunkThreads) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kChunkWaves; ++w) t += h[w][v];
+    bh[(int64_t)blockIdx.x * nb + v] = t;
+  }
+}
+
+// 2. totals, offsets, chunk bases (bh becomes the base of chunk c in bucket
+// v), tile tables
+__global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs s, int R, int E,
+                                                                int nchunks, int32_t* __restrict__ bh,
+                                                                int M, int bm_f, int bm_b, int n_mb,
+                                                                int max_f, int max_b) {
+  __shared__ int sums[2 * kScanWaves + 1];
   __shared__ int s_off[kMaxBuckets];
   __shared__ int s_flag;
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int nb = E + 1;                                  // buckets incl. invalid
-  const int nbits = 32 - __clz(E);                       // bits for values 0..E
-  for (int v = tid; v < kWaves * kMaxBuckets; v += kThreads) (&hist[0][0])[v] = 0;
+  const int tid = threadIdx.x, nb = E + 1;
   if (tid == 0) s_flag = 0;
-  __syncthreads();
-
-  const int chunk = ((R + kWaves - 1) / kWaves + 63) & ~63;
-  const int lo = min(R, wave * chunk), hi = min(R, lo + chunk);
-
-  // 1. histogram per wave chunk
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const bool act = i < hi;
-    int v = 0;
-    if (act) {
-      const int id = ids[i];
-      v = (id >= 0 && id < E) ? id : E;
-    }
-    const uint64_t m = match_mask(v, act, nbits);
-    if (act && (m & lanemask_lt()) == 0) hist[wave][v] += __popcll(m);
-  }
-  __syncthreads();
-
-  // 2. totals, exclusive scan over buckets, per-wave bases
-  int my_count = 0;
+  int run = 0;
   if (tid < nb) {
-    int run = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = hist[w][tid];
-      hist[w][tid] = run;
-      run += c;
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t o = (int64_t)c * nb + tid;
+      const int n = bh[o];
+      bh[o] = run;
+      run += n;
     }
-    my_count = run;
   }
+  __syncthreads();
   int nvalid_total = 0;
-  const int excl = block_exclusive_scan(tid < nb ? my_count : 0, sums, &nvalid_total);
+  const int excl = block_exclusive_scan(tid < nb ? run : 0, sums, &nvalid_total);
   if (tid < nb) {
     s_off[tid] = excl;
-    if (tid < E) s.counts[tid] = my_count;
-    s.offsets[tid] = excl;                                // offsets[E] = valid rows
-    if (tid == E && my_count > 0) s_flag = 1;
-    for (int w = 0; w < kWaves; ++w) hist[w][tid] += excl;
+    if (tid < E) s.counts[tid] = run;
+    s.offsets[tid] = excl;                       // offsets[E] = valid rows
+    if (tid == E && run > 0) s_flag = 1;
+    for (int c = 0; c < nchunks; ++c) bh[(int64_t)c * nb + tid] += excl;
   }
   __syncthreads();
 
-  // 3. replay the ranking and scatter
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const bool act = i < hi;
-    int v = 0;
-    if (act) {
-      const int id = ids[i];
-      v = (id >= 0 && id < E) ? id : E;
-    }
-    const uint64_t m = match_mask(v, act, nbits);
-    int p = 0;
-    if (act) p = hist[wave][v] + __popcll(m & lanemask_lt());
-    if (act && (m & lanemask_lt()) == 0) hist[wave][v] += __popcll(m);
-    if (act && (unsigned)p < (unsigned)R) {   // always true for a consistent ranking
-      s.perm[p] = i;
-      s.dest[i] = p;
-    }
-  }
-
-  // 4. row tiles: forward tiles are cut at minibatch boundaries, backward not
+  // row tiles: forward tiles are cut at minibatch boundaries, backward not
   int nf = 0, nbk = 0;
   int lo_e = 0, hi_e = 0;
   if (tid < E) {
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __res
   __syncthreads();
   __threadfence_block();
   // first forward tile of each minibatch: tiles are in ascending p0
-  for (int m = tid; m <= n_mb; m += kThreads) {
+  for (int m = tid; m <= n_mb; m += kScanThreads) {
     const long long target = (long long)m * M;
     int a = 0, b = total_f;
     while (a < b) {
@@ -202,12 +216,75 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const int32_t* __res
   }
 }
 
+// 3. scatter: replay the chunk's ranking from its bases
+__global__ __launch_bounds__(kChunkThreads) void sched_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                    mok_sched_ptrs s, int R, int E,
+                                                                    int chunk,
+                                                                    const int32_t* __restrict__ bh) {
+  __shared__ int h[kChunkWaves][kMaxBuckets];
+  const int nb = E + 1, nbits = 32 - __clz(E);
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  for (int v = threadIdx.x; v < kChunkWaves * kMaxBuckets; v += kChunkThreads) (&h[0][0])[v] = 0;
+  __syncthreads();
+  chunk_histogram(ids, R, E, chunk, nbits, h);
+  __syncthreads();
+  // h[w][v] <- base of wavefront w's rows in bucket v
+  for (int v = threadIdx.x; v < nb; v += kChunkThreads) {
+    int run = bh[(int64_t)blockIdx.x * nb + v];
+#pragma unroll
+    for (int ww = 0; ww < kChunkWaves; ++ww) {
+      const int c = h[ww][v];
+      h[ww][v] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int lo, hi;
+  wave_rows(blockIdx.x, w, R, chunk, lo, hi);
+  for (int base = lo; base < hi; base += 256) {
+    int v[4];
+    bool act[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + 64 * u + lane;
+      act[u] = i < hi;
+      v[u] = act[u] ? bucket_of(ids[i], E) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + 64 * u + lane;
+      const uint64_t m = match_mask(v[u], act[u], nbits);
+      int p = 0;
+      if (act[u]) p = h[w][v[u]] + __popcll(m & lanemask_lt());
+      if (act[u] && (m & lanemask_lt()) == 0) h[w][v[u]] += __popcll(m);
+      if (act[u] && (unsigned)p < (unsigned)R) {   // always true for a consistent ranking
+        s.perm[p] = i;
+        s.dest[i] = p;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+int mok_schedule_chunk_rows(int64_t R) {
+  // rows per chunk: a multiple of 256 rows, at least 1024, at most 2048 chunks
+  const int64_t per = (R + 2047) / 2048;
+  return (int)std::max<int64_t>(1024, (per + 255) / 256 * 256);
+}
 
 hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E,
                                int M, int bm_f, int bm_b, int n_mb, int max_f, int max_b,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, st, ids, s, R, E, M, bm_f,
-                     bm_b, n_mb, max_f, max_b);
+                               int32_t* chunk_counts, hipStream_t st) {
+  const int chunk = mok_schedule_chunk_rows(R);
+  const int nchunks = (R + chunk - 1) / chunk;
+  if (nchunks > 0)
+    hipLaunchKernelGGL(sched_hist_kernel, dim3(nchunks), dim3(kChunkThreads), 0, st, ids, R, E, chunk,
+                       chunk_counts);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(kScanThreads), 0, st, s, R, E, nchunks,
+                     chunk_counts, M, bm_f, bm_b, n_mb, max_f, max_b);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(sched_scatter_kernel, dim3(nchunks), dim3(kChunkThreads), 0, st, ids, s, R, E,
+                       chunk, chunk_counts);
   return hipGetLastError();
 }

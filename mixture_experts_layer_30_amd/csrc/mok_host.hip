@@ -77,7 +77,8 @@ mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
 }
 
 struct SchedLayout {
-  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, total;
+  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, chunk_counts,
+      total;
 };
 
 SchedLayout sched_layout(const Resolved& r) {
@@ -93,6 +94,9 @@ SchedLayout sched_layout(const Resolved& r) {
   L.mb_start = o;  o = align_up(o + 4 * (size_t)(r.n_mb + 1));
   L.n_bwd = o;     o = align_up(o + 4);
   L.bwd_tiles = o; o = align_up(o + sizeof(mok_tile) * (size_t)r.max_bwd_tiles);
+  // scratch of the build: per-chunk counts per bucket
+  const int64_t chunk = mok_schedule_chunk_rows(r.R);
+  L.chunk_counts = o; o = align_up(o + 4 * (size_t)((r.R + chunk - 1) / chunk) * (r.E + 1));
   L.total = o;
   return L;
 }
@@ -293,9 +297,11 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
   if ((s = check_device()) != MOK_OK) return s;
   const mok_sched_ptrs p = sched_ptrs(r, schedule);
   hipStream_t st = (hipStream_t)stream;
+  int32_t* chunk_counts =
+      reinterpret_cast<int32_t*>(static_cast<uint8_t*>(schedule) + sched_layout(r).chunk_counts);
   MOK_RUN("schedule", mok_launch_schedule(topk_ids, p, (int)r.R, r.E, r.M, kTileRowsFwd,
                                           kTileRowsBwd, r.n_mb, r.max_fwd_tiles,
-                                          r.max_bwd_tiles, st));
+                                          r.max_bwd_tiles, chunk_counts, st));
   return MOK_OK;
 }
 

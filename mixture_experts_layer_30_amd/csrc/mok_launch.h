@@ -22,8 +22,12 @@ struct mok_sched_ptrs {
 constexpr int kTileRowsFwd = 256;
 constexpr int kTileRowsBwd = 256;
 
+// Rows per chunk of the schedule's count/scatter passes, and the launches.
+// chunk_counts holds ceil(R / chunk) * (E + 1) ints.
+int mok_schedule_chunk_rows(int64_t R);
 hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E, int M,
-                               int bm_f, int bm_b, int n_mb, int max_f, int max_b, hipStream_t st);
+                               int bm_f, int bm_b, int n_mb, int max_f, int max_b,
+                               int32_t* chunk_counts, hipStream_t st);
 
 // Gather: for permuted rows p in [p_begin, p_begin + rows) that are valid
 // (p < offsets[E]), copy x[perm[p] / topk] to dst row (p - p_begin).
