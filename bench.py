@@ -34,6 +34,39 @@ GEMM_FLOPS_PER_ROW = {
 }
 
 
+# HBM traffic of the GEMM kernels, from rocprofv3 counter runs of this bench
+# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy of known
+# size); valid only for the kernel sources and workload it was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gemm_traffic_bf16_T4096_H2048_E64_k8_I768.txt")
+KERNEL_SOURCES = ["gemm_core.h", "k_gemm.hip", "mok_device.h", "mok_launch.h", "mok_host.hip"]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_30_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, p, minibatch_rows):
+    """(bytes per launch, source) for `kernel`, or (None, reason)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.loads([ln for ln in f if ln.startswith("{")][-1])
+    except (OSError, IndexError, ValueError):
+        return None, "no traffic record"
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    if rec.get("workload") != p.name or rec.get("minibatch_rows") != minibatch_rows:
+        return None, "counters were taken on another workload"
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None, "no record for this kernel"
+    return k["bytes_per_launch"], os.path.relpath(TRAFFIC_FILE, ROOT)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -51,6 +84,8 @@ def parse():
     ap.add_argument("--driver", type=int, default=0)
     ap.add_argument("--minibatch-rows", type=int, default=0)
     ap.add_argument("--ring-slots", type=int, default=0)
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step only (no forward-only or MXFP8 legs); for counter runs")
     return ap.parse_args()
 
 
@@ -158,25 +193,28 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     ms_step, stats = timed(step, args.steps, trace=True)
-    log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
-    ms_fwd, fstats = timed(fwd_only, args.steps, trace=True)
+    ms_fwd = ms_mx = None
+    mxstats = {}
+    if not args.only_step:
+        log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
+        ms_fwd, _ = timed(fwd_only, args.steps, trace=True)
 
-    # MXFP8 forward on the same workload: weights pre-quantized once (outside
-    # the timed region), x quantized on the fly inside mok_forward.
-    log("[bench] MXFP8 forward timing")
-    wsm = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=False, **cfg)
-    qweights = F.quantize_weights(*weights)
-    ymx = torch.empty_like(dx_)
+        # MXFP8 forward on the same workload: weights pre-quantized once
+        # (outside the timed region), x quantized on the fly inside mok_forward.
+        log("[bench] MXFP8 forward timing")
+        wsm = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=False, **cfg)
+        qweights = F.quantize_weights(*weights)
+        ymx = torch.empty_like(dx_)
 
-    def fwd_mx():
-        mok.build_schedule(wsm.problem, dids, wsm.schedule, wsm.config, stream)
-        mok.forward(wsm.problem, wsm.schedule, dx_, dw_, qweights, ymx, wsm.workspace, None,
-                    wsm.config, stream)
+        def fwd_mx():
+            mok.build_schedule(wsm.problem, dids, wsm.schedule, wsm.config, stream)
+            mok.forward(wsm.problem, wsm.schedule, dx_, dw_, qweights, ymx, wsm.workspace, None,
+                        wsm.config, stream)
 
-    for _ in range(2):
-        fwd_mx()
-    ms_mx, mxstats = timed(fwd_mx, args.steps, trace=True)
-    del wsm
+        for _ in range(2):
+            fwd_mx()
+        ms_mx, mxstats = timed(fwd_mx, args.steps, trace=True)
+        del wsm
 
     R, H, I = p.R, p.H, p.I
     flops_step = p.fwd_flops() + p.bwd_flops()
@@ -196,10 +234,12 @@ def main():
     dn = stats[dom][0]
     dom_flops_per_launch = GEMM_FLOPS_PER_ROW[dom] * R * H * I * args.steps / dn
     achieved = gemms[dom]["tflops"]
+    mb_rows = mok.schedule_layout(ws.problem, ws.config).minibatch_rows
+    traffic, traffic_src = measured_traffic(dom, p, mb_rows)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "flops_per_launch": dom_flops_per_launch,
-                "avg_launch_ms": stats[dom][1] / dn}
+                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
+                "flops_per_launch": dom_flops_per_launch, "avg_launch_ms": stats[dom][1] / dn}
     move = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
                for k in ("schedule", "gather", "combine", "reverse_combine", "bwd_gather",
                          "reverse_dispatch"))
@@ -215,24 +255,26 @@ def main():
                    or mok.schedule_layout(ws.problem, ws.config).minibatch_rows,
                    "ring_slots": mok.schedule_layout(ws.problem, ws.config).ring_slots,
                    "driver": {0: "default (launch-per-minibatch)", 1: "launch-per-minibatch",
-                              2: "persistent"}[args.driver]},
+                              2: "persistent (not provided)"}[args.driver]},
         "tokens_per_s": round(p.T / (ms_step * 1e-3), 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
         "sched_gather_combine_share": round(move / ms_step, 4),
         "schedule_share": round(kernels.get("schedule", {}).get("ms_per_step", 0.0) / ms_step, 4),
-        "forward": {"ms": round(ms_fwd, 4), "tflops": round(fwd_flops / (ms_fwd * 1e-3) / 1e12, 2),
-                    "tokens_per_s": round(p.T / (ms_fwd * 1e-3), 1)},
         "kernels": kernels,
         "roofline": roofline,
-        "mxfp8_forward": {
+    }
+    if ms_fwd is not None:
+        out["forward"] = {"ms": round(ms_fwd, 4), "tflops": round(fwd_flops / (ms_fwd * 1e-3) / 1e12, 2),
+                          "tokens_per_s": round(p.T / (ms_fwd * 1e-3), 1)}
+    if ms_mx is not None:
+        out["mxfp8_forward"] = {
             "ms": round(ms_mx, 4), "tflops": round(fwd_flops / (ms_mx * 1e-3) / 1e12, 2),
             "pct_fp8_peak": round(100 * fwd_flops / (ms_mx * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
             "tokens_per_s": round(p.T / (ms_mx * 1e-3), 1),
             "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
                             for k, v in mxstats.items() if k in GEMM_FLOPS_PER_ROW},
-        },
-    }
+        }
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(p, x, ids, w, wg, wu, wd, dy, min(args.cpu_tokens, p.T),

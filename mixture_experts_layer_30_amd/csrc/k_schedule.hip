@@ -84,13 +84,17 @@ MOK_DEV int count_tiles(int lo, int hi, int cut, int bm) {
   return n;
 }
 
-MOK_DEV void write_tiles(mok_tile* out, int room, int e, int lo, int hi, int cut, int bm) {
+// Writes the tiles of one expert segment; with mb_start, a tile that begins
+// at a multiple of `cut` records its table index (first + n) there.
+MOK_DEV void write_tiles(mok_tile* out, int room, int e, int lo, int hi, int cut, int bm,
+                         int32_t* mb_start, int first) {
   int n = 0;
   for (int p = lo; p < hi;) {
     const int end = min(hi, (p / cut + 1) * cut);
     for (int q = p; q < end && n < room; q += bm) {
       mok_tile t;
       t.e = e; t.p0 = q; t.p1 = min(q + bm, end); t.m = q / cut;
+      if (mb_start && q % cut == 0) mb_start[q / cut] = first + n;
       out[n++] = t;
     }
     p = end;
@@ -158,13 +162,15 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs
   __shared__ int s_flag;
   const int tid = threadIdx.x, nb = E + 1;
   if (tid == 0) s_flag = 0;
+  constexpr int kBatch = 16;                     // chunk counts loaded per round trip
   int run = 0;
   if (tid < nb) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t o = (int64_t)c * nb + tid;
-      const int n = bh[o];
-      bh[o] = run;
-      run += n;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int n[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) n[u] = c0 + u < nchunks ? bh[(int64_t)(c0 + u) * nb + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) run += n[u];
     }
   }
   __syncthreads();
@@ -175,7 +181,17 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs
     if (tid < E) s.counts[tid] = run;
     s.offsets[tid] = excl;                       // offsets[E] = valid rows
     if (tid == E && run > 0) s_flag = 1;
-    for (int c = 0; c < nchunks; ++c) bh[(int64_t)c * nb + tid] += excl;
+    int base = excl;
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int n[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) n[u] = c0 + u < nchunks ? bh[(int64_t)(c0 + u) * nb + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (c0 + u < nchunks) bh[(int64_t)(c0 + u) * nb + tid] = base;
+        base += n[u];
+      }
+    }
   }
   __syncthreads();
 
@@ -191,28 +207,24 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs
   int total_f = 0, total_b = 0;
   const int start_f = block_exclusive_scan(nf, sums, &total_f);
   const int start_b = block_exclusive_scan(nbk, sums, &total_b);
-  if (tid < E) {
-    write_tiles(s.fwd_tiles + start_f, max_f - start_f, tid, lo_e, hi_e, M, bm_f);
-    write_tiles(s.bwd_tiles + start_b, max_b - start_b, tid, lo_e, hi_e, 0x7FFFFFFF, bm_b);
-  }
   total_f = min(total_f, max_f);
   total_b = min(total_b, max_b);
+  // First forward tile of each minibatch m: every m*M below the valid-row
+  // count starts a tile (forward tiles are cut at multiples of M and expert
+  // segments tile [0, valid rows)); minibatches past the valid rows start at
+  // the end of the table.
+  const int nvalid = s_off[E];
+  for (int m = tid; m <= n_mb; m += kScanThreads)
+    if ((int64_t)m * M >= nvalid) s.mb_tile_start[m] = total_f;
+  if (tid < E) {
+    write_tiles(s.fwd_tiles + start_f, max_f - start_f, tid, lo_e, hi_e, M, bm_f, s.mb_tile_start,
+                start_f);
+    write_tiles(s.bwd_tiles + start_b, max_b - start_b, tid, lo_e, hi_e, 0x7FFFFFFF, bm_b, nullptr, 0);
+  }
   if (tid == 0) {
     *s.n_fwd_tiles = total_f;
     *s.n_bwd_tiles = total_b;
     *s.status = s_flag ? 1 : 0;
-  }
-  __syncthreads();
-  __threadfence_block();
-  // first forward tile of each minibatch: tiles are in ascending p0
-  for (int m = tid; m <= n_mb; m += kScanThreads) {
-    const long long target = (long long)m * M;
-    int a = 0, b = total_f;
-    while (a < b) {
-      const int c = (a + b) >> 1;
-      if ((long long)s.fwd_tiles[c].p0 < target) a = c + 1; else b = c;
-    }
-    s.mb_tile_start[m] = a;
   }
 }
 
