@@ -65,7 +65,7 @@ typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
 
 /* Status word bits written by mok_build_schedule (read it whenever you like). */
 #define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
-#define MOK_STATUS_WATCHDOG      0x2   /* a persistent-driver wait timed out      */
+#define MOK_STATUS_WATCHDOG      0x2   /* reserved (persistent driver, not provided) */
 
 /* Problem shape. Supported: T >= 1, 1 <= topk <= E <= 512, T*topk < 2^31,
  * H and I multiples of 128. dtype MOK_MXFP8 is forward-only. */
@@ -95,7 +95,7 @@ typedef struct {
   int32_t driver;                /* 0 = default (= 1), 1 = one launch per
                                     minibatch stage (gather, gate/up, down),
                                     2 = one persistent launch for all minibatches
-                                    (currently returns MOK_ERR_UNSUPPORTED).      */
+                                    (not provided: MOK_ERR_UNSUPPORTED).          */
 } mok_config;
 
 typedef struct {
