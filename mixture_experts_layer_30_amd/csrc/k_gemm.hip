@@ -20,16 +20,18 @@ namespace {
 using G256 = Geo<256, 256, 2, 2>;
 
 // ================================================================== forward
-// A forward tile: row tile ti of minibatch m (rows in ring slot m mod N_s).
+// A forward tile: row tile ti, of minibatch m = tiles[ti].m (rows in ring
+// slot m mod N_s).
 struct FwdTile {
   mok_tile t;
   int nrows;
   int64_t slot_row0;     // ring row of the tile's first row
 };
 
-MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int m, int ti, FwdTile& ft) {
+MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int ti, FwdTile& ft) {
   ft.t = a.tiles[ti];
   ft.nrows = ft.t.p1 - ft.t.p0;
+  const int m = ft.t.m;
   ft.slot_row0 = (int64_t)(m % a.n_slots) * a.M + (ft.t.p0 - (int64_t)m * a.M);
 }
 
@@ -37,11 +39,11 @@ MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int m, int ti, FwdTile& ft) {
 // groups alternating Wg and Wu, so accumulator column blocks j = 2jj (gate) and
 // 2jj + 1 (up) cover the same 32 h-columns.
 template <bool F8>
-MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti, int ny) {
+MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) {
   using G = G256;
   Smem<G, F8>& sm = *reinterpret_cast<Smem<G, F8>*>(lds_raw);
   FwdTile ft;
-  fwd_tile_at(a, m, ti, ft);
+  fwd_tile_at(a, ti, ft);
   const int64_t H = a.H, I = a.I;
   const int n0 = ny * (G::BN / 2);
   const int64_t xrow = F8 ? H : 2 * H;                       // bytes per X row
@@ -143,11 +145,11 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti,
 // down GEMM of one row tile x 256 output columns; each row is pushed to its
 // flat position perm[p] of obuf (unique destinations, no atomics).
 template <bool F8>
-MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti, int ny) {
+MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) {
   using G = G256;
   Smem<G, F8>& sm = *reinterpret_cast<Smem<G, F8>*>(lds_raw);
   FwdTile ft;
-  fwd_tile_at(a, m, ti, ft);
+  fwd_tile_at(a, ti, ft);
   const int64_t H = a.H, I = a.I;
   const int n0 = ny * G::BN;
   const int64_t hrow = F8 ? I : 2 * I;
@@ -172,25 +174,25 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int m, int ti, i
                      [&](int r) { return ob + (int64_t)rows[r] * H; });
 }
 
-// Launch grids are 1-D upper bounds; the tile count of minibatch m is read
-// on the device and the logical tile order is XCD-aware (xcd_tile), row-major
-// over (row tile, column tile).
+// One launch covers the tiles of minibatches [m0, m1). Launch grids are 1-D
+// upper bounds; the tile count is read on the device and the logical tile
+// order is XCD-aware (xcd_tile), row-major over (row tile, column tile).
 template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m, int ncol) {
+__global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m0, int m1, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
-  const int t0 = a.mb_tile_start[m];
-  const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
+  const int t0 = a.mb_tile_start[m0];
+  const int L = xcd_tile((a.mb_tile_start[m1] - t0) * ncol);
   if (L < 0) return;
-  gateup_tile<F8>(a, lds_raw, m, t0 + L / ncol, L % ncol);
+  gateup_tile<F8>(a, lds_raw, t0 + L / ncol, L % ncol);
 }
 
 template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m, int ncol) {
+__global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m0, int m1, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
-  const int t0 = a.mb_tile_start[m];
-  const int L = xcd_tile((a.mb_tile_start[m + 1] - t0) * ncol);
+  const int t0 = a.mb_tile_start[m0];
+  const int L = xcd_tile((a.mb_tile_start[m1] - t0) * ncol);
   if (L < 0) return;
-  down_tile<F8>(a, lds_raw, m, t0 + L / ncol, L % ncol);
+  down_tile<F8>(a, lds_raw, t0 + L / ncol, L % ncol);
 }
 
 // ================================================================== backward
@@ -340,21 +342,21 @@ unsigned cdivu(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 unsigned grid8(int64_t n) { return (unsigned)((n + kXcds - 1) / kXcds * kXcds); }
 
-hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+hipError_t mok_launch_gateup(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                              hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN / 2);
-  const dim3 grid(grid8((int64_t)max_tiles_mb * ncol));
-  if (mxfp8) hipLaunchKernelGGL(gateup_kernel<true>, grid, dim3(kThreads), 0, st, a, m, ncol);
-  else hipLaunchKernelGGL(gateup_kernel<false>, grid, dim3(kThreads), 0, st, a, m, ncol);
+  const dim3 grid(grid8((int64_t)max_tiles * ncol));
+  if (mxfp8) hipLaunchKernelGGL(gateup_kernel<true>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
+  else hipLaunchKernelGGL(gateup_kernel<false>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   return hipGetLastError();
 }
 
-hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                            hipStream_t st) {
   const int ncol = (int)cdivu(a.H, G256::BN);
-  const dim3 grid(grid8((int64_t)max_tiles_mb * ncol));
-  if (mxfp8) hipLaunchKernelGGL(down_kernel<true>, grid, dim3(kThreads), 0, st, a, m, ncol);
-  else hipLaunchKernelGGL(down_kernel<false>, grid, dim3(kThreads), 0, st, a, m, ncol);
+  const dim3 grid(grid8((int64_t)max_tiles * ncol));
+  if (mxfp8) hipLaunchKernelGGL(down_kernel<true>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
+  else hipLaunchKernelGGL(down_kernel<false>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ struct Resolved {
   bool mx;
   int driver;
   int M, n_slots, n_mb;
-  int max_fwd_tiles, max_bwd_tiles, max_tiles_mb;
+  int max_fwd_tiles, max_bwd_tiles;
 };
 
 mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
@@ -72,7 +72,6 @@ mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
   r->n_slots = ns;
   r->max_fwd_tiles = (int)(cdiv(R, kTileRowsFwd) + r->E + r->n_mb + 1);
   r->max_bwd_tiles = (int)(cdiv(R, kTileRowsBwd) + r->E + 1);
-  r->max_tiles_mb = (int)std::min<int64_t>(cdiv(M, kTileRowsFwd) + r->E, r->max_fwd_tiles);
   return MOK_OK;
 }
 
@@ -354,17 +353,20 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
     xsrc = ws + W.xq;
     xscales = ws + W.xqs;
   }
-  {
-    for (int m = 0; m < r.n_mb; ++m) {
-      const int64_t p0 = (int64_t)m * r.M;
-      const int64_t rows = std::min<int64_t>(r.M, r.R - p0);
-      const size_t slot_row = (size_t)(m % r.n_slots) * r.M;
-      MOK_RUN("gather", mok_launch_gather(xsrc, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows,
-                                          a.ring_x + slot_row * xrow, xscales, srow,
-                                          r.mx ? a.ring_xs + slot_row * srow : nullptr, st));
-      MOK_RUN("gateup_gemm", mok_launch_gateup(a, m, r.max_tiles_mb, r.mx, st));
-      MOK_RUN("down_gemm", mok_launch_down(a, m, r.max_tiles_mb, r.mx, st));
-    }
+  // Minibatches go through the ring N_s at a time: the group [m0, m1) with
+  // m0 a multiple of N_s occupies slots 0 .. m1-m0-1, i.e. one contiguous
+  // window of the ring, so each stage is one launch per group (one launch
+  // per minibatch would add a partly filled last wave per minibatch).
+  for (int m0 = 0; m0 < r.n_mb; m0 += r.n_slots) {
+    const int m1 = std::min(r.n_mb, m0 + r.n_slots);
+    const int64_t p0 = (int64_t)m0 * r.M;
+    const int64_t rows = std::min<int64_t>((int64_t)m1 * r.M, r.R) - p0;
+    const int max_tiles = (int)std::min<int64_t>(cdiv(rows, kTileRowsFwd) + r.E + (m1 - m0),
+                                                 r.max_fwd_tiles);
+    MOK_RUN("gather", mok_launch_gather(xsrc, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows,
+                                        a.ring_x, xscales, srow, r.mx ? a.ring_xs : nullptr, st));
+    MOK_RUN("gateup_gemm", mok_launch_gateup(a, m0, m1, max_tiles, r.mx, st));
+    MOK_RUN("down_gemm", mok_launch_down(a, m0, m1, max_tiles, r.mx, st));
   }
   MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
                              static_cast<bf16_t*>(y), st));

@@ -85,11 +85,12 @@ struct mok_fwd_args {
   bf16_t* ab;            // [R][2I] saved pre-activations (NULL = none)
 };
 
-// gate/up GEMM + SwiGLU epilogue over the row tiles of minibatch m.
-hipError_t mok_launch_gateup(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+// gate/up GEMM + SwiGLU epilogue over the row tiles of minibatches
+// [m0, m1) (at most max_tiles tiles).
+hipError_t mok_launch_gateup(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                              hipStream_t st);
-// down GEMM over the row tiles of minibatch m; writes obuf[perm[p]].
-hipError_t mok_launch_down(const mok_fwd_args& a, int m, int max_tiles_mb, bool mxfp8,
+// down GEMM over the row tiles of minibatches [m0, m1); writes obuf[perm[p]].
+hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                            hipStream_t st);
 
 struct mok_bwd_args {
