@@ -86,7 +86,106 @@ def parse():
     ap.add_argument("--ring-slots", type=int, default=0)
     ap.add_argument("--only-step", action="store_true",
                     help="time the step only (no forward-only or MXFP8 legs); for counter runs")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="write the GEMM traffic record from four rocprofv3 counter_collection.csv "
+                         "files (FETCH_SIZE and WRITE_SIZE of a --only-step run, then of a 1 GiB "
+                         "device copy) and exit; needs no GPU")
     return ap.parse_args()
+
+
+# kernel name prefixes (as rocprofv3 prints them) of the bf16 GEMM kernels
+GEMM_KERNEL_NAMES = {
+    "gateup_kernel<false>": "gateup_gemm", "down_kernel<false>": "down_gemm",
+    "bwd_dh_kernel": "bwd_dh_gemm", "bwd_dwd_kernel": "bwd_dwd_gemm",
+    "bwd_dwgu_kernel": "bwd_dwgu_gemm", "bwd_dx_kernel": "bwd_dx_gemm",
+}
+
+
+def _counter_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, counter value)} from a counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                d = int(r["Dispatch_Id"])
+                name, val = r["Kernel_Name"], float(r["Counter_Value"])
+                out[d] = (name, out[d][1] + val if d in out else val)
+    return out
+
+
+def write_traffic_record(args):
+    """Average FETCH_SIZE / WRITE_SIZE per launch of each GEMM kernel, each
+    scaled by what the same counter reads for a 1 GiB device copy, into
+    TRAFFIC_FILE (text summary plus one JSON line that the bench reads)."""
+    import mixture_experts_layer_30_amd as mok
+    from synthetic import CONFIGS
+    fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.traffic_record
+    p = CONFIGS[args.config]
+    cfg = mok.make_config(minibatch_rows=args.minibatch_rows, ring_slots=args.ring_slots)
+    mb_rows = mok.schedule_layout(mok.make_problem(p.T, p.H, p.I, p.E, p.k), cfg).minibatch_rows
+    copy_kib = float(1 << 20)
+
+    def calib(path, counter):
+        vals = [v for n, v in _counter_per_dispatch(path, counter).values() if "copyBuffer" in n]
+        if not vals:
+            raise SystemExit(f"{path}: no copy kernel with {counter}")
+        return copy_kib / max(vals)
+
+    ff, wf = calib(cal_fetch_csv, "FETCH_SIZE"), calib(cal_write_csv, "WRITE_SIZE")
+    per = {}
+    for path, counter, key in ((fetch_csv, "FETCH_SIZE", "fetch_kib"), (write_csv, "WRITE_SIZE", "write_kib")):
+        for name, val in _counter_per_dispatch(path, counter).values():
+            short = next((v for k, v in GEMM_KERNEL_NAMES.items() if k in name), None)
+            if short:
+                per.setdefault(short, {}).setdefault(key, []).append(val)
+    kernels = {}
+    for short in GEMM_KERNEL_NAMES.values():
+        d = per.get(short, {})
+        if not d.get("fetch_kib") or not d.get("write_kib"):
+            continue
+        fk = sum(d["fetch_kib"]) / len(d["fetch_kib"])
+        wk = sum(d["write_kib"]) / len(d["write_kib"])
+        kernels[short] = {"dispatches": len(d["fetch_kib"]), "fetch_kib": round(fk, 1),
+                          "write_kib": round(wk, 1), "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
+    rec = {"workload": p.name, "minibatch_rows": mb_rows, "fetch_factor": round(ff, 4),
+           "write_factor": round(wf, 4), "sources_sha256": kernel_sources_sha256(), "kernels": kernels}
+    extra = f" --minibatch-rows {args.minibatch_rows}" if args.minibatch_rows else ""
+    lines = [
+        f"# HBM traffic of the grouped-GEMM kernels: MoE layer step, bf16, {p.name} "
+        f"(minibatch {mb_rows} rows)",
+        "",
+        "Commands (repository root on an MI355X, ROCm 7.2; one counter per run):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp",
+        f"rocprofv3 --pmc FETCH_SIZE -d <f> -o pmc -f csv -- python3 /root/repo/bench.py --steps 2 --warmup 1 --cpu-tokens 0 --only-step{extra}",
+        f"rocprofv3 --pmc WRITE_SIZE -d <w> -o pmc -f csv -- python3 /root/repo/bench.py --steps 2 --warmup 1 --cpu-tokens 0 --only-step{extra}",
+        "# calibration: a plain 1 GiB device copy (hipMemcpy blit kernel __amd_rocclr_copyBuffer)",
+        "rocprofv3 --pmc FETCH_SIZE -d <cf> -o pmc -f csv -- python3 -c \"import torch; a=torch.ones(2**28, "
+        "device='cuda', dtype=torch.int32); b=torch.empty_like(a); b.copy_(a); torch.cuda.synchronize()\"",
+        "rocprofv3 --pmc WRITE_SIZE -d <cw> -o pmc -f csv -- python3 -c \"(same)\"",
+        f"python3 bench.py{extra} --traffic-record <f>/pmc_counter_collection.csv <w>/pmc_counter_collection.csv "
+        "<cf>/pmc_counter_collection.csv <cw>/pmc_counter_collection.csv",
+        "```",
+        "",
+        f"Calibration: the 1 GiB copy reads FETCH_SIZE = {copy_kib / ff:.1f} KiB and WRITE_SIZE = "
+        f"{copy_kib / wf:.1f} KiB, so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f} "
+        "(the copy moves 1048576 KiB each way).",
+        "",
+        "Per dispatch averages over the run (3 steps, every launch of each kernel):",
+        "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+        "|---|---:|---:|---:|---:|",
+    ]
+    for short, k in kernels.items():
+        lines.append(f"| {short} | {k['dispatches']} | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | "
+                     f"{k['bytes_per_launch'] / 1e6:.1f} MB |")
+    lines += ["", "Machine-readable record (bench.py reads the last line; it reports the traffic only while "
+              "the kernel sources hash to `sources_sha256` and the workload matches):", "", json.dumps(rec)]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(TRAFFIC_FILE, ROOT)}", file=sys.stderr)
 
 
 def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok, reps=1):
@@ -125,6 +224,9 @@ def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok, reps=1):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        write_traffic_record(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)

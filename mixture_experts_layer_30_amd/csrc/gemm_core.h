@@ -135,16 +135,16 @@ struct LoadKD {
   static constexpr int kDma = R / 32;
   static constexpr int kReads = 1;               // LDS reads per fragment
   Rows src;
-  MOK_DEV void dma(int j, uint8_t* t) const {
+  MOK_DEV void dma1(int j, uint8_t* t, int q) const {  // copy q of pair j
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
+    const int g = w + 4 * q;                     // window g = physical rows 8g .. 8g+7
+    const int row = swap03(8 * g + (l >> 3));    // logical row stored there
+    const int lc = (l & 7) ^ (row & 7);          // logical chunk at physical chunk l&7
+    copy16_to_lds(src.row(row) + j * kSlotRow + lc * 16, t + g * 1024);
+  }
+  MOK_DEV void dma(int j, uint8_t* t) const {
 #pragma unroll
-    for (int q = 0; q < kDma; ++q) {
-      const int g = w + 4 * q;                   // window g = physical rows 8g .. 8g+7
-      const int row = swap03(8 * g + (l >> 3));  // logical row stored there
-      const int lc = (l & 7) ^ (row & 7);        // logical chunk at physical chunk l&7
-      const uint8_t* gp = src.row(row) + j * kSlotRow + lc * 16;
-      copy16_to_lds(gp, t + g * 1024);
-    }
+    for (int q = 0; q < kDma; ++q) dma1(j, t, q);
   }
   MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id();
@@ -167,19 +167,20 @@ struct LoadKO {
   int64_t ld;              // bytes between k-rows
   int K;
   int ncols;               // valid columns (multiple of 8, >= 8)
-  MOK_DEV void dma(int j, uint8_t* t) const {
+  MOK_DEV void dma1(int j, uint8_t* t, int q) const {  // copy q of pair j
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
+    const int g = w + 4 * q;                     // window g = k-rows 2g, 2g+1
+    const int kl = 2 * g + (l >> 5);
+    const int c = (l & 31) ^ ((kl & 3) << 2);    // logical chunk at physical chunk l&31
+    const int k = j * 64 + kl;
+    const int cc = min(c, (ncols >> 3) - 1);
+    const uint8_t* gp = k >= K ? kZeroRow + c * 16
+                      : (k < ksplit ? src0 + (int64_t)k * ld : src1 + (int64_t)(k - ksplit) * ld) + cc * 16;
+    copy16_to_lds(gp, t + g * 1024);
+  }
+  MOK_DEV void dma(int j, uint8_t* t) const {
 #pragma unroll
-    for (int q = 0; q < kDma; ++q) {
-      const int g = w + 4 * q;                   // window g = k-rows 2g, 2g+1
-      const int kl = 2 * g + (l >> 5);
-      const int c = (l & 31) ^ ((kl & 3) << 2);  // logical chunk at physical chunk l&31
-      const int k = j * 64 + kl;
-      const int cc = min(c, (ncols >> 3) - 1);
-      const uint8_t* gp = k >= K ? kZeroRow + c * 16
-                        : (k < ksplit ? src0 + (int64_t)k * ld : src1 + (int64_t)(k - ksplit) * ld) + cc * 16;
-      copy16_to_lds(gp, t + g * 1024);
-    }
+    for (int q = 0; q < kDma; ++q) dma1(j, t, q);
   }
   MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id(), g = l >> 4, L = l & 15;
@@ -297,12 +298,16 @@ struct RdPerFrag {
 };
 
 template <class G>
+MOK_DEV void mfma_b16_1(const FragsB16<G>& f, int i, int j, Acc<G::FM, G::FN>& acc) {
+  acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+}
+
+template <class G>
 MOK_DEV void mfma_b16(const FragsB16<G>& f, Acc<G::FM, G::FN>& acc) {
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < G::FN; ++j)
-      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+    for (int j = 0; j < G::FN; ++j) mfma_b16_1<G>(f, i, j, acc);
 }
 
 // fp8: the fragments of one whole stage (one 64-wide scaled K step) and the
@@ -379,6 +384,12 @@ struct Pipe {
     if constexpr (SA::kDma > 0) sa.dma(j, reinterpret_cast<uint8_t*>(sm.sa[b]));
     if constexpr (SB::kDma > 0) sb.dma(j, reinterpret_cast<uint8_t*>(sm.sb[b]));
   }
+  // copy u (0 .. 2*kDma-1) of pair j: A copies first, then B (bf16 only)
+  MOK_DEV void dma_unit(int j, int u) const {
+    const int b = j & 1;
+    if (u < LA::kDma) la.dma1(j, sm.a[b], u);
+    else lb.dma1(j, sm.b[b], u - LA::kDma);
+  }
   MOK_DEV void publish() const {                 // all copies landed, all LDS reads done
     wait_vm_lds<0>();
     barrier_lds();
@@ -413,44 +424,52 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
   barrier_lds();
 
   if constexpr (!F8) {
+    static_assert(LA::kDma == 8 && LB::kDma == 8, "16 copies per pair");
     FragsB16<G> f0, f1;
     read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, 0, f0);
-    // stage kt: K steps 0 (f0, read before) and 1 (f1); reads the first
-    // fragments of stage kt+1 into f0. Odd kt ends its pair: barrier and,
-    // with COPY, the copies of pair kt/2 + 2.
-    auto stage = [&](int kt, bool ODD, bool COPY) {
+    // One region: the 16 MFMAs of fragments f while the 8 fragments of the
+    // next K step are read into n; the reads go with the first 8 MFMAs, and
+    // with CP >= 0 copies 8*CP' .. 8*CP'+7 of pair cp follow the last 8, one
+    // after each MFMA, so that the copies never stall MFMA issue in a burst.
+    auto region = [&](const FragsB16<G>& f, FragsB16<G>& n, const uint8_t* ta, const uint8_t* tb, int h,
+                      int kk, int cp, int half) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_b16<G, LA, LB>(ta, tb, h, kk, n);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) mfma_b16_1<G>(f, t >> 2, t & 3, acc);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        mfma_b16_1<G>(f, 2 + (t >> 2), t & 3, acc);
+        if (cp >= 0) p.dma_unit(cp, 8 * half + t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // stage kt: K steps 0 (f0, read before) and 1 (f1). An odd stage ends its
+    // pair j: barrier, then (COPY) the A copies of pair j+2 spread over its
+    // second region; the following even stage spreads the B copies of that
+    // pair over its first region (PEND).
+    auto stage = [&](int kt, bool ODD, bool COPY, bool PEND) {
       const int j = kt >> 1, slot = j & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      read_b16<G, LA, LB>(sm.a[slot], sm.b[slot], ODD ? 1 : 0, 1, f1);
-      mfma_b16<G>(f0, acc);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ODD) {
-        p.publish();
-        if (COPY) p.dma(j + 2);
-      }
+      region(f0, f1, sm.a[slot], sm.b[slot], ODD ? 1 : 0, 1, PEND ? j + 1 : -1, 1);
+      if (ODD) p.publish();
       const int nslot = ODD ? (slot ^ 1) : slot;
-      read_b16<G, LA, LB>(sm.a[nslot], sm.b[nslot], ODD ? 0 : 1, 0, f0);
-      mfma_b16<G>(f1, acc);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      region(f1, f0, sm.a[nslot], sm.b[nslot], ODD ? 0 : 1, 0, COPY ? j + 2 : -1, 0);
     };
     int kt = 0;
     for (; kt + 5 < nk; kt += 2) {               // pair kt/2 + 2 exists
-      stage(kt, false, false);
-      stage(kt + 1, true, true);
+      stage(kt, false, false, kt >= 2);
+      stage(kt + 1, true, true, false);
     }
-    for (; kt < nk; ++kt) stage(kt, (kt & 1) != 0, (kt & 1) != 0 && kt + 3 < nk);
+    for (; kt < nk; ++kt) {
+      const bool odd = (kt & 1) != 0;
+      stage(kt, odd, odd && (kt >> 1) + 2 < np, !odd && kt >= 2 && (kt >> 1) + 1 < np);
+    }
   } else {
     const int sh_lane = 8 * (lane_id() >> 5);
     FragsF8<G> f;
