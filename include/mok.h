@@ -168,7 +168,10 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
  * i; then y[t] = sum_{j=0..k-1} topk_w[t][j] * out[t*k + j], accumulated in
  * fp32 in ascending j and rounded once to bf16.
  * fwd_ctx: NULL for inference; else receives what mok_backward needs
- * (bf16 only). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
+ * (bf16 only): the expert outputs, the gate/up pre-activations and the
+ * gathered x rows in permuted order (so with a context, X rows are gathered
+ * straight to their permuted positions there and the ring reuses only the
+ * h slots). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
  * mok_mxfp8_quantize): x rows are quantized along H and h along I the same
  * way on the fly; accumulation is fp32, y is bf16. */
 mok_status mok_forward(const mok_problem* problem, const mok_config* config,
@@ -177,7 +180,8 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward (bf16). [MoK clip] How-to item 2: reverse-combine then
- * reverse-dispatch with the same schedule. Outputs:
+ * reverse-dispatch with the same schedule. x must be the forward's input;
+ * the weight gradients read its gathered rows from fwd_ctx. Outputs:
  *   d_topk_w[t][j] = <dy[t], out[t*k+j]>           (fp32)
  *   dx [T][H], dw_gate/dw_up [E][I][H], dw_down [E][H][I]   (bf16)
  * Every reduction runs in a fixed order with no atomics; an expert with no

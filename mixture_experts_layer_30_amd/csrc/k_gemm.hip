@@ -26,6 +26,7 @@ struct FwdTile {
   mok_tile t;
   int nrows;
   int64_t slot_row0;     // ring row of the tile's first row
+  int64_t x_row0;        // row of the tile's first row in ring_x
 };
 
 MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int ti, FwdTile& ft) {
@@ -33,6 +34,7 @@ MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int ti, FwdTile& ft) {
   ft.nrows = ft.t.p1 - ft.t.p0;
   const int m = ft.t.m;
   ft.slot_row0 = (int64_t)(m % a.n_slots) * a.M + (ft.t.p0 - (int64_t)m * a.M);
+  ft.x_row0 = a.x_resident ? ft.t.p0 : ft.slot_row0;
 }
 
 // gate/up GEMM + SwiGLU of one row tile x 128 h-columns. The B tile holds 32-row
@@ -49,12 +51,12 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
   const int64_t xrow = F8 ? H : 2 * H;                       // bytes per X row
   const int64_t wrow = F8 ? H : 2 * H;                       // bytes per weight row
   const int64_t eoff = (int64_t)ft.t.e * I * wrow;
-  LoadKD<G::BM, RowsStrided> la{{a.ring_x + ft.slot_row0 * xrow, xrow, ft.nrows}};
+  LoadKD<G::BM, RowsStrided> la{{a.ring_x + ft.x_row0 * xrow, xrow, ft.nrows}};
   LoadKD<G::BN, RowsGateUp> lb{{(const uint8_t*)a.wg + eoff, (const uint8_t*)a.wu + eoff, wrow, n0, (int)I}};
   Acc<G::FM, G::FN> acc;
   if constexpr (F8) {
     const int64_t sx = H / 32;
-    LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_xs + ft.slot_row0 * sx, sx, ft.nrows}};
+    LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_xs + ft.x_row0 * sx, sx, ft.nrows}};
     const int64_t se = (int64_t)ft.t.e * I * sx;
     LoadScalesD<G::BN, RowsGateUp> lsb{{a.sg + se, a.su + se, sx, n0, (int)I}};
     mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);

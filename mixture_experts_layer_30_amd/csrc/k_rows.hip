@@ -45,7 +45,15 @@ __global__ __launch_bounds__(256) void gather_kernel(
   const uint4* src = reinterpret_cast<const uint4*>(x + t * row_bytes);
   uint4* d = reinterpret_cast<uint4*>(dst + r * row_bytes);
   const int64_t n16 = row_bytes >> 4;
-  for (int64_t c = lane; c < n16; c += 64) d[c] = src[c];
+  int64_t c = lane;
+  for (; c + 192 < n16; c += 256) {              // four loads in flight per lane
+    const uint4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
+    d[c] = v0;
+    d[c + 64] = v1;
+    d[c + 128] = v2;
+    d[c + 192] = v3;
+  }
+  for (; c < n16; c += 64) d[c] = src[c];
   if (scales) {
     const uint32_t* ss = reinterpret_cast<const uint32_t*>(scales + t * sbytes);
     uint32_t* ds = reinterpret_cast<uint32_t*>(dst_scales + r * sbytes);
@@ -55,6 +63,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
 
 // ------------------------------------------------------------------ combine
 // One thread per (token, 8 columns). y = sum over j ascending of w*o in fp32.
+// The k rows are read 8 at a time before any is used, so their loads
+// overlap (rows of invalid ids and j >= k read a valid row and are dropped).
 __global__ __launch_bounds__(256) void combine_kernel(
     const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
@@ -65,14 +75,26 @@ __global__ __launch_bounds__(256) void combine_kernel(
   if (t >= T) return;
   const int nvalid = *offsets_E;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int64_t i = t * topk + j;
-    if (dest[i] >= nvalid) continue;
-    const float wj = w ? w[i] : 1.0f;
-    float o[8];
-    unpack8(reinterpret_cast<const uint4*>(obuf + i * H)[c], o);
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    uint4 v[8];
+    float wv[8];
+    bool ok[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj, o[q], acc[q]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int64_t i = t * topk + min(j, topk - 1);
+      ok[u] = j < topk && dest[i] < nvalid;
+      wv[u] = w ? w[i] : 1.0f;
+      v[u] = reinterpret_cast<const uint4*>(obuf + i * H)[c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+      float o[8];
+      unpack8(v[u], o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wv[u], o[q], acc[q]);
+    }
   }
   reinterpret_cast<uint4*>(y + t * H)[c] = pack8(acc);
 }
@@ -80,7 +102,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // ------------------------------------------------------------------ reverse-combine
 // One wavefront per token: dw[t][j] = <dy[t], obuf[t*k+j]> reduced in a fixed
 // order (each lane sums its columns in ascending order, then a xor butterfly),
-// and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order.
+// and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order. The k rows go 8 at
+// a time through one pass over the columns, so their loads overlap.
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
@@ -91,30 +114,46 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
   const int nvalid = *offsets_E;
   const int64_t nch = H >> 3;
   const uint4* dyr = reinterpret_cast<const uint4*>(dy + t * H);
-  for (int j = 0; j < topk; ++j) {
-    const int64_t i = t * topk + j;
-    const int p = dest[i];
-    const bool valid = p < nvalid;
-    const float wj = w[i];
-    const uint4* orow = reinterpret_cast<const uint4*>(obuf + i * H);
-    uint4* drow = reinterpret_cast<uint4*>(dO + (int64_t)p * H);
-    float part = 0.f;
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    int64_t row[8];
+    int pos[8];
+    bool ok[8];
+    float wv[8], part[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      row[u] = t * topk + min(j, topk - 1);
+      pos[u] = dest[row[u]];
+      ok[u] = j < topk && pos[u] < nvalid;
+      wv[u] = w[row[u]];
+      part[u] = 0.f;
+    }
     for (int64_t c = lane; c < nch; c += 64) {
-      float g[8], o[8], d[8];
+      float g[8];
       unpack8(dyr[c], g);
-      if (valid) {
-        unpack8(orow[c], o);
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const uint4*>(obuf + row[u] * H)[c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
+        float o[8], d[8];
+        unpack8(v[u], o);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          part = fmaf(g[q], o[q], part);
-          d[q] = wj * g[q];
+          part[u] = fmaf(g[q], o[q], part[u]);
+          d[q] = wv[u] * g[q];
         }
-        drow[c] = pack8(d);
+        reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = pack8(d);
       }
     }
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) part += __shfl_xor(part, s);
-    if (lane == 0) dw[i] = valid ? part : 0.0f;
+    for (int u = 0; u < 8; ++u) {
+      float pt = part[u];
+#pragma unroll
+      for (int s = 32; s >= 1; s >>= 1) pt += __shfl_xor(pt, s);
+      if (lane == 0 && j0 + u < topk) dw[t * topk + j0 + u] = ok[u] ? pt : 0.0f;
+    }
   }
 }
 

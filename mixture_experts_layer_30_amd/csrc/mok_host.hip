@@ -123,7 +123,7 @@ struct FwdWs {
   size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
 };
 struct BwdWs {
-  size_t dO, dab, hb, dxrows, xg, total;
+  size_t dO, dab, hb, dxrows, total;
 };
 
 FwdWs fwd_ws(const Resolved& r) {
@@ -148,17 +148,27 @@ BwdWs bwd_ws(const Resolved& r) {
   w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
-  w.xg = o;     o = align_up(o + (size_t)r.R * 2 * r.H);
   w.total = r.mx ? 0 : o;
   return w;
 }
 
 size_t ws_bytes(const Resolved& r) { return std::max(fwd_ws(r).total, bwd_ws(r).total); }
 
-size_t ctx_bytes(const Resolved& r) {
-  if (r.mx) return 0;
-  return align_up((size_t)r.R * 2 * r.H) + align_up((size_t)r.R * 4 * r.I);
+// fwd_ctx: the down outputs in flat row order [R][H], the gate/up
+// pre-activations a | b [R][2I] and the gathered x in permuted order [R][H].
+struct CtxLayout {
+  size_t obuf, ab, xg, total;
+};
+CtxLayout ctx_layout(const Resolved& r) {
+  CtxLayout c;
+  c.obuf = 0;
+  c.ab = align_up((size_t)r.R * 2 * r.H);
+  c.xg = c.ab + align_up((size_t)r.R * 4 * r.I);
+  c.total = c.xg + align_up((size_t)r.R * 2 * r.H);
+  return c;
 }
+
+size_t ctx_bytes(const Resolved& r) { return r.mx ? 0 : ctx_layout(r).total; }
 
 // gfx950 check and compute-unit count, once per device (device properties
 // only; no device memory is touched).
@@ -337,8 +347,14 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   a.ring_x = ws + W.ring_x; a.ring_xs = ws + W.ring_xs;
   a.ring_h = ws + W.ring_h; a.ring_hs = ws + W.ring_hs;
   uint8_t* ctx = static_cast<uint8_t*>(fwd_ctx);
-  a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx : ws + W.obuf);
-  a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + align_up((size_t)r.R * 2 * r.H)) : nullptr;
+  const CtxLayout C = ctx_layout(r);
+  a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx + C.obuf : ws + W.obuf);
+  a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + C.ab) : nullptr;
+  // With a context the gathered rows go straight to their permuted
+  // positions in it (the backward's weight gradients read them there), so
+  // X ring slots are not reused; h still cycles through the ring.
+  a.x_resident = ctx ? 1 : 0;
+  if (ctx) a.ring_x = ctx + C.xg;
 
   // MXFP8: x is quantized once per token (blocks lie inside a row, so this is
   // bitwise the same as quantizing each gathered row), then fp8 rows and their
@@ -363,8 +379,9 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
     const int64_t rows = std::min<int64_t>((int64_t)m1 * r.M, r.R) - p0;
     const int max_tiles = (int)std::min<int64_t>(cdiv(rows, kTileRowsFwd) + r.E + (m1 - m0),
                                                  r.max_fwd_tiles);
+    uint8_t* xdst = a.x_resident ? a.ring_x + p0 * xrow : a.ring_x;
     MOK_RUN("gather", mok_launch_gather(xsrc, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows,
-                                        a.ring_x, xscales, srow, r.mx ? a.ring_xs : nullptr, st));
+                                        xdst, xscales, srow, r.mx ? a.ring_xs : nullptr, st));
     MOK_RUN("gateup_gemm", mok_launch_gateup(a, m0, m1, max_tiles, r.mx, st));
     MOK_RUN("down_gemm", mok_launch_down(a, m0, m1, max_tiles, r.mx, st));
   }
@@ -401,13 +418,14 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   a.wg = static_cast<const bf16_t*>(weights->w_gate);
   a.wu = static_cast<const bf16_t*>(weights->w_up);
   a.wd = static_cast<const bf16_t*>(weights->w_down);
-  const bf16_t* obuf = reinterpret_cast<const bf16_t*>(ctx);
-  a.ab = reinterpret_cast<const bf16_t*>(ctx + align_up((size_t)r.R * 2 * r.H));
+  const CtxLayout C = ctx_layout(r);
+  const bf16_t* obuf = reinterpret_cast<const bf16_t*>(ctx + C.obuf);
+  a.ab = reinterpret_cast<const bf16_t*>(ctx + C.ab);
+  a.xg = reinterpret_cast<const bf16_t*>(ctx + C.xg);
   a.dO = reinterpret_cast<bf16_t*>(ws + W.dO);
   a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
   a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
-  a.xg = reinterpret_cast<bf16_t*>(ws + W.xg);
   a.dwg = static_cast<bf16_t*>(dw_gate);
   a.dwu = static_cast<bf16_t*>(dw_up);
   a.dwd = static_cast<bf16_t*>(dw_down);
@@ -416,8 +434,6 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                        sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
                                        const_cast<bf16_t*>(a.dO), st));
-    MOK_RUN("bwd_gather", mok_launch_gather(x, sp.perm, sp.offsets + r.E, r.k, 2 * r.H, 0, r.R,
-                                            const_cast<bf16_t*>(a.xg), nullptr, 0, nullptr, st));
     MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
   }
   MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));

@@ -76,6 +76,9 @@ struct mok_fwd_args {
   const uint8_t* su;
   const uint8_t* sd;
   // ring: slot s holds X rows at ring_x + s*M*xrow_bytes, h rows at ring_h + ...
+  // With x_resident, ring_x instead holds every gathered X row at its
+  // permuted position p (kept for the backward in fwd_ctx).
+  int x_resident;
   uint8_t* ring_x;
   uint8_t* ring_xs;      // MXFP8 scales of ring_x rows
   uint8_t* ring_h;
@@ -106,7 +109,7 @@ struct mok_bwd_args {
   const bf16_t* wd;
   const bf16_t* dO;      // [R][H] permuted
   const bf16_t* ab;      // [R][2I] permuted (saved by forward)
-  const bf16_t* xg;      // [R][H] gathered x, permuted
+  const bf16_t* xg;      // [R][H] gathered x, permuted (saved by the forward)
   bf16_t* dab;           // [R][2I] permuted: dA | dB
   bf16_t* hb;            // [R][I] permuted: recomputed h
   bf16_t* dxrows;        // [R][H] flat row order
