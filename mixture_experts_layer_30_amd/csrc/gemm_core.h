@@ -390,6 +390,18 @@ struct Pipe {
     if (u < LA::kDma) la.dma1(j, sm.a[b], u);
     else lb.dma1(j, sm.b[b], u - LA::kDma);
   }
+  // fp8: copy u of one side of pair j (u < 8: a K-contiguous window; u == 8:
+  // the side's scale words)
+  MOK_DEV void dma_a1(int j, int u) const {
+    const int s = j & 1;
+    if (u < LA::kDma) la.dma1(j, sm.a[s], u);
+    else if constexpr (SA::kDma > 0) sa.dma(j, reinterpret_cast<uint8_t*>(sm.sa[s]));
+  }
+  MOK_DEV void dma_b1(int j, int u) const {
+    const int s = j & 1;
+    if (u < LB::kDma) lb.dma1(j, sm.b[s], u);
+    else if constexpr (SB::kDma > 0) sb.dma(j, reinterpret_cast<uint8_t*>(sm.sb[s]));
+  }
   MOK_DEV void publish() const {                 // all copies landed, all LDS reads done
     wait_vm_lds<0>();
     barrier_lds();
@@ -471,35 +483,44 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       stage(kt, odd, odd && (kt >> 1) + 2 < np, !odd && kt >= 2 && (kt >> 1) + 1 < np);
     }
   } else {
+    static_assert(LA::kDma == 8 && LB::kDma == 8, "8 + 8 window copies per pair");
     const int sh_lane = 8 * (lane_id() >> 5);
     FragsF8<G> f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) read_f8_a<G>(sm.a[0], sm.sa[0], 0, i, f);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) read_f8_b<G>(sm.b[0], sm.sb[0], 0, jj, f);
-    auto stage = [&](int kt, bool ODD, bool COPY) {
+    // the copies of one side of pair cp go one after each of a region's 8
+    // MFMAs, the side's scale words with the last (cp < 0: none)
+    auto copy_after = [&](int t, int cp, bool bside) {
+      if (cp < 0) return;
+      if (bside) {
+        p.dma_b1(cp, t);
+        if (t == 7) p.dma_b1(cp, 8);
+      } else {
+        p.dma_a1(cp, t);
+        if (t == 7) p.dma_a1(cp, 8);
+      }
+    };
+    // stage kt: one 64-wide scaled K step in two regions. An odd stage ends
+    // its pair j: barrier, then (COPY) the A side of pair j+2 is copied
+    // during its region B; the following even stage copies the B side of
+    // that pair during its region A (PEND).
+    auto stage = [&](int kt, bool ODD, bool COPY, bool PEND) {
       const int j = kt >> 1, slot = j & 1, h = ODD ? 1 : 0;
       const int sh = 16 * h + sh_lane;
+      const int pend = PEND ? j + 1 : -1, cpy = COPY ? j + 2 : -1;
       // region A: rows 0-1; read rows 2-3 of this stage (rows 0-1 and all B
       // fragments were read during the previous stage)
       __builtin_amdgcn_sched_barrier(0);
-      read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 2, f);
-      read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 3, f);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) mfma_f8<G>(f, i, jj, sh, acc);
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      for (int t = 0; t < 8; ++t) {
+        mfma_f8<G>(f, t >> 2, t & 3, sh, acc);
+        if (t < 2) read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 2 + t, f);
+        copy_after(t, pend, true);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ODD) {
-        p.publish();
-        if (COPY) p.dma(j + 2);
-      }
+      if (ODD) p.publish();
       // region B: rows 2-3, column block by column block; each B fragment of
       // the next stage is read once its last MFMA here has issued, rows 0-1
       // of the next stage go into the registers region A freed
@@ -510,23 +531,22 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         mfma_f8<G>(g, 2, jj, sh, acc);
+        copy_after(2 * jj, cpy, false);
         mfma_f8<G>(g, 3, jj, sh, acc);
+        copy_after(2 * jj + 1, cpy, false);
         read_f8_b<G>(sm.b[nslot], sm.sb[nslot], nh, jj, f);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 5 < nk; kt += 2) {
-      stage(kt, false, false);
-      stage(kt + 1, true, true);
+    for (; kt + 5 < nk; kt += 2) {               // pair kt/2 + 2 exists
+      stage(kt, false, false, kt >= 2);
+      stage(kt + 1, true, true, false);
     }
-    for (; kt < nk; ++kt) stage(kt, (kt & 1) != 0, (kt & 1) != 0 && kt + 3 < nk);
+    for (; kt < nk; ++kt) {
+      const bool odd = (kt & 1) != 0;
+      stage(kt, odd, odd && (kt >> 1) + 2 < np, !odd && kt >= 2 && (kt >> 1) + 1 < np);
+    }
   }
 }
 
