@@ -371,11 +371,12 @@ def _mx_experts(experts):
     return _Q()
 
 
-def _mx_ffn(X, Wg, Wu, Wd):
+def _mx_ffn(X, Wg, Wu, Wd, with_ab=False):
     a = mxfp8_roundtrip(X) @ Wg.T
     b = mxfp8_roundtrip(X) @ Wu.T
     h = mxfp8_roundtrip(swiglu(a, b))
-    return h @ Wd.T
+    out = h @ Wd.T
+    return (out, a, b) if with_ab else out
 
 
 def forward_mxfp8(x, topk_ids, topk_w, experts):
@@ -414,3 +415,95 @@ def forward_mxfp8_tokens(x_rows, ids_rows, w_rows, experts):
         outs[sel[:, 0], sel[:, 1]] = _mx_ffn(x_rows[sel[:, 0]], *qexp[e])
     return np.einsum("tj,tjh->th", w_rows, outs), outs
 
+
+
+# ============================================================================ MXFP8 backward
+# [MoK card] "What it is": the layer supports BF16 and MXFP8, forward and
+# backward; "Limits": MXFP8 needs the weights pre-quantized by the op. The
+# pages do not say which backward operands are quantized along which axis;
+# the reading here (every operand of every backward GEMM is MXFP8, blocked
+# along that GEMM's contraction axis, because the scaled MFMA takes 8-bit A
+# and B with scales along K):
+#   dh        = Q_H(dO)       . Q_H(Wd)          K = H
+#   dXrows    = Q_I([dA|dB])  . Q_I([Wg; Wu])    K = 2I
+#   dWd[e]    = Q_t(dO)^T     . Q_t(h)           K = the expert's rows
+#   dWg|u[e]  = Q_t(dA|dB)^T  . Q_t(X)           K = the expert's rows
+# Q_H / Q_I quantize along H / I; Q_t quantizes along the expert's rows in
+# blocks of 32 counted from its first permuted row (the last block is padded
+# with zeros, which changes no block maximum). a, b come from the MXFP8
+# forward; h = silu(a)*b, dA, dB and dO are the exact values the definition
+# gives, then quantized where they enter a GEMM. d topk_w and dx are as in the
+# bf16 backward.
+
+
+def _mx_along_rows(V):
+    """Quantize-dequantize V [n][K] along K (each row, blocks of 32)."""
+    return mxfp8_roundtrip(V)
+
+
+def _mx_along_cols(V):
+    """Quantize-dequantize V [K][n] along K (each column, blocks of 32)."""
+    return mxfp8_roundtrip(np.asarray(V, np.float64).T).T
+
+
+def _mx_along_tokens(V):
+    """Quantize-dequantize V [c][n] along its c rows in blocks of 32 starting
+    at row 0; rows past c (up to a multiple of 32) are zero padding."""
+    V = np.asarray(V, np.float64)
+    c = V.shape[0]
+    cp = -(-c // 32) * 32
+    Vp = np.zeros((cp,) + V.shape[1:])
+    Vp[:c] = V
+    return _mx_along_cols(Vp)[:c]
+
+
+def backward_mxfp8(x, topk_ids, topk_w, experts, dy):
+    """MXFP8 backward (readings above). Returns the same dict as backward()."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    k = ids.shape[1]
+    E = len(experts)
+    w = np.asarray(topk_w, np.float64).reshape(T, k)
+    s = schedule(ids, E)
+    R = T * k
+    I = np.asarray(experts[0][0]).shape[0]
+    qexp = _mx_experts(experts)
+    obuf = np.zeros((R, H))
+    ab = {}
+    for e in range(E):
+        lo, hi = s["offsets"][e], s["offsets"][e + 1]
+        if hi == lo:
+            continue
+        P = s["perm"][lo:hi]
+        obuf[P], a, b = _mx_ffn(x[P // k], *qexp[e], with_ab=True)
+        ab[e] = (a, b)
+    y = np.einsum("tj,tjh->th", w, obuf.reshape(T, k, H))
+    dw = np.einsum("th,tjh->tj", dy, obuf.reshape(T, k, H))
+    wf = w.reshape(-1)
+    dxrows = np.zeros((R, H))
+    dWg = np.zeros((E, I, H))
+    dWu = np.zeros((E, I, H))
+    dWd = np.zeros((E, H, I))
+    for e in range(E):
+        lo, hi = s["offsets"][e], s["offsets"][e + 1]
+        if hi == lo:
+            continue
+        P = s["perm"][lo:hi]
+        Wg, Wu, Wd = experts[e]
+        a, b = ab[e]
+        X = x[P // k]
+        h = swiglu(a, b)
+        dO = wf[P][:, None] * dy[P // k]
+        dh = _mx_along_rows(dO) @ _mx_along_cols(Wd)
+        dA, dB = _swiglu_backward(dh, a, b)
+        dAB = _mx_along_rows(np.concatenate([dA, dB], axis=1))
+        Wgu = _mx_along_cols(np.concatenate([Wg, Wu], axis=0))
+        dxrows[P] = dAB @ Wgu
+        dWd[e] = _mx_along_tokens(dO).T @ _mx_along_tokens(h)
+        Xt = _mx_along_tokens(X)
+        dWg[e] = _mx_along_tokens(dA).T @ Xt
+        dWu[e] = _mx_along_tokens(dB).T @ Xt
+    dx = dxrows.reshape(T, k, H).sum(axis=1)
+    return {"dx": dx, "dWg": dWg, "dWu": dWu, "dWd": dWd, "dw": dw, "y": y}
