@@ -105,6 +105,16 @@ typedef struct {
   const uint8_t* s_gate;         /* MXFP8 only, else NULL */
   const uint8_t* s_up;
   const uint8_t* s_down;
+  /* MXFP8 backward only (else NULL): the weights quantized along the other
+   * axis, for the GEMMs that contract over I or H of their output side:
+   * w_down_t = Wd^T [E][I][H] E4M3 with s_down_t [E][I][H/32] (blocks along H);
+   * w_gu_t = [Wg; Wu]^T [E][H][2I] E4M3 with s_gu_t [E][H][2I/32] (blocks
+   * along 2I; I is a multiple of 32, so no block spans Wg and Wu). Both come
+   * from mok_mxfp8_quantize of the transposed bf16 weights. */
+  const void* w_down_t;
+  const void* w_gu_t;
+  const uint8_t* s_down_t;
+  const uint8_t* s_gu_t;
 } mok_weights;
 
 /* Byte offsets of the arrays inside the schedule buffer (each 256-aligned). */
@@ -167,11 +177,11 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
  * its epilogue, down grouped GEMM writing each expert output to its flat row
  * i; then y[t] = sum_{j=0..k-1} topk_w[t][j] * out[t*k + j], accumulated in
  * fp32 in ascending j and rounded once to bf16.
- * fwd_ctx: NULL for inference; else receives what mok_backward needs
- * (bf16 only): the expert outputs, the gate/up pre-activations and the
- * gathered x rows in permuted order (so with a context, X rows are gathered
- * straight to their permuted positions there and the ring reuses only the
- * h slots). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
+ * fwd_ctx: NULL for inference; else receives what mok_backward needs: the
+ * expert outputs and the gate/up pre-activations (bf16), and for bf16 the
+ * gathered x rows in permuted order (so with a context, bf16 X rows are
+ * gathered straight to their permuted positions there and the ring reuses
+ * only the h slots). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
  * mok_mxfp8_quantize): x rows are quantized along H and h along I the same
  * way on the fly; accumulation is fp32, y is bf16. */
 mok_status mok_forward(const mok_problem* problem, const mok_config* config,
@@ -179,9 +189,15 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config,
                        const mok_weights* weights, void* y, void* fwd_ctx,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward (bf16). [MoK clip] How-to item 2: reverse-combine then
- * reverse-dispatch with the same schedule. x must be the forward's input;
- * the weight gradients read its gathered rows from fwd_ctx. Outputs:
+/* Backward. [MoK clip] How-to item 2: reverse-combine then reverse-dispatch
+ * with the same schedule; [MoK card] "What it is": forward and backward in
+ * BF16 and MXFP8. x must be the forward's input (bf16: the weight gradients
+ * read its gathered rows from fwd_ctx). MXFP8 (fwd_ctx from an MXFP8
+ * forward, weights with the transposed copies of mok_weights): every
+ * backward GEMM takes MXFP8 operands blocked by 32 along its contraction
+ * axis -- dO along H, dA|dB along 2I, and for the weight gradients dO, h,
+ * dA|dB and x along each expert's rows in blocks counted from its first
+ * permuted row; accumulation fp32, outputs bf16 / fp32 as below. Outputs:
  *   d_topk_w[t][j] = <dy[t], out[t*k+j]>           (fp32)
  *   dx [T][H], dw_gate/dw_up [E][I][H], dw_down [E][H][I]   (bf16)
  * Every reduction runs in a fixed order with no atomics; an expert with no

@@ -46,7 +46,9 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
-                ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("w_down_t", ctypes.c_void_p), ("w_gu_t", ctypes.c_void_p),
+                ("s_down_t", ctypes.c_void_p), ("s_gu_t", ctypes.c_void_p)]
 
 
 class ScheduleLayout(ctypes.Structure):
@@ -163,16 +165,17 @@ def build_schedule(problem, topk_ids, schedule, config=None, stream=None):
                                     _stream(stream)), "mok_build_schedule")
 
 
-def _weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None):
-    return Weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
-                   None if s_gate is None else s_gate.data_ptr(),
-                   None if s_up is None else s_up.data_ptr(),
-                   None if s_down is None else s_down.data_ptr())
+def _weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, w_down_t=None, w_gu_t=None,
+             s_down_t=None, s_gu_t=None):
+    p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    return Weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), p(s_gate), p(s_up), p(s_down),
+                   p(w_down_t), p(w_gu_t), p(s_down_t), p(s_gu_t))
 
 
 def forward(problem, schedule, x, topk_w, weights, y, workspace, fwd_ctx=None, config=None,
             stream=None):
-    """weights: (w_gate, w_up, w_down[, s_gate, s_up, s_down]) tensors."""
+    """weights: (w_gate, w_up, w_down[, s_gate, s_up, s_down[, w_down_t, w_gu_t, s_down_t,
+    s_gu_t]]) tensors (the last four only matter to the MXFP8 backward)."""
     w = _weights(*weights)
     _check(lib().mok_forward(ctypes.byref(problem), _cfg(config), _ptr(schedule), _ptr(x),
                              _ptr(topk_w), ctypes.byref(w), _ptr(y), _ptr(fwd_ctx),

@@ -105,6 +105,7 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
     using HS = HalfF32<G>;
     uint8_t* hq = a.ring_h + ft.slot_row0 * I + n0;
     uint8_t* hsc = a.ring_hs + ft.slot_row0 * (I / 32) + n0 / 32;
+    bf16_t* abp = a.ab ? a.ab + (int64_t)ft.t.p0 * 2 * I + n0 : nullptr;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (half) __syncthreads();
@@ -125,6 +126,11 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
           for (int v = 0; v < 8; ++v) {
             h[u + v] = av[v] * sigmoidf_(av[v]) * bv[v];
             amax = fmaxf(amax, fabsf(h[u + v]));
+          }
+          if (abp) {                             // saved for the backward
+            const int64_t rr = 128 * half + r;
+            *reinterpret_cast<uint4*>(abp + rr * 2 * I + blk * 32 + u) = pack_bf16x8(av);
+            *reinterpret_cast<uint4*>(abp + rr * 2 * I + I + blk * 32 + u) = pack_bf16x8(bv);
           }
         }
         const int sc = mx_scale_byte(amax);
@@ -338,6 +344,170 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, i
           a.xg + (int64_t)o * H + n0, H, (int)min<int64_t>(G::BN, H - n0), c, out, H);
 }
 
+// ================================================================== MXFP8 backward
+// The backward GEMMs with MXFP8 operands on the scaled MFMA ([MoK card]
+// "What it is": forward and backward in BF16 and MXFP8). Every operand is
+// K-contiguous: the weights come transposed and quantized along the
+// contraction axis, the activations are quantized along it (rows) or
+// token-blocked (weight gradients, K = an expert's rows).
+
+// dh = dO . Wd[e] (K = H) from dO rows and Wd^T rows, then the SwiGLU
+// backward; writes dA|dB (bf16, for the token-blocked copies), dA|dB rows
+// quantized along 2I (for dX) and h (bf16).
+__global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, int ncol) {
+  using G = G256;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
+  Smem<G, true>& sm = *reinterpret_cast<Smem<G, true>*>(lds_raw);
+  mok_tile t;
+  int ny;
+  if (!bwd_tile(a, ncol, t, ny)) return;
+  const int nrows = t.p1 - t.p0;
+  const int64_t H = a.H, I = a.I, sH = H / 32, s2I = 2 * I / 32;
+  const int n0 = ny * G::BN;
+  const int64_t wrow = (int64_t)t.e * I + n0;           // first Wd^T row of the tile
+  const LoadKD<G::BM, RowsStrided> la{{a.dOq + (int64_t)t.p0 * H, H, nrows}};
+  const LoadKD<G::BN, RowsStrided> lb{{a.wdt + wrow * H, H, (int)(I - n0)}};
+  const LoadScalesD<G::BM, RowsStrided> lsa{{a.dOs + (int64_t)t.p0 * sH, sH, nrows}};
+  const LoadScalesD<G::BN, RowsStrided> lsb{{a.wdt_s + wrow * sH, sH, (int)(I - n0)}};
+  Acc<G::FM, G::FN> acc;
+  mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);
+  // per row and 32-column block: dA, dB, h from dh and the saved a, b;
+  // the 32 dA (and dB) values of the block share one scale along I
+  using HS = HalfF32<G>;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half) __syncthreads();
+    HS::put(lds_raw, acc, half);
+    __syncthreads();
+    const int rows = min(128, nrows - 128 * half);
+    for (int idx = threadIdx.x; idx < 128 * (G::BN / 32); idx += kThreads) {
+      const int r = idx / (G::BN / 32), blk = idx % (G::BN / 32);
+      const int c0 = blk * 32;
+      if (r >= rows || n0 + c0 >= I) continue;
+      const int64_t p = t.p0 + 128 * half + r;
+      float da[32], db[32];
+      float amaxa = 0.f, amaxb = 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; u += 8) {
+        float dh[8], av[8], bv[8], h[8];
+        HS::get8(lds_raw, r, c0 + u, dh);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + n0 + c0 + u), av);
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + I + n0 + c0 + u), bv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float sg = sigmoidf_(av[v]);
+          da[u + v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
+          db[u + v] = dh[v] * av[v] * sg;
+          h[v] = av[v] * sg * bv[v];
+          amaxa = fmaxf(amaxa, fabsf(da[u + v]));
+          amaxb = fmaxf(amaxb, fabsf(db[u + v]));
+        }
+        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c0 + u) = pack_bf16x8(da + u);
+        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c0 + u) = pack_bf16x8(db + u);
+        *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
+      }
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const float* v = side ? db : da;
+        const int sc = mx_scale_byte(side ? amaxb : amaxa);
+        const float inv = mx_inv_scale(sc);
+        uint32_t w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          w[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
+                 (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
+        const int64_t col = (side ? I : 0) + n0 + c0;
+        uint4* d = reinterpret_cast<uint4*>(a.dabq + p * 2 * I + col);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        a.dabs[p * s2I + col / 32] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+// dX rows = [dA | dB] . [Wg[e]; Wu[e]] (K = 2I) from quantized dA|dB rows and
+// [Wg; Wu]^T rows; row p goes to flat row perm[p].
+__global__ __launch_bounds__(kThreads, 1) void bwd_dx8_kernel(mok_bwd_args a, int ncol) {
+  using G = G256;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
+  Smem<G, true>& sm = *reinterpret_cast<Smem<G, true>*>(lds_raw);
+  mok_tile t;
+  int ny;
+  if (!bwd_tile(a, ncol, t, ny)) return;
+  const int nrows = t.p1 - t.p0;
+  const int64_t H = a.H, I = a.I, K = 2 * I, sK = K / 32;
+  const int n0 = ny * G::BN;
+  const int64_t wrow = (int64_t)t.e * H + n0;
+  const LoadKD<G::BM, RowsStrided> la{{a.dabq + (int64_t)t.p0 * K, K, nrows}};
+  const LoadKD<G::BN, RowsStrided> lb{{a.wgut + wrow * K, K, (int)(H - n0)}};
+  const LoadScalesD<G::BM, RowsStrided> lsa{{a.dabs + (int64_t)t.p0 * sK, sK, nrows}};
+  const LoadScalesD<G::BN, RowsStrided> lsb{{a.wgut_s + wrow * sK, sK, (int)(H - n0)}};
+  Acc<G::FM, G::FN> acc;
+  mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), acc);
+  int* rows = tile_rows<Smem<G, true>>(lds_raw);
+  for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
+  bf16_t* d = a.dxrows + n0;
+  store_tile_bf16<G>(lds_raw, acc, nrows, (int)(H - n0), [&](int r) { return d + (int64_t)rows[r] * H; });
+}
+
+// Weight gradient out[m][n] = sum over the expert's rows of A[m][k] B[n][k],
+// both operands token-blocked MXFP8 rows of the expert (K = tok_pad(rows)).
+MOK_DEV void dw8_tile(uint8_t* lds_raw, const uint8_t* A, const uint8_t* As, int mlim, const uint8_t* B,
+                      const uint8_t* Bs, int nlim, int kp, bf16_t* out, int64_t ldo) {
+  using G = G256;
+  Smem<G, true>& sm = *reinterpret_cast<Smem<G, true>*>(lds_raw);
+  const LoadKD<G::BM, RowsStrided> la{{A, kp, mlim}};
+  const LoadKD<G::BN, RowsStrided> lb{{B, kp, nlim}};
+  const LoadScalesD<G::BM, RowsStrided> lsa{{As, kp / 32, mlim}};
+  const LoadScalesD<G::BN, RowsStrided> lsb{{Bs, kp / 32, nlim}};
+  Acc<G::FM, G::FN> acc;
+  mainloop<G, true>(sm, la, lb, lsa, lsb, kp / 64, acc);
+  store_tile_bf16<G>(lds_raw, acc, mlim, nlim, [&](int r) { return out + (int64_t)r * ldo; });
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, int tiles_per_e) {
+  using G = G256;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
+  const int L = xcd_tile(a.E * tiles_per_e);
+  if (L < 0) return;
+  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  const int64_t H = a.H, I = a.I;
+  const int ntn = (int)((I + G::BN - 1) / G::BN);
+  const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
+  // wave-uniform: kept in scalar registers
+  const int kp = __builtin_amdgcn_readfirstlane(tok_pad(a.offsets[e + 1] - a.offsets[e]));
+  const int64_t koff = __builtin_amdgcn_readfirstlane(tok_koff(a.offsets, e));
+  dw8_tile(lds_raw, a.dOT + H * koff + (int64_t)m0 * kp, a.dOTs + H * (koff / 32) + (int64_t)m0 * (kp / 32),
+           (int)min<int64_t>(G::BM, H - m0), a.hT + I * koff + (int64_t)n0 * kp,
+           a.hTs + I * (koff / 32) + (int64_t)n0 * (kp / 32), (int)min<int64_t>(G::BN, I - n0), kp,
+           a.dwd + (int64_t)e * H * I + (int64_t)m0 * I + n0, I);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu8_kernel(mok_bwd_args a, int tiles_per_e) {
+  using G = G256;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
+  const int L = xcd_tile(a.E * tiles_per_e);
+  if (L < 0) return;
+  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  const int64_t H = a.H, I = a.I;
+  const int ntn = (int)((H + G::BN - 1) / G::BN);
+  const int mt = tl / ntn;
+  const int n0 = (tl % ntn) * G::BN;
+  // stacked [dWg; dWu] rows; tiles split at I (I is a multiple of 128)
+  const int tiles_g = (int)((I + G::BM - 1) / G::BM);
+  const bool up = mt >= tiles_g;
+  const int m0 = (up ? mt - tiles_g : mt) * G::BM;
+  const int64_t arow = (up ? I : 0) + m0;               // row of the token-blocked dA|dB
+  // wave-uniform: kept in scalar registers
+  const int kp = __builtin_amdgcn_readfirstlane(tok_pad(a.offsets[e + 1] - a.offsets[e]));
+  const int64_t koff = __builtin_amdgcn_readfirstlane(tok_koff(a.offsets, e));
+  bf16_t* out = (up ? a.dwu : a.dwg) + (int64_t)e * I * H + (int64_t)m0 * H + n0;
+  dw8_tile(lds_raw, a.dabT + 2 * I * koff + arow * kp, a.dabTs + 2 * I * (koff / 32) + arow * (kp / 32),
+           (int)min<int64_t>(G::BM, I - m0), a.xT + H * koff + (int64_t)n0 * kp,
+           a.xTs + H * (koff / 32) + (int64_t)n0 * (kp / 32), (int)min<int64_t>(G::BN, H - n0), kp, out, H);
+}
+
 unsigned cdivu(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
@@ -366,6 +536,30 @@ hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles,
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN);
   hipLaunchKernelGGL(bwd_dh_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_bwd_dh8(const mok_bwd_args& a, hipStream_t st) {
+  const int ncol = (int)cdivu(a.I, G256::BN);
+  hipLaunchKernelGGL(bwd_dh8_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_bwd_dx8(const mok_bwd_args& a, hipStream_t st) {
+  const int ncol = (int)cdivu(a.H, G256::BN);
+  hipLaunchKernelGGL(bwd_dx8_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_bwd_dwd8(const mok_bwd_args& a, hipStream_t st) {
+  const int tpe = (int)(cdivu(a.H, G256::BM) * cdivu(a.I, G256::BN));
+  hipLaunchKernelGGL(bwd_dwd8_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st) {
+  const int tpe = (int)(2 * cdivu(a.I, G256::BM) * cdivu(a.H, G256::BN));
+  hipLaunchKernelGGL(bwd_dwgu8_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
   return hipGetLastError();
 }
 

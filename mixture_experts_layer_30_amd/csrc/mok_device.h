@@ -21,6 +21,16 @@ struct mok_tile {          // one row tile of one expert: permuted rows [p0, p1)
   int32_t e, p0, p1, m;    // m = minibatch index (p0 / M) for forward tiles
 };
 
+// Token-blocked MXFP8 layout of the backward: an expert with c routed rows
+// takes tok_pad(c) positions of the padded token axis (c rounded up to 128,
+// so its scale words are whole), starting at tok_koff(offsets, e).
+MOK_DEV int tok_pad(int c) { return (c + 127) & ~127; }
+MOK_DEV int tok_koff(const int32_t* offsets, int e) {
+  int k = 0;
+  for (int i = 0; i < e; ++i) k += tok_pad(offsets[i + 1] - offsets[i]);
+  return k;
+}
+
 // ------------------------------------------------------------------ bf16 helpers
 MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 

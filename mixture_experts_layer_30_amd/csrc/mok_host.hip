@@ -123,7 +123,10 @@ struct FwdWs {
   size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
 };
 struct BwdWs {
-  size_t dO, dab, hb, dxrows, total;
+  size_t dO, dab, hb, dxrows;
+  // MXFP8 only
+  size_t dOq, dOs, dabq, dabs, dOT, dOTs, hT, hTs, dabT, dabTs, xT, xTs;
+  size_t total;
 };
 
 FwdWs fwd_ws(const Resolved& r) {
@@ -148,14 +151,34 @@ BwdWs bwd_ws(const Resolved& r) {
   w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
-  w.total = r.mx ? 0 : o;
+  w.dOq = w.dOs = w.dabq = w.dabs = w.dOT = w.dOTs = w.hT = w.hTs = w.dabT = w.dabTs = w.xT = w.xTs = 0;
+  if (r.mx) {
+    // token-blocked operands: KT bounds the padded token axis (each expert's
+    // rows rounded up to 128)
+    const size_t R = (size_t)r.R, H = (size_t)r.H, I = (size_t)r.I;
+    const size_t KT = R + 128 * (size_t)r.E;
+    w.dOq = o;   o = align_up(o + R * H);
+    w.dOs = o;   o = align_up(o + R * (H / 32));
+    w.dabq = o;  o = align_up(o + R * 2 * I);
+    w.dabs = o;  o = align_up(o + R * (2 * I / 32));
+    w.dOT = o;   o = align_up(o + H * KT);
+    w.dOTs = o;  o = align_up(o + H * (KT / 32));
+    w.hT = o;    o = align_up(o + I * KT);
+    w.hTs = o;   o = align_up(o + I * (KT / 32));
+    w.dabT = o;  o = align_up(o + 2 * I * KT);
+    w.dabTs = o; o = align_up(o + 2 * I * (KT / 32));
+    w.xT = o;    o = align_up(o + H * KT);
+    w.xTs = o;   o = align_up(o + H * (KT / 32));
+  }
+  w.total = o;
   return w;
 }
 
 size_t ws_bytes(const Resolved& r) { return std::max(fwd_ws(r).total, bwd_ws(r).total); }
 
 // fwd_ctx: the down outputs in flat row order [R][H], the gate/up
-// pre-activations a | b [R][2I] and the gathered x in permuted order [R][H].
+// pre-activations a | b [R][2I] and (bf16 only) the gathered x in permuted
+// order [R][H]; the MXFP8 backward token-blocks x from x itself.
 struct CtxLayout {
   size_t obuf, ab, xg, total;
 };
@@ -164,11 +187,11 @@ CtxLayout ctx_layout(const Resolved& r) {
   c.obuf = 0;
   c.ab = align_up((size_t)r.R * 2 * r.H);
   c.xg = c.ab + align_up((size_t)r.R * 4 * r.I);
-  c.total = c.xg + align_up((size_t)r.R * 2 * r.H);
+  c.total = c.xg + (r.mx ? 0 : align_up((size_t)r.R * 2 * r.H));
   return c;
 }
 
-size_t ctx_bytes(const Resolved& r) { return r.mx ? 0 : ctx_layout(r).total; }
+size_t ctx_bytes(const Resolved& r) { return ctx_layout(r).total; }
 
 // gfx950 check and compute-unit count, once per device (device properties
 // only; no device memory is touched).
@@ -323,7 +346,6 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
-  if (r.mx && fwd_ctx) return MOK_ERR_UNSUPPORTED;
   // The persistent minibatch kernel (driver 2) is not provided: its first
   // version did not complete on the device and the cause was not established.
   if (r.driver == 2) return MOK_ERR_UNSUPPORTED;
@@ -353,8 +375,8 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   // With a context the gathered rows go straight to their permuted
   // positions in it (the backward's weight gradients read them there), so
   // X ring slots are not reused; h still cycles through the ring.
-  a.x_resident = ctx ? 1 : 0;
-  if (ctx) a.ring_x = ctx + C.xg;
+  a.x_resident = ctx && !r.mx ? 1 : 0;
+  if (a.x_resident) a.ring_x = ctx + C.xg;
 
   // MXFP8: x is quantized once per token (blocks lie inside a row, so this is
   // bitwise the same as quantizing each gathered row), then fp8 rows and their
@@ -398,8 +420,9 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
-  if (r.mx) return MOK_ERR_UNSUPPORTED;
   if (!schedule || !fwd_ctx || !weights || !dw_gate || !dw_up || !dw_down) return MOK_ERR_INVALID_ARG;
+  if (r.mx && (!weights->w_down_t || !weights->w_gu_t || !weights->s_down_t || !weights->s_gu_t))
+    return MOK_ERR_INVALID_ARG;
   if (r.T > 0 && (!x || !topk_w || !dy || !dx || !d_topk_w)) return MOK_ERR_INVALID_ARG;
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   const BwdWs W = bwd_ws(r);
@@ -421,7 +444,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   const CtxLayout C = ctx_layout(r);
   const bf16_t* obuf = reinterpret_cast<const bf16_t*>(ctx + C.obuf);
   a.ab = reinterpret_cast<const bf16_t*>(ctx + C.ab);
-  a.xg = reinterpret_cast<const bf16_t*>(ctx + C.xg);
+  a.xg = r.mx ? nullptr : reinterpret_cast<const bf16_t*>(ctx + C.xg);
   a.dO = reinterpret_cast<bf16_t*>(ws + W.dO);
   a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
@@ -430,6 +453,43 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   a.dwu = static_cast<bf16_t*>(dw_up);
   a.dwd = static_cast<bf16_t*>(dw_down);
 
+  if (r.mx) {
+    a.wdt = static_cast<const uint8_t*>(weights->w_down_t);
+    a.wdt_s = weights->s_down_t;
+    a.wgut = static_cast<const uint8_t*>(weights->w_gu_t);
+    a.wgut_s = weights->s_gu_t;
+    a.dOq = ws + W.dOq;   a.dOs = ws + W.dOs;
+    a.dabq = ws + W.dabq; a.dabs = ws + W.dabs;
+    a.dOT = ws + W.dOT;   a.dOTs = ws + W.dOTs;
+    a.hT = ws + W.hT;     a.hTs = ws + W.hTs;
+    a.dabT = ws + W.dabT; a.dabTs = ws + W.dabTs;
+    a.xT = ws + W.xT;     a.xTs = ws + W.xTs;
+    if (r.T > 0) {
+      MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
+                                         sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
+                                         const_cast<bf16_t*>(a.dO), st));
+      // dO rows along H for dh (rows of invalid ids are quantized too, and
+      // never read)
+      MOK_RUN("mx_quantize_dO", mok_launch_mxfp8_quantize(a.dO, r.R, r.H, a.dOq, a.dOs, st));
+      MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh8(a, st));
+      MOK_RUN("token_quantize", mok_launch_token_quantize(a.dO, r.H, nullptr, r.k, sp.offsets, r.E, r.R, r.H,
+                                                          a.dOT, a.dOTs, st));
+      MOK_RUN("token_quantize", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, sp.offsets, r.E, r.R, r.I,
+                                                          a.hT, a.hTs, st));
+      MOK_RUN("token_quantize", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, sp.offsets, r.E, r.R,
+                                                          2 * r.I, a.dabT, a.dabTs, st));
+      MOK_RUN("token_quantize", mok_launch_token_quantize(static_cast<const bf16_t*>(x), r.H, sp.perm, r.k,
+                                                          sp.offsets, r.E, r.R, r.H, a.xT, a.xTs, st));
+    }
+    MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd8(a, st));
+    MOK_RUN("bwd_dwgu_gemm", mok_launch_bwd_dwgu8(a, st));
+    if (r.T > 0) {
+      MOK_RUN("bwd_dx_gemm", mok_launch_bwd_dx8(a, st));
+      MOK_RUN("reverse_dispatch", mok_launch_reverse_dispatch(a.dxrows, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
+                                          static_cast<bf16_t*>(dx), st));
+    }
+    return MOK_OK;
+  }
   if (r.T > 0) {
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                        sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,

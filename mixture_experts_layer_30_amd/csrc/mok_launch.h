@@ -116,9 +116,39 @@ struct mok_bwd_args {
   bf16_t* dwg;
   bf16_t* dwu;
   bf16_t* dwd;
+  // MXFP8 backward (NULL for bf16). Token-blocked operands of expert e are
+  // [N][Kp_e] E4M3 matrices at byte N*koff_e (Kp_e = rows rounded up to 128,
+  // koff_e = sum of Kp over experts before e), scales [N][Kp_e/32] at N*koff_e/32.
+  const uint8_t* wdt;    // Wd^T [E][I][H], blocks along H
+  const uint8_t* wdt_s;
+  const uint8_t* wgut;   // [Wg; Wu]^T [E][H][2I], blocks along 2I
+  const uint8_t* wgut_s;
+  uint8_t* dOq;          // dO rows [R][H], blocks along H
+  uint8_t* dOs;
+  uint8_t* dabq;         // dA | dB rows [R][2I], blocks along 2I
+  uint8_t* dabs;
+  uint8_t* dOT;          // token-blocked dO (N = H)
+  uint8_t* dOTs;
+  uint8_t* hT;           // token-blocked h (N = I)
+  uint8_t* hTs;
+  uint8_t* dabT;         // token-blocked dA | dB (N = 2I)
+  uint8_t* dabTs;
+  uint8_t* xT;           // token-blocked x rows (N = H)
+  uint8_t* xTs;
 };
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st);     // dh, SwiGLU bwd
 hipError_t mok_launch_bwd_dwd(const mok_bwd_args& a, hipStream_t st);    // dWd
 hipError_t mok_launch_bwd_dwgu(const mok_bwd_args& a, hipStream_t st);   // dWg, dWu
 hipError_t mok_launch_bwd_dx(const mok_bwd_args& a, hipStream_t st);     // dX rows
+// MXFP8 backward GEMMs (same roles; operands in the MXFP8 fields of mok_bwd_args)
+hipError_t mok_launch_bwd_dh8(const mok_bwd_args& a, hipStream_t st);
+hipError_t mok_launch_bwd_dx8(const mok_bwd_args& a, hipStream_t st);
+hipError_t mok_launch_bwd_dwd8(const mok_bwd_args& a, hipStream_t st);
+hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st);
+// Token-blocked MXFP8 copy of the rows of every expert (layout as in
+// mok_bwd_args): row p of the source is src + p*ld, or with perm the token
+// row src + (perm[p] / topk)*ld; N columns; R routed rows.
+hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
+                                     const int32_t* offsets, int E, int64_t R, int64_t N,
+                                     uint8_t* dst, uint8_t* dst_scales, hipStream_t st);

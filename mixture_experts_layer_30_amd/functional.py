@@ -52,6 +52,22 @@ def run_backward(w: Workspace, x, topk_w, weights, dy):
     return dx, dwg, dwu, dwd, dtw
 
 
+def quantize_weights_backward(wg, wu, wd):
+    """The transposed MXFP8 weight copies the MXFP8 backward needs: Wd^T
+    [E][I][H] blocked along H, and [Wg; Wu]^T [E][H][2I] blocked along 2I.
+    Returns (w_down_t, w_gu_t, s_down_t, s_gu_t)."""
+    wdt = wd.transpose(1, 2).contiguous()
+    wgut = torch.cat([wg, wu], dim=1).transpose(1, 2).contiguous()
+    out = []
+    for m in (wdt, wgut):
+        q = torch.empty(m.shape, dtype=torch.uint8, device=m.device)
+        s = torch.empty(m.shape[:-1] + (m.shape[-1] // 32,), dtype=torch.uint8, device=m.device)
+        mxfp8_quantize(m.reshape(-1, m.shape[-1]), q, s)
+        out.append((q, s))
+    (qd, sd), (qgu, sgu) = out
+    return qd, qgu, sd, sgu
+
+
 def quantize_weights(wg, wu, wd):
     """MXFP8 copies of the expert weights along their contraction axes."""
     out = []

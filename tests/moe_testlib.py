@@ -12,6 +12,13 @@ REL_FRO_BF16 = 1e-2
 MAX_ABS_FRAC_BF16 = 5e-2
 # MXFP8 forward against the oracle fed the same dequantized operands.
 REL_FRO_MXFP8 = 2e-2
+# MXFP8 backward against the oracle's MXFP8 backward. Besides fp32 vs fp64
+# accumulation, the device quantizes bf16/fp32 intermediates (dO, dA, dB, h)
+# where the oracle quantizes fp64 ones; an element whose value sits within
+# that difference (~2^-9 relative) of an E4M3 rounding boundary lands one
+# code (up to 2^-3 relative) away, and each output sees several quantized
+# operands in sequence (dX rows: dO, Wd^T, then dA|dB, [Wg;Wu]^T).
+REL_FRO_MXFP8_BWD = 4e-2
 
 
 def to_dev_bf16(bits, device="cuda"):

@@ -113,14 +113,16 @@ def test_calls_reject_bad_arguments_before_any_launch():
     w0 = mok.Weights(0x1000, None, 0x1000, None, None, None)
     assert L.mok_forward(ctypes.byref(prob), None, fake, fake, fake, ctypes.byref(w0), fake, None,
                          fake, ws, None) == mok.MOK_ERR_INVALID_ARG
-    # MXFP8 forward needs scales; its backward is not provided
+    # MXFP8 forward needs scales; its backward needs the transposed weight copies
     pm = P(dtype=mok.MOK_MXFP8)
     wsm, _, cbm = mok.buffer_sizes(pm)
-    assert cbm == 0
+    _, _, cb = mok.buffer_sizes(prob)
+    assert 0 < cbm < cb                      # outputs and a, b; no gathered x
     assert L.mok_forward(ctypes.byref(pm), None, fake, fake, fake, ctypes.byref(w), fake, None,
                          fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
-    assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(w), fake,
-                          fake, fake, fake, fake, fake, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED
+    wm = mok.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(wm), fake,
+                          fake, fake, fake, fake, fake, fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
     # the persistent minibatch driver is switched off
     assert L.mok_forward(ctypes.byref(prob), ctypes.byref(mok.make_config(driver=2)), fake, fake,
                          fake, ctypes.byref(w), fake, None, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED

@@ -1,11 +1,13 @@
 """GPU parity of MXFP8: the quantizer must be bit-identical to the oracle's
 (codes and scale bytes); the MXFP8 forward must match the oracle fed the same
-dequantized operands within a relative Frobenius error of 2e-2."""
+dequantized operands within a relative Frobenius error of 2e-2; the MXFP8
+backward must match the oracle's MXFP8 backward within REL_FRO_MXFP8_BWD."""
 import numpy as np
 import pytest
 
 import oracle
-from moe_testlib import REL_FRO_MXFP8, ExpertsF64, f64, from_dev_bf16, rel_fro, to_dev_bf16
+from moe_testlib import (REL_FRO_MXFP8, REL_FRO_MXFP8_BWD, ExpertsF64, f64, from_dev_bf16, rel_fro,
+                         to_dev_bf16)
 from synthetic import CONFIGS, bf16_to_f32, f32_to_bf16_bits, problem
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +127,78 @@ def test_mxfp8_forward_bitwise_deterministic():
     for _ in range(4):
         y, _ = gpu_mx_forward(p, d)
         assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+
+
+# ------------------------------------------------------------------ MXFP8 backward
+def gpu_mx_fwd_bwd(p, d, dy_bits, **cfg):
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=True, **cfg)
+    qw = F.quantize_weights(*d["weights"]) + F.quantize_weights_backward(*d["weights"])
+    F.run_schedule(ws, d["ids"])
+    y = F.run_forward(ws, d["x"], d["w"], qw)
+    wg, wu, wd = d["weights"]
+    dx = torch.empty_like(d["x"])
+    dwg, dwu, dwd = torch.empty_like(wg), torch.empty_like(wu), torch.empty_like(wd)
+    dtw = torch.empty_like(d["w"])
+    mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d["x"], d["w"], qw, to_dev_bf16(dy_bits), dx, dwg,
+                 dwu, dwd, dtw, ws.workspace, ws.config)
+    torch.cuda.synchronize()
+    return y, (dx, dwg, dwu, dwd, dtw)
+
+
+def _check_mx_backward(p, got, ref):
+    dx, dwg, dwu, dwd, dtw = got
+    errs = {"dx": rel_fro(from_dev_bf16(dx), ref["dx"]),
+            "d topk_w": rel_fro(dtw.cpu().numpy().astype(np.float64), ref["dw"])}
+    for name, t in (("dWg", dwg), ("dWu", dwu), ("dWd", dwd)):
+        g = from_dev_bf16(t)
+        assert np.all(np.isfinite(g)), name
+        for e in range(p.E):
+            if not ref[name][e].any():
+                assert not g[e].any(), f"{name}[{e}] of an empty expert must be exactly zero"
+        errs[name] = rel_fro(g, ref[name])
+    print("MXFP8 backward relative Frobenius errors:", {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= REL_FRO_MXFP8_BWD, f"{k}: relative Frobenius error {v:.3e}"
+
+
+@pytest.mark.parametrize("p", SMALL_MX, ids=lambda p: p.name)
+@pytest.mark.parametrize("cfg", [dict(), dict(minibatch_rows=64, ring_slots=2)], ids=["default", "M64-ring2"])
+def test_mxfp8_backward_small(p, cfg):
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs, host_inputs
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    dy = make_dy(p)
+    _, got = gpu_mx_fwd_bwd(p, device_inputs(p), dy, **cfg)
+    ref = oracle.backward_mxfp8(f64(x), ids, w.astype(np.float64), ExpertsF64(wg, wu, wd), f64(dy))
+    _check_mx_backward(p, got, ref)
+
+
+def test_mxfp8_backward_empty_experts_and_ragged_segments():
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs, host_inputs
+    p = problem(90, 256, 256, 8, 2, seed=54)
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    ids = np.where(ids >= 5, ids % 5, ids)      # experts 5..7 get no rows
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 5, ids[:, 1])
+    dy = make_dy(p)
+    _, got = gpu_mx_fwd_bwd(p, device_inputs(p, ids_override=ids), dy)
+    ref = oracle.backward_mxfp8(f64(x), ids, w.astype(np.float64), ExpertsF64(wg, wu, wd), f64(dy))
+    _check_mx_backward(p, got, ref)
+
+
+def test_mxfp8_backward_bitwise_deterministic():
+    import torch
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs
+    p = problem(512, 512, 256, 16, 4, seed=55)
+    d = device_inputs(p)
+    dy = make_dy(p)
+    _, g0 = gpu_mx_fwd_bwd(p, d, dy)
+    for _ in range(2):
+        _, g = gpu_mx_fwd_bwd(p, d, dy)
+        for a, b in zip(g, g0):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
