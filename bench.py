@@ -295,8 +295,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     ms_step, stats = timed(step, args.steps, trace=True)
-    ms_fwd = ms_mx = None
-    mxstats = {}
+    ms_fwd = ms_mx = ms_mxs = ms_wq = None
+    mxstats = mxsstats = {}
     if not args.only_step:
         log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
         ms_fwd, _ = timed(fwd_only, args.steps, trace=True)
@@ -317,6 +317,28 @@ def main():
             fwd_mx()
         ms_mx, mxstats = timed(fwd_mx, args.steps, trace=True)
         del wsm
+
+        # MXFP8 training step: schedule -> MXFP8 forward saving the context ->
+        # MXFP8 backward. The weights (and their transposed copies for the
+        # backward) are quantized before the timed region, as the pages'
+        # pre-quantized weights; that quantization is timed on its own.
+        log("[bench] MXFP8 step timing")
+        wst = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=True, **cfg)
+        qfull = qweights + F.quantize_weights_backward(*weights)
+
+        def step_mx():
+            mok.build_schedule(wst.problem, dids, wst.schedule, wst.config, stream)
+            mok.forward(wst.problem, wst.schedule, dx_, dw_, qfull, ymx, wst.workspace, wst.fwd_ctx,
+                        wst.config, stream)
+            mok.backward(wst.problem, wst.schedule, wst.fwd_ctx, dx_, dw_, qfull, ddy, gx, gwg, gwu, gwd,
+                         gtw, wst.workspace, wst.config, stream)
+
+        for _ in range(2):
+            step_mx()
+        ms_mxs, mxsstats = timed(step_mx, args.steps, trace=True)
+        ms_wq, _ = timed(lambda: (F.quantize_weights(*weights), F.quantize_weights_backward(*weights)), 3,
+                         trace=False)
+        del wst
 
     R, H, I = p.R, p.H, p.I
     flops_step = p.fwd_flops() + p.bwd_flops()
@@ -376,6 +398,16 @@ def main():
             "tokens_per_s": round(p.T / (ms_mx * 1e-3), 1),
             "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
                             for k, v in mxstats.items() if k in GEMM_FLOPS_PER_ROW},
+        }
+    if ms_mxs is not None:
+        out["mxfp8_step"] = {
+            "ms": round(ms_mxs, 4), "tflops": round(flops_step / (ms_mxs * 1e-3) / 1e12, 2),
+            "pct_fp8_peak": round(100 * flops_step / (ms_mxs * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+            "tokens_per_s": round(p.T / (ms_mxs * 1e-3), 1),
+            "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
+                            for k, v in mxsstats.items() if k in GEMM_FLOPS_PER_ROW},
+            "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in mxsstats.items()},
+            "weight_quantize_ms": round(ms_wq, 4),
         }
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")

@@ -476,8 +476,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, i
   const int ntn = (int)((I + G::BN - 1) / G::BN);
   const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
   // wave-uniform: kept in scalar registers
-  const int kp = __builtin_amdgcn_readfirstlane(tok_pad(a.offsets[e + 1] - a.offsets[e]));
-  const int64_t koff = __builtin_amdgcn_readfirstlane(tok_koff(a.offsets, e));
+  const int64_t koff = __builtin_amdgcn_readfirstlane(a.koff[e]);
+  const int kp = __builtin_amdgcn_readfirstlane(a.koff[e + 1]) - (int)koff;
   dw8_tile(lds_raw, a.dOT + H * koff + (int64_t)m0 * kp, a.dOTs + H * (koff / 32) + (int64_t)m0 * (kp / 32),
            (int)min<int64_t>(G::BM, H - m0), a.hT + I * koff + (int64_t)n0 * kp,
            a.hTs + I * (koff / 32) + (int64_t)n0 * (kp / 32), (int)min<int64_t>(G::BN, I - n0), kp,
@@ -500,8 +500,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu8_kernel(mok_bwd_args a, 
   const int m0 = (up ? mt - tiles_g : mt) * G::BM;
   const int64_t arow = (up ? I : 0) + m0;               // row of the token-blocked dA|dB
   // wave-uniform: kept in scalar registers
-  const int kp = __builtin_amdgcn_readfirstlane(tok_pad(a.offsets[e + 1] - a.offsets[e]));
-  const int64_t koff = __builtin_amdgcn_readfirstlane(tok_koff(a.offsets, e));
+  const int64_t koff = __builtin_amdgcn_readfirstlane(a.koff[e]);
+  const int kp = __builtin_amdgcn_readfirstlane(a.koff[e + 1]) - (int)koff;
   bf16_t* out = (up ? a.dwu : a.dwg) + (int64_t)e * I * H + (int64_t)m0 * H + n0;
   dw8_tile(lds_raw, a.dabT + 2 * I * koff + arow * kp, a.dabTs + 2 * I * (koff / 32) + arow * (kp / 32),
            (int)min<int64_t>(G::BM, I - m0), a.xT + H * koff + (int64_t)n0 * kp,

@@ -193,44 +193,49 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
 // expert's rows): expert e's rows [o_e, o_e + c_e) of the source, transposed
 // to [N][Kp_e] and quantized along the rows in blocks of 32 counted from o_e
 // (positions past c_e are zero, which decode to zero under the block's
-// scale). One workgroup per (32 positions of the padded token axis, 256
-// columns): it stages the 32 x 256 block in LDS, then each thread turns one
-// column into 32 codes and a scale.
+// scale). One workgroup per (64 columns x 128 positions of the padded token
+// axis, which never straddle two experts since every Kp is a multiple of
+// 128): it stages the 128 x 64 block in LDS (128-byte row segments in),
+// then 4 adjacent threads per column quantize its four 32-row blocks and
+// write them as one 128-byte segment of the transposed row.
 __global__ __launch_bounds__(256) void token_quantize_kernel(
     const bf16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm, int topk,
-    const int32_t* __restrict__ offsets, int E, int64_t N, uint8_t* __restrict__ dst,
-    uint8_t* __restrict__ dsts) {
-  __shared__ float tile[32][257];
-  __shared__ int s_e, s_koff;
-  const int t0 = (int)blockIdx.x * 32;          // position on the padded token axis
-  if (threadIdx.x == 0) {
-    int k = 0, found = -1, ko = 0;
-    for (int e = 0; e < E; ++e) {
-      const int kp = tok_pad(offsets[e + 1] - offsets[e]);
-      if (t0 < k + kp) {
-        found = e;
-        ko = k;
-        break;
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ koffs, int E, int64_t N,
+    uint8_t* __restrict__ dst, uint8_t* __restrict__ dsts) {
+  __shared__ float tile[128][65];
+  __shared__ int s_koff[kMaxExperts + 1];
+  __shared__ int s_e;
+  // blockIdx.x: 64-column slice (adjacent workgroups read adjacent slices of
+  // the same rows); blockIdx.y: 128 positions of the padded token axis
+  const int t0 = (int)blockIdx.y * 128;         // position on the padded token axis
+  for (int i = threadIdx.x; i <= E; i += 256) s_koff[i] = koffs[i];
+  __syncthreads();
+  if (threadIdx.x == 0) {                        // the expert e with koff[e] <= t0 < koff[e+1]
+    int lo = 0, hi = E;                          // invariant: koff[lo] <= t0, answer < hi
+    if (t0 >= s_koff[E]) {
+      lo = -1;
+    } else {
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_koff[mid] <= t0) lo = mid; else hi = mid;
       }
-      k += kp;
     }
-    s_e = found;
-    s_koff = ko;
+    s_e = lo;
   }
   __syncthreads();
   const int e = s_e;
   if (e < 0) return;                             // past every expert's positions
-  const int koff = s_koff;
-  const int c = offsets[e + 1] - offsets[e], kp = tok_pad(c);
-  const int rb = (t0 - koff) >> 5;               // block of 32 rows within the expert
-  const int nrow = min(32, c - 32 * rb);         // rows of this block that exist (may be <= 0)
-  const int64_t n0 = (int64_t)blockIdx.y * 256;
-  for (int idx = threadIdx.x; idx < 32 * 32; idx += 256) {
-    const int r = idx >> 5, ch = idx & 31;
+  const int koff = s_koff[e];
+  const int c = offsets[e + 1] - offsets[e], kp = s_koff[e + 1] - koff;
+  const int r0 = t0 - koff;                      // first row of the block within the expert
+  const int nrow = min(128, c - r0);             // rows of this block that exist (may be <= 0)
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  for (int idx = threadIdx.x; idx < 128 * 8; idx += 256) {
+    const int r = idx >> 3, ch = idx & 7;
     const int64_t col = n0 + ch * 8;
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (r < nrow && col < N) {
-      const int64_t p = offsets[e] + 32 * rb + r;
+      const int64_t p = offsets[e] + r0 + r;
       const int64_t row = perm ? (int64_t)(perm[p] / topk) : p;
       unpack8(*reinterpret_cast<const uint4*>(src + row * ld + col), v);
     }
@@ -238,25 +243,41 @@ __global__ __launch_bounds__(256) void token_quantize_kernel(
     for (int u = 0; u < 8; ++u) tile[r][ch * 8 + u] = v[u];
   }
   __syncthreads();
-  const int64_t n = n0 + threadIdx.x;
+  const int cl = threadIdx.x >> 2, qb = threadIdx.x & 3;   // column, 32-row block
+  const int64_t n = n0 + cl;
   if (n >= N) return;
   float amax = 0.f;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(tile[r][threadIdx.x]));
+  for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(tile[32 * qb + r][cl]));
   const int sc = mx_scale_byte(amax);
   const float inv = mx_inv_scale(sc);
   uint32_t wds[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int r = 4 * u;
-    wds[u] = e4m3_encode(tile[r][threadIdx.x] * inv) | (e4m3_encode(tile[r + 1][threadIdx.x] * inv) << 8) |
-             (e4m3_encode(tile[r + 2][threadIdx.x] * inv) << 16) |
-             (e4m3_encode(tile[r + 3][threadIdx.x] * inv) << 24);
+    const int r = 32 * qb + 4 * u;
+    wds[u] = e4m3_encode(tile[r][cl] * inv) | (e4m3_encode(tile[r + 1][cl] * inv) << 8) |
+             (e4m3_encode(tile[r + 2][cl] * inv) << 16) | (e4m3_encode(tile[r + 3][cl] * inv) << 24);
   }
-  uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + 32 * rb);
+  uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + r0 + 32 * qb);
   d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
   d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
-  dsts[N * (koff / 32) + n * (kp / 32) + rb] = (uint8_t)sc;
+  dsts[N * (koff / 32) + n * (kp / 32) + r0 / 32 + qb] = (uint8_t)sc;
+}
+
+// koff[e] = sum over e' < e of tok_pad(rows of e'), e = 0..E, by a Hillis-Steele
+// scan of up to kMaxExperts values in one workgroup (integer, exact).
+__global__ __launch_bounds__(256) void token_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                            int32_t* __restrict__ koff) {
+  __shared__ int v[2][kMaxExperts + 1];
+  for (int i = threadIdx.x; i <= E; i += 256) v[0][i] = i == 0 ? 0 : tok_pad(offsets[i] - offsets[i - 1]);
+  __syncthreads();
+  int cur = 0;
+  for (int d = 1; d <= E; d <<= 1) {
+    for (int i = threadIdx.x; i <= E; i += 256) v[cur ^ 1][i] = v[cur][i] + (i >= d ? v[cur][i - d] : 0);
+    __syncthreads();
+    cur ^= 1;
+  }
+  for (int i = threadIdx.x; i <= E; i += 256) koff[i] = v[cur][i];
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
@@ -321,12 +342,19 @@ hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K,
 }
 
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
-                                     const int32_t* offsets, int E, int64_t R, int64_t N,
-                                     uint8_t* dst, uint8_t* dst_scales, hipStream_t st) {
+                                     const int32_t* offsets, const int32_t* koff, int E, int64_t R,
+                                     int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st) {
   const int64_t positions = R + 128 * (int64_t)E;          // bound of the padded token axis
   if (R <= 0 || N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(token_quantize_kernel, dim3((unsigned)((positions + 31) / 32), (unsigned)((N + 255) / 256)),
-                     dim3(256), 0, st, src, ld, perm, topk, offsets, E, N, dst, dst_scales);
+  if (E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(token_quantize_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((positions + 127) / 128)),
+                     dim3(256), 0, st, src, ld, perm, topk, offsets, koff, E, N, dst, dst_scales);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int32_t* koff, hipStream_t st) {
+  if (E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(token_offsets_kernel, dim3(1), dim3(256), 0, st, offsets, E, koff);
   return hipGetLastError();
 }
 

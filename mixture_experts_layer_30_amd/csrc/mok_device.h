@@ -23,13 +23,10 @@ struct mok_tile {          // one row tile of one expert: permuted rows [p0, p1)
 
 // Token-blocked MXFP8 layout of the backward: an expert with c routed rows
 // takes tok_pad(c) positions of the padded token axis (c rounded up to 128,
-// so its scale words are whole), starting at tok_koff(offsets, e).
+// so its scale words are whole), starting at koff[e] = the sum of tok_pad
+// over the experts before it (mok_launch_token_offsets computes koff[0..E]).
 MOK_DEV int tok_pad(int c) { return (c + 127) & ~127; }
-MOK_DEV int tok_koff(const int32_t* offsets, int e) {
-  int k = 0;
-  for (int i = 0; i < e; ++i) k += tok_pad(offsets[i + 1] - offsets[i]);
-  return k;
-}
+constexpr int kMaxExperts = 512;
 
 // ------------------------------------------------------------------ bf16 helpers
 MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
@@ -62,26 +59,21 @@ MOK_DEV int mx_scale_byte(float amax) {
 
 // E4M3 code of q (|q| < 2^9 after block scaling), round to nearest even,
 // saturating to +-448; the sign bit is copied from q (so -0 -> 0x80).
+// Branch-free: for |q| >= 2^-6 the float's 23-bit mantissa is rounded to 3
+// bits in the integer domain (adding 2^19 - 1 plus the lowest kept bit
+// carries exactly when the dropped part is above half, or half with an odd
+// kept part; a carry out of the mantissa bumps the exponent), the exponent
+// is rebiased from 127 to 7, and codes above 0x7E (448) saturate; below 2^-6
+// the value is a multiple of 2^-9, rounded with rint (ties to even, 8 ->
+// 0x08 = 2^-6).
 MOK_DEV uint32_t e4m3_encode(float q) {
-  uint32_t b = __float_as_uint(q);
-  uint32_t sign = (b >> 24) & 0x80u;
-  float a = fabsf(q);
-  uint32_t code;
-  if (a >= 448.0f) {
-    code = 0x7E;
-  } else if (a < 0.015625f) {            // below 2^-6: subnormal grid of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);   // rint = ties to even; 8 -> 0x08
-  } else {
-    uint32_t ab = __float_as_uint(a);
-    int ex = (int)((ab >> 23) & 0xFF) - 127;        // -6 .. 8
-    uint32_t mant = ab & 0x7FFFFFu;
-    uint32_t keep = mant >> 20, rem = mant & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
-    if (keep == 8u) { keep = 0; ++ex; }
-    code = ((uint32_t)(ex + 7) << 3) | keep;
-    if (code > 0x7Eu) code = 0x7E;
-  }
-  return code | sign;
+  const uint32_t b = __float_as_uint(q);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t ab = b & 0x7FFFFFFFu;
+  const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);
+  const int32_t nc = min((int32_t)(r >> 20) - (120 << 3), 0x7E);
+  const uint32_t sc = (uint32_t)__builtin_rintf(__uint_as_float(ab) * 512.0f);
+  return (ab < 0x3C800000u ? sc : (uint32_t)nc) | sign;   // 0x3C800000 = 2^-6
 }
 
 // 2^(127 - s) as a float multiplier (exact; s in 0..254).

@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int32_t kVersion = 100;   // 0.1.0
-constexpr int kMaxE = 512;
+constexpr int kMaxE = kMaxExperts;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -125,7 +125,7 @@ struct FwdWs {
 struct BwdWs {
   size_t dO, dab, hb, dxrows;
   // MXFP8 only
-  size_t dOq, dOs, dabq, dabs, dOT, dOTs, hT, hTs, dabT, dabTs, xT, xTs;
+  size_t dOq, dOs, dabq, dabs, dOT, dOTs, hT, hTs, dabT, dabTs, xT, xTs, koff;
   size_t total;
 };
 
@@ -151,7 +151,7 @@ BwdWs bwd_ws(const Resolved& r) {
   w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
-  w.dOq = w.dOs = w.dabq = w.dabs = w.dOT = w.dOTs = w.hT = w.hTs = w.dabT = w.dabTs = w.xT = w.xTs = 0;
+  w.dOq = w.dOs = w.dabq = w.dabs = w.dOT = w.dOTs = w.hT = w.hTs = w.dabT = w.dabTs = w.xT = w.xTs = w.koff = 0;
   if (r.mx) {
     // token-blocked operands: KT bounds the padded token axis (each expert's
     // rows rounded up to 128)
@@ -169,6 +169,7 @@ BwdWs bwd_ws(const Resolved& r) {
     w.dabTs = o; o = align_up(o + 2 * I * (KT / 32));
     w.xT = o;    o = align_up(o + H * KT);
     w.xTs = o;   o = align_up(o + H * (KT / 32));
+    w.koff = o;  o = align_up(o + 4 * ((size_t)r.E + 1));
   }
   w.total = o;
   return w;
@@ -464,6 +465,8 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     a.hT = ws + W.hT;     a.hTs = ws + W.hTs;
     a.dabT = ws + W.dabT; a.dabTs = ws + W.dabTs;
     a.xT = ws + W.xT;     a.xTs = ws + W.xTs;
+    a.koff = reinterpret_cast<int32_t*>(ws + W.koff);
+    MOK_RUN("token_offsets", mok_launch_token_offsets(sp.offsets, r.E, a.koff, st));
     if (r.T > 0) {
       MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                          sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
@@ -472,14 +475,14 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
       // never read)
       MOK_RUN("mx_quantize_dO", mok_launch_mxfp8_quantize(a.dO, r.R, r.H, a.dOq, a.dOs, st));
       MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh8(a, st));
-      MOK_RUN("token_quantize", mok_launch_token_quantize(a.dO, r.H, nullptr, r.k, sp.offsets, r.E, r.R, r.H,
+      MOK_RUN("token_quantize_dO", mok_launch_token_quantize(a.dO, r.H, nullptr, r.k, sp.offsets, a.koff, r.E, r.R, r.H,
                                                           a.dOT, a.dOTs, st));
-      MOK_RUN("token_quantize", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, sp.offsets, r.E, r.R, r.I,
+      MOK_RUN("token_quantize_h", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, sp.offsets, a.koff, r.E, r.R, r.I,
                                                           a.hT, a.hTs, st));
-      MOK_RUN("token_quantize", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, sp.offsets, r.E, r.R,
+      MOK_RUN("token_quantize_dAB", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, sp.offsets, a.koff, r.E, r.R,
                                                           2 * r.I, a.dabT, a.dabTs, st));
-      MOK_RUN("token_quantize", mok_launch_token_quantize(static_cast<const bf16_t*>(x), r.H, sp.perm, r.k,
-                                                          sp.offsets, r.E, r.R, r.H, a.xT, a.xTs, st));
+      MOK_RUN("token_quantize_x", mok_launch_token_quantize(static_cast<const bf16_t*>(x), r.H, sp.perm, r.k,
+                                                          sp.offsets, a.koff, r.E, r.R, r.H, a.xT, a.xTs, st));
     }
     MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd8(a, st));
     MOK_RUN("bwd_dwgu_gemm", mok_launch_bwd_dwgu8(a, st));

@@ -135,6 +135,7 @@ struct mok_bwd_args {
   uint8_t* dabTs;
   uint8_t* xT;           // token-blocked x rows (N = H)
   uint8_t* xTs;
+  int32_t* koff;         // [E+1] start of each expert on the padded token axis
 };
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st);     // dh, SwiGLU bwd
@@ -150,5 +151,7 @@ hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st);
 // mok_bwd_args): row p of the source is src + p*ld, or with perm the token
 // row src + (perm[p] / topk)*ld; N columns; R routed rows.
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
-                                     const int32_t* offsets, int E, int64_t R, int64_t N,
-                                     uint8_t* dst, uint8_t* dst_scales, hipStream_t st);
+                                     const int32_t* offsets, const int32_t* koff, int E, int64_t R,
+                                     int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st);
+// koff[0..E] of the padded token axis from the expert offsets (one workgroup)
+hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int32_t* koff, hipStream_t st);
