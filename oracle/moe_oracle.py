@@ -457,6 +457,27 @@ def _mx_along_tokens(V):
     return _mx_along_cols(Vp)[:c]
 
 
+def _mx_backward_rows(X, dYr, wr, W, Q):
+    """One expert's rows in permuted order: X [c][H] their x rows, dYr [c][H]
+    the upstream gradient of their tokens, wr [c] their combine weights; W the
+    expert's exact (Wg, Wu, Wd), Q its dequantized forward copies.
+    Returns the rows' expert outputs and dX rows (both row-local), and the
+    expert's dWg, dWu, dWd (which need all of its rows)."""
+    Wg, Wu, Wd = W
+    out, a, b = _mx_ffn(X, *Q, with_ab=True)
+    h = swiglu(a, b)
+    dO = wr[:, None] * dYr
+    dh = _mx_along_rows(dO) @ _mx_along_cols(Wd)
+    dA, dB = _swiglu_backward(dh, a, b)
+    dAB = _mx_along_rows(np.concatenate([dA, dB], axis=1))
+    dxr = dAB @ _mx_along_cols(np.concatenate([Wg, Wu], axis=0))
+    Xt = _mx_along_tokens(X)
+    dWg = _mx_along_tokens(dA).T @ Xt
+    dWu = _mx_along_tokens(dB).T @ Xt
+    dWd = _mx_along_tokens(dO).T @ _mx_along_tokens(h)
+    return out, dxr, dWg, dWu, dWd
+
+
 def backward_mxfp8(x, topk_ids, topk_w, experts, dy):
     """MXFP8 backward (readings above). Returns the same dict as backward()."""
     x = np.asarray(x, np.float64)
@@ -470,18 +491,8 @@ def backward_mxfp8(x, topk_ids, topk_w, experts, dy):
     R = T * k
     I = np.asarray(experts[0][0]).shape[0]
     qexp = _mx_experts(experts)
-    obuf = np.zeros((R, H))
-    ab = {}
-    for e in range(E):
-        lo, hi = s["offsets"][e], s["offsets"][e + 1]
-        if hi == lo:
-            continue
-        P = s["perm"][lo:hi]
-        obuf[P], a, b = _mx_ffn(x[P // k], *qexp[e], with_ab=True)
-        ab[e] = (a, b)
-    y = np.einsum("tj,tjh->th", w, obuf.reshape(T, k, H))
-    dw = np.einsum("th,tjh->tj", dy, obuf.reshape(T, k, H))
     wf = w.reshape(-1)
+    obuf = np.zeros((R, H))
     dxrows = np.zeros((R, H))
     dWg = np.zeros((E, I, H))
     dWu = np.zeros((E, I, H))
@@ -491,19 +502,47 @@ def backward_mxfp8(x, topk_ids, topk_w, experts, dy):
         if hi == lo:
             continue
         P = s["perm"][lo:hi]
-        Wg, Wu, Wd = experts[e]
-        a, b = ab[e]
-        X = x[P // k]
-        h = swiglu(a, b)
-        dO = wf[P][:, None] * dy[P // k]
-        dh = _mx_along_rows(dO) @ _mx_along_cols(Wd)
-        dA, dB = _swiglu_backward(dh, a, b)
-        dAB = _mx_along_rows(np.concatenate([dA, dB], axis=1))
-        Wgu = _mx_along_cols(np.concatenate([Wg, Wu], axis=0))
-        dxrows[P] = dAB @ Wgu
-        dWd[e] = _mx_along_tokens(dO).T @ _mx_along_tokens(h)
-        Xt = _mx_along_tokens(X)
-        dWg[e] = _mx_along_tokens(dA).T @ Xt
-        dWu[e] = _mx_along_tokens(dB).T @ Xt
+        obuf[P], dxrows[P], dWg[e], dWu[e], dWd[e] = _mx_backward_rows(
+            x[P // k], dy[P // k], wf[P], experts[e], qexp[e])
+    y = np.einsum("tj,tjh->th", w, obuf.reshape(T, k, H))
+    dw = np.einsum("th,tjh->tj", dy, obuf.reshape(T, k, H))
     dx = dxrows.reshape(T, k, H).sum(axis=1)
     return {"dx": dx, "dWg": dWg, "dWu": dWu, "dWd": dWd, "dw": dw, "y": y}
+
+
+def backward_mxfp8_expert_weights(e, x, topk_ids, topk_w, experts, dy):
+    """(dWg[e], dWu[e], dWd[e]) of the MXFP8 backward for one expert, from all
+    rows routed to it (in permuted order: ascending flat index)."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids).reshape(T, -1)
+    w = np.asarray(topk_w, np.float64).reshape(ids.shape)
+    sel = np.argwhere(ids == e)
+    Wg, Wu, Wd = experts[e]
+    I = Wg.shape[0]
+    if sel.size == 0:
+        return np.zeros((I, H)), np.zeros((I, H)), np.zeros((H, I))
+    t, j = sel[:, 0], sel[:, 1]
+    _, _, dWg, dWu, dWd = _mx_backward_rows(x[t], np.asarray(dy, np.float64)[t], w[t, j], experts[e],
+                                            _mx_experts(experts)[e])
+    return dWg, dWu, dWd
+
+
+def backward_mxfp8_tokens(x_rows, ids_rows, w_rows, experts, dy_rows):
+    """dx and d topk_w of the MXFP8 backward for a subset of tokens (their
+    parts are row-local: per-row quantization along H and 2I)."""
+    x_rows = np.asarray(x_rows, np.float64)
+    dy_rows = np.asarray(dy_rows, np.float64)
+    n, H = x_rows.shape
+    ids_rows = np.asarray(ids_rows).reshape(n, -1)
+    w_rows = np.asarray(w_rows, np.float64).reshape(n, -1)
+    qexp = _mx_experts(experts)
+    dx = np.zeros((n, H))
+    dw = np.zeros(ids_rows.shape)
+    for e in sorted(set(int(v) for v in ids_rows.reshape(-1) if 0 <= v < len(experts))):
+        sel = np.argwhere(ids_rows == e)
+        t, j = sel[:, 0], sel[:, 1]
+        out, dxr, _, _, _ = _mx_backward_rows(x_rows[t], dy_rows[t], w_rows[t, j], experts[e], qexp[e])
+        dw[t, j] = np.sum(dy_rows[t] * out, axis=1)
+        np.add.at(dx, t, dxr)
+    return dx, dw

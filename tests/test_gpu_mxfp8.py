@@ -202,3 +202,32 @@ def test_mxfp8_backward_bitwise_deterministic():
         for a, b in zip(g, g0):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.timeout(900)
+def test_mxfp8_fwd_bwd_full_size_sampled():
+    """The benchmark workload (T=4096, H=2048, E=64, top-8, I=768) through the
+    MXFP8 forward with context and the MXFP8 backward at the default
+    minibatch: sampled tokens for dx and d topk_w, the least and most loaded
+    experts for the weight gradients."""
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs, host_inputs, sampled_tokens
+    p = CONFIGS[1]
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    dy = make_dy(p)
+    _, (dx, dwg, dwu, dwd, dtw) = gpu_mx_fwd_bwd(p, device_inputs(p), dy)
+    ex = ExpertsF64(wg, wu, wd)
+    toks = sampled_tokens(p.T, 2, 5)
+    dxr, dwr = oracle.backward_mxfp8_tokens(f64(x[toks]), ids[toks], w[toks].astype(np.float64), ex,
+                                            f64(dy[toks]))
+    errs = {"dx[sampled]": rel_fro(from_dev_bf16(dx)[toks], dxr),
+            "d topk_w[sampled]": rel_fro(dtw.cpu().numpy()[toks].astype(np.float64), dwr)}
+    counts = np.bincount(ids.reshape(-1), minlength=p.E)
+    for e in (int(np.argmin(counts)), int(np.argmax(counts))):
+        dg, du, dd = oracle.backward_mxfp8_expert_weights(e, f64(x), ids, w.astype(np.float64), ex, f64(dy))
+        errs[f"dWg[{e}]"] = rel_fro(from_dev_bf16(dwg[e]), dg)
+        errs[f"dWu[{e}]"] = rel_fro(from_dev_bf16(dwu[e]), du)
+        errs[f"dWd[{e}]"] = rel_fro(from_dev_bf16(dwd[e]), dd)
+    print("MXFP8 backward, full size:", {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= REL_FRO_MXFP8_BWD, f"{k}: relative Frobenius error {v:.3e}"

@@ -137,3 +137,17 @@ def test_empty_expert_exact_zero():
     g = mxb(x, ids, w, ex, dy)
     for key in ("dWg", "dWu", "dWd"):
         assert not g[key][3].any()
+
+
+def test_sampled_helpers_match_full():
+    x, ids, w, ex = rand_case(40, 64, 64, 5, 2, seed=71)
+    dy = np.random.default_rng(72).standard_normal((40, 64))
+    g = mxb(x, ids, w, ex, dy)
+    for e in range(5):
+        dWg, dWu, dWd = oracle.backward_mxfp8_expert_weights(e, x, ids, w, ex, dy)
+        assert rel(dWg, g["dWg"][e]) < 1e-12 and rel(dWu, g["dWu"][e]) < 1e-12
+        assert rel(dWd, g["dWd"][e]) < 1e-12
+    toks = np.array([0, 7, 19, 33])
+    dx, dw = oracle.backward_mxfp8_tokens(x[toks], ids[toks], w[toks], ex, dy[toks])
+    assert rel(dx, g["dx"][toks]) < 1e-12
+    assert rel(dw, g["dw"][toks]) < 1e-12
