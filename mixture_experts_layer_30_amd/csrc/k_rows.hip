@@ -104,10 +104,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // order (each lane sums its columns in ascending order, then a xor butterfly),
 // and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order. The k rows go 8 at
 // a time through one pass over the columns, so their loads overlap.
+// With dOq (MXFP8 backward) each dO row is also quantized along H from its
+// bf16 values: a 32-column block is the 4 chunks of 4 adjacent lanes.
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
-    int64_t H, float* __restrict__ dw, bf16_t* __restrict__ dO) {
+    int64_t H, float* __restrict__ dw, bf16_t* __restrict__ dO, uint8_t* __restrict__ dOq,
+    uint8_t* __restrict__ dOs) {
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
   if (t >= T) return;
@@ -144,7 +147,25 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
           part[u] = fmaf(g[q], o[q], part[u]);
           d[q] = wv[u] * g[q];
         }
-        reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = pack8(d);
+        const uint4 packed = pack8(d);
+        reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = packed;
+        if (dOq) {
+          float b[8];
+          unpack8(packed, b);                    // the stored bf16 values
+          float amax = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(b[q]));
+          amax = fmaxf(amax, __shfl_xor(amax, 1));
+          amax = fmaxf(amax, __shfl_xor(amax, 2));
+          const int sc = mx_scale_byte(amax);
+          const float inv = mx_inv_scale(sc);
+          const uint32_t lo = e4m3_encode(b[0] * inv) | (e4m3_encode(b[1] * inv) << 8) |
+                              (e4m3_encode(b[2] * inv) << 16) | (e4m3_encode(b[3] * inv) << 24);
+          const uint32_t hi = e4m3_encode(b[4] * inv) | (e4m3_encode(b[5] * inv) << 8) |
+                              (e4m3_encode(b[6] * inv) << 16) | (e4m3_encode(b[7] * inv) << 24);
+          reinterpret_cast<uint2*>(dOq + (int64_t)pos[u] * H)[c] = make_uint2(lo, hi);
+          if ((c & 3) == 0) dOs[(int64_t)pos[u] * (H / 32) + (c >> 2)] = (uint8_t)sc;
+        }
       }
     }
 #pragma unroll
@@ -314,11 +335,11 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
 
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, bf16_t* dO,
-                                      hipStream_t st) {
+                                      int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
+                                      uint8_t* dOs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(reverse_combine_kernel, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf, w,
-                     dest, offsets_E, T, topk, H, dw, dO);
+                     dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
   return hipGetLastError();
 }
 

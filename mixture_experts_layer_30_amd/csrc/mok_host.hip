@@ -468,12 +468,10 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     a.koff = reinterpret_cast<int32_t*>(ws + W.koff);
     MOK_RUN("token_offsets", mok_launch_token_offsets(sp.offsets, r.E, a.koff, st));
     if (r.T > 0) {
+      // also quantizes the dO rows along H for dh
       MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                          sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
-                                         const_cast<bf16_t*>(a.dO), st));
-      // dO rows along H for dh (rows of invalid ids are quantized too, and
-      // never read)
-      MOK_RUN("mx_quantize_dO", mok_launch_mxfp8_quantize(a.dO, r.R, r.H, a.dOq, a.dOs, st));
+                                         const_cast<bf16_t*>(a.dO), a.dOq, a.dOs, st));
       MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh8(a, st));
       MOK_RUN("token_quantize_dO", mok_launch_token_quantize(a.dO, r.H, nullptr, r.k, sp.offsets, a.koff, r.E, r.R, r.H,
                                                           a.dOT, a.dOTs, st));
@@ -496,7 +494,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   if (r.T > 0) {
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                        sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
-                                       const_cast<bf16_t*>(a.dO), st));
+                                       const_cast<bf16_t*>(a.dO), nullptr, nullptr, st));
     MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
   }
   MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));

@@ -46,7 +46,8 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
 // dw[t][j] = <dy[t], obuf[t*k+j]>; dO[dest[t*k+j]] = bf16(w[t][j] * dy[t]).
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, bf16_t* dO, hipStream_t st);
+                                      int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
+                                      uint8_t* dOs, hipStream_t st);
 
 // dx[t] = sum_j dxrows[t*k+j] (valid rows only), fp32, j ascending.
 hipError_t mok_launch_reverse_dispatch(const bf16_t* dxrows, const int32_t* dest,

@@ -231,3 +231,23 @@ def test_mxfp8_fwd_bwd_full_size_sampled():
     print("MXFP8 backward, full size:", {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= REL_FRO_MXFP8_BWD, f"{k}: relative Frobenius error {v:.3e}"
+
+
+def test_mxfp8_backward_one_hot_expert_and_invalid_ids():
+    """Out-of-range ids: their rows sort after all valid rows, get no expert
+    output (d topk_w 0, no dx contribution) and no token-blocked positions."""
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs, host_inputs
+    p = problem(200, 256, 128, 6, 2, seed=21)
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    ids2 = ids.copy()
+    ids2[:, 0] = 4                      # one expert gets a row of every token
+    ids2[:, 1] = np.where(np.arange(200) % 3 == 0, 2, 5)
+    ids2[7, 1] = 99
+    ids2[150, 0] = -1
+    dy = make_dy(p)
+    _, got = gpu_mx_fwd_bwd(p, device_inputs(p, ids2), dy)
+    ref = oracle.backward_mxfp8(f64(x), ids2, w.astype(np.float64), ExpertsF64(wg, wu, wd), f64(dy))
+    dtw = got[4].cpu().numpy()
+    assert dtw[7, 1] == 0.0 and dtw[150, 0] == 0.0
+    _check_mx_backward(p, got, ref)
