@@ -38,7 +38,7 @@ GEMM_FLOPS_PER_ROW = {
 # (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy of known
 # size); valid only for the kernel sources and workload it was taken on.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gemm_traffic_bf16_T4096_H2048_E64_k8_I768.txt")
-KERNEL_SOURCES = ["gemm_core.h", "k_gemm.hip", "mok_device.h", "mok_launch.h", "mok_host.hip"]
+KERNEL_SOURCES = ["gemm_core.h", "k_gemm.hip", "k_rows.hip", "mok_device.h", "mok_launch.h", "mok_host.hip"]
 
 
 def kernel_sources_sha256():
@@ -93,12 +93,29 @@ def parse():
     return ap.parse_args()
 
 
-# kernel name prefixes (as rocprofv3 prints them) of the bf16 GEMM kernels
+# kernel name prefixes (as rocprofv3 prints them) of the bf16 GEMM kernels and
+# of the row-moving (permute) kernels; combine_kernel serves both the combine
+# and the reverse-dispatch, so its record averages the two launches
 GEMM_KERNEL_NAMES = {
     "gateup_kernel<false>": "gateup_gemm", "down_kernel<false>": "down_gemm",
     "bwd_dh_kernel": "bwd_dh_gemm", "bwd_dwd_kernel": "bwd_dwd_gemm",
     "bwd_dwgu_kernel": "bwd_dwgu_gemm", "bwd_dx_kernel": "bwd_dx_gemm",
+    "gather_kernel": "gather", "reverse_combine_kernel": "reverse_combine",
+    "::combine_kernel": "combine+reverse_dispatch",
 }
+
+
+def permute_bytes(p):
+    """Algorithmic HBM bytes per step of the row-moving kernels (rows moved in
+    + out; index and weight arrays included), summed over a step's launches
+    (the gather runs once per minibatch)."""
+    R, T, H = p.R, p.T, p.H
+    return {
+        "gather": R * 2 * H * 2 + R * 4,                         # x row in, ring row out, perm
+        "combine": R * 2 * H + R * 8 + T * 2 * H,                # obuf rows, w + dest, y rows
+        "reverse_combine": R * 2 * H * 2 + T * 2 * H + R * 12,   # obuf in, dO out, dY, w/dest/dw
+        "reverse_dispatch": R * 2 * H + R * 4 + T * 2 * H,       # dX rows, dest, dx rows
+    }
 
 
 def _counter_per_dispatch(path, counter):
@@ -152,7 +169,7 @@ def write_traffic_record(args):
            "write_factor": round(wf, 4), "sources_sha256": kernel_sources_sha256(), "kernels": kernels}
     extra = f" --minibatch-rows {args.minibatch_rows}" if args.minibatch_rows else ""
     lines = [
-        f"# HBM traffic of the grouped-GEMM kernels: MoE layer step, bf16, {p.name} "
+        f"# HBM traffic of the grouped-GEMM and row-moving kernels: MoE layer step, bf16, {p.name} "
         f"(minibatch {mb_rows} rows)",
         "",
         "Commands (repository root on an MI355X, ROCm 7.2; one counter per run):",
@@ -173,7 +190,8 @@ def write_traffic_record(args):
         f"{copy_kib / wf:.1f} KiB, so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f} "
         "(the copy moves 1048576 KiB each way).",
         "",
-        "Per dispatch averages over the run (3 steps, every launch of each kernel):",
+        "Per dispatch averages over the run (3 steps, every launch of each kernel; "
+        "`combine_kernel` serves both the forward combine and the backward reverse-dispatch):",
         "",
         "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
         "|---|---:|---:|---:|---:|",
@@ -364,9 +382,26 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
                 "flops_per_launch": dom_flops_per_launch, "avg_launch_ms": stats[dom][1] / dn}
+    permute = {}
+    for k, nbytes in permute_bytes(p).items():
+        if k in kernels:
+            kms, nl = kernels[k]["ms_per_step"], kernels[k]["launches_per_step"]
+            permute[k] = {"algorithmic_gbs": round(nbytes / (kms * 1e-3) / 1e9, 1),
+                          "bytes_per_step": nbytes, "ms_per_step": round(kms, 4),
+                          "launches_per_step": nl}
+            # counters of combine_kernel average its combine and reverse-dispatch launches
+            key = "combine+reverse_dispatch" if k in ("combine", "reverse_dispatch") else k
+            tb, _ = measured_traffic(key, p, mb_rows)
+            if tb is not None:
+                permute[k]["measured_hbm_gbs"] = round(tb * nl / (kms * 1e-3) / 1e9, 1)
+    if permute:
+        tot_b = sum(v["bytes_per_step"] for v in permute.values())
+        tot_ms = sum(v["ms_per_step"] for v in permute.values())
+        permute["all"] = {"algorithmic_gbs": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+                          "bytes_per_step": tot_b, "ms_per_step": round(tot_ms, 4),
+                          "frac_of_hbm_peak": round(tot_b / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     move = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
-               for k in ("schedule", "gather", "combine", "reverse_combine", "bwd_gather",
-                         "reverse_dispatch"))
+               for k in ("schedule", "gather", "combine", "reverse_combine", "reverse_dispatch"))
     gemm_ms = sum(v["ms_per_step"] for v in gemms.values())
     fwd_flops = p.fwd_flops()
     out = {
@@ -386,6 +421,8 @@ def main():
         "sched_gather_combine_share": round(move / ms_step, 4),
         "schedule_share": round(kernels.get("schedule", {}).get("ms_per_step", 0.0) / ms_step, 4),
         "kernels": kernels,
+        "permute_gbs": round(permute["all"]["algorithmic_gbs"], 1) if permute else None,
+        "permute": permute,
         "roofline": roofline,
     }
     if ms_fwd is not None:
