@@ -612,6 +612,49 @@ MOK_DEV void store_tile_bf16(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nro
   }
 }
 
+// Store a tile accumulated with the operands exchanged (mainloop called with
+// the column-side loader first, so acc holds the transpose: accumulator row
+// index = output column, accumulator column index = output row) as bf16 rows.
+// Each lane then holds 4 adjacent output columns per 4 accumulator elements:
+// they are rounded in pairs (v_cvt_pk_bf16_f32, round to nearest even) and
+// written as one 8-byte LDS store; the whole 256 x 256 bf16 tile is staged at
+// once (128 KiB; 16-byte chunk c of row m at chunk c ^ (m & 15), so the 32 rows
+// of one store instruction spread over all banks), then read back and stored
+// as 16-byte vectors along rows. dst(r), nrows and ncols as in store_tile_bf16.
+template <class G, class Dst>
+MOK_DEV void store_tile_bf16_t(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nrows, int ncols, Dst dst) {
+  static_assert(G::BM == 256 && G::BN == 256, "256 x 256 tiles");
+  typedef __attribute__((ext_vector_type(2))) float f2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2_t;
+  constexpr int PITCH = 512;
+  const int l = lane_id();
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < G::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) {
+      const int m = G::wn() * G::WTN + j * 32 + (l & 31);            // output row
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n0 = G::wm() * G::WTM + i * 32 + 8 * g + 4 * (l >> 5);   // output column
+        const b2_t lo = __builtin_convertvector((f2_t){acc.c[i][j][4 * g], acc.c[i][j][4 * g + 1]}, b2_t);
+        const b2_t hi = __builtin_convertvector((f2_t){acc.c[i][j][4 * g + 2], acc.c[i][j][4 * g + 3]}, b2_t);
+        const int off = m * PITCH + ((((n0 >> 3) ^ (m & 15))) << 4) + ((n0 & 7) << 1);
+        *reinterpret_cast<uint2*>(lds + off) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+      }
+    }
+  __syncthreads();
+  constexpr int CPR = G::BN / 8;                                     // 16-byte chunks per row
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < G::BM * CPR; idx += kThreads) {
+    const int r = idx / CPR, c = idx % CPR;
+    if (r >= nrows || 8 * c >= ncols) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + ((c ^ (r & 15)) << 4));
+    *reinterpret_cast<uint4*>(dst(r) + 8 * c) = v;
+  }
+}
+
 // Logical tile of this workgroup for a 1-D grid over `total` tiles.
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs (each
 // with its own L2); this gives each XCD one contiguous range of logical

@@ -150,6 +150,24 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
   }
 }
 
+// Kernels whose tile ends in a plain bf16 row store can run the main loop with
+// the operands exchanged and store the transposed accumulators directly
+// (store_tile_bf16_t); chosen per kernel family from measurements.
+constexpr bool kTrDown = true, kTrDx = true, kTrDw = true;
+
+template <bool TR, class G, bool F8, class LA, class LB, class SA, class SB>
+MOK_DEV void mainloop_x(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
+                        Acc<G::FM, G::FN>& acc) {
+  if constexpr (TR) mainloop<G, F8>(sm, lb, la, sb, sa, nk, acc);
+  else mainloop<G, F8>(sm, la, lb, sa, sb, nk, acc);
+}
+
+template <bool TR, class G, class Dst>
+MOK_DEV void store_bf16_x(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nrows, int ncols, Dst dst) {
+  if constexpr (TR) store_tile_bf16_t<G>(lds, acc, nrows, ncols, dst);
+  else store_tile_bf16<G>(lds, acc, nrows, ncols, dst);
+}
+
 // down GEMM of one row tile x 256 output columns; each row is pushed to its
 // flat position perm[p] of obuf (unique destinations, no atomics).
 template <bool F8>
@@ -169,17 +187,19 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) 
     const int64_t sx = I / 32;
     LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_hs + ft.slot_row0 * sx, sx, ft.nrows}};
     LoadScalesD<G::BN, RowsStrided> lsb{{a.sd + ((int64_t)ft.t.e * H + n0) * sx, sx, (int)(H - n0)}};
-    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(I / 64), acc);
+    mainloop_x<kTrDown, G, true>(sm, la, lb, lsa, lsb, (int)(I / 64), acc);
   } else {
     NoScales ns;
-    mainloop<G, false>(sm, la, lb, ns, ns, (int)(I / 32), acc);
+    mainloop_x<kTrDown, G, false>(sm, la, lb, ns, ns, (int)(I / 32), acc);
   }
-  // destination rows, staged above the epilogue's fp32 half-tile
+  // destination rows, staged in the top 1 KiB of LDS once every wavefront
+  // has left the main loop
   int* rows = tile_rows<Smem<G, F8>>(lds_raw);
+  __syncthreads();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < ft.nrows ? a.perm[ft.t.p0 + r] : 0;
   bf16_t* ob = a.obuf + n0;
-  store_tile_bf16<G>(lds_raw, acc, ft.nrows, (int)(H - n0),
-                     [&](int r) { return ob + (int64_t)rows[r] * H; });
+  store_bf16_x<kTrDown, G>(lds_raw, acc, ft.nrows, (int)(H - n0),
+                           [&](int r) { return ob + (int64_t)rows[r] * H; });
 }
 
 // One launch covers the tiles of minibatches [m0, m1). Launch grids are 1-D
@@ -282,12 +302,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
                         2 * H, (int)(2 * I), (int)min<int64_t>(G::BN, H - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), acc);
+  mainloop_x<kTrDx, G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), acc);
   int* rows = tile_rows<Smem<G, false>>(lds_raw);
+  __syncthreads();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   bf16_t* d = a.dxrows + n0;
-  store_tile_bf16<G>(lds_raw, acc, nrows, (int)(H - n0),
-                     [&](int r) { return d + (int64_t)rows[r] * H; });
+  store_bf16_x<kTrDx, G>(lds_raw, acc, nrows, (int)(H - n0),
+                         [&](int r) { return d + (int64_t)rows[r] * H; });
 }
 
 // Weight gradients out[m][n] = sum over the expert's rows p (ascending) of
@@ -302,8 +323,8 @@ MOK_DEV void dw_tile(uint8_t* lds_raw, const bf16_t* A, int64_t lda, int mlimit,
                         0x7FFFFFFF, 2 * ldb, K, nlimit};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (K + 31) / 32, acc);
-  store_tile_bf16<G>(lds_raw, acc, mlimit, nlimit, [&](int r) { return out + (int64_t)r * ldo; });
+  mainloop_x<kTrDw, G, false>(sm, la, lb, ns, ns, (K + 31) / 32, acc);
+  store_bf16_x<kTrDw, G>(lds_raw, acc, mlimit, nlimit, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int tiles_per_e) {
@@ -444,11 +465,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx8_kernel(mok_bwd_args a, in
   const LoadScalesD<G::BM, RowsStrided> lsa{{a.dabs + (int64_t)t.p0 * sK, sK, nrows}};
   const LoadScalesD<G::BN, RowsStrided> lsb{{a.wgut_s + wrow * sK, sK, (int)(H - n0)}};
   Acc<G::FM, G::FN> acc;
-  mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), acc);
+  mainloop_x<kTrDx, G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), acc);
   int* rows = tile_rows<Smem<G, true>>(lds_raw);
+  __syncthreads();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   bf16_t* d = a.dxrows + n0;
-  store_tile_bf16<G>(lds_raw, acc, nrows, (int)(H - n0), [&](int r) { return d + (int64_t)rows[r] * H; });
+  store_bf16_x<kTrDx, G>(lds_raw, acc, nrows, (int)(H - n0), [&](int r) { return d + (int64_t)rows[r] * H; });
 }
 
 // Weight gradient out[m][n] = sum over the expert's rows of A[m][k] B[n][k],
@@ -462,8 +484,8 @@ MOK_DEV void dw8_tile(uint8_t* lds_raw, const uint8_t* A, const uint8_t* As, int
   const LoadScalesD<G::BM, RowsStrided> lsa{{As, kp / 32, mlim}};
   const LoadScalesD<G::BN, RowsStrided> lsb{{Bs, kp / 32, nlim}};
   Acc<G::FM, G::FN> acc;
-  mainloop<G, true>(sm, la, lb, lsa, lsb, kp / 64, acc);
-  store_tile_bf16<G>(lds_raw, acc, mlim, nlim, [&](int r) { return out + (int64_t)r * ldo; });
+  mainloop_x<kTrDw, G, true>(sm, la, lb, lsa, lsb, kp / 64, acc);
+  store_bf16_x<kTrDw, G>(lds_raw, acc, mlim, nlim, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, int tiles_per_e) {

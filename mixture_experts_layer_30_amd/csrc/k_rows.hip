@@ -105,7 +105,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order. The k rows go 8 at
 // a time through one pass over the columns, so their loads overlap.
 // With dOq (MXFP8 backward) each dO row is also quantized along H from its
-// bf16 values: a 32-column block is the 4 chunks of 4 adjacent lanes.
+// bf16 values: a 32-column block is the 4 chunks of 4 adjacent lanes
+// (QUANT = true; the bf16 backward launches the variant without it).
+template <bool QUANT>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
         }
         const uint4 packed = pack8(d);
         reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = packed;
-        if (dOq) {
+        if constexpr (QUANT) {
           float b[8];
           unpack8(packed, b);                    // the stored bf16 values
           float amax = 0.f;
@@ -338,8 +340,12 @@ hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, cons
                                       int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
                                       uint8_t* dOs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(reverse_combine_kernel, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf, w,
-                     dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
+  if (dOq)
+    hipLaunchKernelGGL(reverse_combine_kernel<true>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf,
+                       w, dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
+  else
+    hipLaunchKernelGGL(reverse_combine_kernel<false>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy,
+                       obuf, w, dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
   return hipGetLastError();
 }
 
