@@ -254,32 +254,56 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
   Acc<G::FM, G::FN> acc;
   mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
   // dA, dB and h per element from an fp32 half-tile of dh in LDS and the
-  // saved a, b (16-byte loads and stores along the row).
+  // saved a, b (16-byte loads and stores along the row). A thread keeps one
+  // 8-column group c and takes rows r0, r0 + 8, ..., r0 + 120 of each half,
+  // in two groups of 8 rows whose a, b loads are all issued before the
+  // group's stores (the first group's before the staging): a wait for a load
+  // issued after stores also waits for those stores, so loads interleaved
+  // with the stores would serialise every row.
   using HS = HalfF32<G>;
+  const int c = (threadIdx.x % (G::BN / 8)) * 8, r0 = threadIdx.x / (G::BN / 8);
+  const bool colok = n0 + c < I;
+  const bf16_t* abt = a.ab + (int64_t)t.p0 * 2 * I + n0 + c;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (half) __syncthreads();
-    HS::put(lds_raw, acc, half);
-    __syncthreads();
     const int rows = min(128, nrows - 128 * half);
-    for (int idx = threadIdx.x; idx < 128 * (G::BN / 8); idx += kThreads) {
-      const int r = idx / (G::BN / 8), c = (idx % (G::BN / 8)) * 8;
-      if (r >= rows || n0 + c >= I) continue;
-      const int64_t p = t.p0 + 128 * half + r;
-      float dh[8], av[8], bv[8], da[8], db[8], h[8];
-      HS::get8(lds_raw, r, c, dh);
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + n0 + c), av);
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + I + n0 + c), bv);
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      uint4 va[8], vb[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float sg = sigmoidf_(av[u]);
-        da[u] = dh[u] * bv[u] * sg * (1.0f + av[u] * (1.0f - sg));
-        db[u] = dh[u] * av[u] * sg;
-        h[u] = av[u] * sg * bv[u];
+        const int r = r0 + 64 * grp + 8 * u;
+        if (colok && r < rows) {
+          const bf16_t* q = abt + (int64_t)(128 * half + r) * 2 * I;
+          va[u] = *reinterpret_cast<const uint4*>(q);
+          vb[u] = *reinterpret_cast<const uint4*>(q + I);
+        }
       }
-      *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c) = pack_bf16x8(da);
-      *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c) = pack_bf16x8(db);
-      *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c) = pack_bf16x8(h);
+      if (grp == 0) {
+        if (half) __syncthreads();
+        HS::put(lds_raw, acc, half);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + 64 * grp + 8 * u;
+        if (!colok || r >= rows) continue;
+        const int64_t p = t.p0 + 128 * half + r;
+        float dh[8], av[8], bv[8], da[8], db[8], h[8];
+        HS::get8(lds_raw, r, c, dh);
+        unpack_bf16x8(va[u], av);
+        unpack_bf16x8(vb[u], bv);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const float sg = sigmoidf_(av[v]);
+          da[v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
+          db[v] = dh[v] * av[v] * sg;
+          h[v] = av[v] * sg * bv[v];
+        }
+        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c) = pack_bf16x8(da);
+        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c) = pack_bf16x8(db);
+        *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c) = pack_bf16x8(h);
+      }
     }
   }
 }
@@ -395,53 +419,77 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
   // per row and 32-column block: dA, dB, h from dh and the saved a, b;
   // the 32 dA (and dB) values of the block share one scale along I
   using HS = HalfF32<G>;
+  // a thread keeps one 32-column block and takes rows r0, r0 + 32, r0 + 64,
+  // r0 + 96 of each half, in two groups of 2 rows whose a, b loads are issued
+  // before the group's stores (see bwd_dh_kernel)
+  const int blk = threadIdx.x % (G::BN / 32), r0 = threadIdx.x / (G::BN / 32), c0 = blk * 32;
+  const bool colok = n0 + c0 < I;
+  const bf16_t* abt = a.ab + (int64_t)t.p0 * 2 * I + n0 + c0;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (half) __syncthreads();
-    HS::put(lds_raw, acc, half);
-    __syncthreads();
     const int rows = min(128, nrows - 128 * half);
-    for (int idx = threadIdx.x; idx < 128 * (G::BN / 32); idx += kThreads) {
-      const int r = idx / (G::BN / 32), blk = idx % (G::BN / 32);
-      const int c0 = blk * 32;
-      if (r >= rows || n0 + c0 >= I) continue;
-      const int64_t p = t.p0 + 128 * half + r;
-      float da[32], db[32];
-      float amaxa = 0.f, amaxb = 0.f;
 #pragma unroll
-      for (int u = 0; u < 32; u += 8) {
-        float dh[8], av[8], bv[8], h[8];
-        HS::get8(lds_raw, r, c0 + u, dh);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + n0 + c0 + u), av);
-        unpack_bf16x8(*reinterpret_cast<const uint4*>(a.ab + p * 2 * I + I + n0 + c0 + u), bv);
+    for (int grp = 0; grp < 2; ++grp) {
+      uint4 va[2][4], vb[2][4];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const float sg = sigmoidf_(av[v]);
-          da[u + v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
-          db[u + v] = dh[v] * av[v] * sg;
-          h[v] = av[v] * sg * bv[v];
-          amaxa = fmaxf(amaxa, fabsf(da[u + v]));
-          amaxb = fmaxf(amaxb, fabsf(db[u + v]));
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const int r = r0 + 32 * (2 * grp + i2);
+        if (colok && r < rows) {
+          const bf16_t* q = abt + (int64_t)(128 * half + r) * 2 * I;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            va[i2][u] = *reinterpret_cast<const uint4*>(q + 8 * u);
+            vb[i2][u] = *reinterpret_cast<const uint4*>(q + I + 8 * u);
+          }
         }
-        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c0 + u) = pack_bf16x8(da + u);
-        *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c0 + u) = pack_bf16x8(db + u);
-        *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
+      }
+      if (grp == 0) {
+        if (half) __syncthreads();
+        HS::put(lds_raw, acc, half);
+        __syncthreads();
       }
 #pragma unroll
-      for (int side = 0; side < 2; ++side) {
-        const float* v = side ? db : da;
-        const int sc = mx_scale_byte(side ? amaxb : amaxa);
-        const float inv = mx_inv_scale(sc);
-        uint32_t w[8];
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const int r = r0 + 32 * (2 * grp + i2);
+        if (!colok || r >= rows) continue;
+        const int64_t p = t.p0 + 128 * half + r;
+        float da[32], db[32];
+        float amaxa = 0.f, amaxb = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          w[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
-                 (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
-        const int64_t col = (side ? I : 0) + n0 + c0;
-        uint4* d = reinterpret_cast<uint4*>(a.dabq + p * 2 * I + col);
-        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        a.dabs[p * s2I + col / 32] = (uint8_t)sc;
+        for (int u = 0; u < 32; u += 8) {
+          float dh[8], av[8], bv[8], h[8];
+          HS::get8(lds_raw, r, c0 + u, dh);
+          unpack_bf16x8(va[i2][u / 8], av);
+          unpack_bf16x8(vb[i2][u / 8], bv);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            const float sg = sigmoidf_(av[v]);
+            da[u + v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
+            db[u + v] = dh[v] * av[v] * sg;
+            h[v] = av[v] * sg * bv[v];
+            amaxa = fmaxf(amaxa, fabsf(da[u + v]));
+            amaxb = fmaxf(amaxb, fabsf(db[u + v]));
+          }
+          *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c0 + u) = pack_bf16x8(da + u);
+          *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c0 + u) = pack_bf16x8(db + u);
+          *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
+        }
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+          const float* v = side ? db : da;
+          const int sc = mx_scale_byte(side ? amaxb : amaxa);
+          const float inv = mx_inv_scale(sc);
+          uint32_t w[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            w[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
+                   (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
+          const int64_t col = (side ? I : 0) + n0 + c0;
+          uint4* d = reinterpret_cast<uint4*>(a.dabq + p * 2 * I + col);
+          d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          a.dabs[p * s2I + col / 32] = (uint8_t)sc;
+        }
       }
     }
   }

@@ -31,17 +31,19 @@ constexpr int kMaxExperts = 512;
 // ------------------------------------------------------------------ bf16 helpers
 MOK_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-MOK_DEV bf16_t f32_to_bf16(float f) {  // round to nearest even (finite inputs)
-  uint32_t b = __float_as_uint(f);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (bf16_t)(b >> 16);
-}
+// fp32 -> bf16, round to nearest even: one v_cvt_pk_bf16_f32 per pair on
+// gfx950 (the same result as rounding the bit pattern for finite inputs).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 MOK_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-MOK_DEV float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+MOK_DEV bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu); }
+
+// logistic sigmoid with the hardware reciprocal (about 1 ulp)
+MOK_DEV float sigmoidf_(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // ------------------------------------------------------------------ MXFP8 (OCP MX v1.0)
 // E8M0 scale byte of a 32-element block from its largest magnitude:
