@@ -223,64 +223,56 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
 // write them as one 128-byte segment of the transposed row.
 __global__ __launch_bounds__(256) void token_quantize_kernel(
     const bf16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm, int topk,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ koffs, int E, int64_t N,
-    uint8_t* __restrict__ dst, uint8_t* __restrict__ dsts) {
-  __shared__ float tile[128][65];
-  __shared__ int s_koff[kMaxExperts + 1];
-  __shared__ int s_e;
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ koffs,
+    const int32_t* __restrict__ blk_e, int64_t N, uint8_t* __restrict__ dst, uint8_t* __restrict__ dsts) {
+  // the 128 x 64 block as bf16, row pitch 128 B; the 8-column chunk ch of row
+  // r sits at chunk ch ^ (2 * (r / 32)), so that the four 32-row blocks read
+  // by the four threads of one column fall in different banks
+  __shared__ __attribute__((aligned(16))) bf16_t tile[128 * 64];
   // blockIdx.x: 64-column slice (adjacent workgroups read adjacent slices of
   // the same rows); blockIdx.y: 128 positions of the padded token axis
-  const int t0 = (int)blockIdx.y * 128;         // position on the padded token axis
-  for (int i = threadIdx.x; i <= E; i += 256) s_koff[i] = koffs[i];
-  __syncthreads();
-  if (threadIdx.x == 0) {                        // the expert e with koff[e] <= t0 < koff[e+1]
-    int lo = 0, hi = E;                          // invariant: koff[lo] <= t0, answer < hi
-    if (t0 >= s_koff[E]) {
-      lo = -1;
-    } else {
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_koff[mid] <= t0) lo = mid; else hi = mid;
-      }
-    }
-    s_e = lo;
-  }
-  __syncthreads();
-  const int e = s_e;
-  if (e < 0) return;                             // past every expert's positions
-  const int koff = s_koff[e];
-  const int c = offsets[e + 1] - offsets[e], kp = s_koff[e + 1] - koff;
-  const int r0 = t0 - koff;                      // first row of the block within the expert
+  const int e = blk_e[blockIdx.y];               // expert owning these positions, -1 past the end
+  if (e < 0) return;
+  const int koff = koffs[e], kp = koffs[e + 1] - koff;
+  const int o = offsets[e], c = offsets[e + 1] - o;
+  const int r0 = (int)blockIdx.y * 128 - koff;   // first row of the block within the expert
   const int nrow = min(128, c - r0);             // rows of this block that exist (may be <= 0)
   const int64_t n0 = (int64_t)blockIdx.x * 64;
-  for (int idx = threadIdx.x; idx < 128 * 8; idx += 256) {
-    const int r = idx >> 3, ch = idx & 7;
-    const int64_t col = n0 + ch * 8;
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < nrow && col < N) {
-      const int64_t p = offsets[e] + r0 + r;
-      const int64_t row = perm ? (int64_t)(perm[p] / topk) : p;
-      unpack8(*reinterpret_cast<const uint4*>(src + row * ld + col), v);
-    }
+  uint4 v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) tile[r][ch * 8 + u] = v[u];
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + 256 * i, r = idx >> 3;
+    const int64_t col = n0 + (idx & 7) * 8;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nrow && col < N) {
+      const int64_t p = o + r0 + r;
+      const int64_t row = perm ? (int64_t)(perm[p] / topk) : p;
+      v[i] = *reinterpret_cast<const uint4*>(src + row * ld + col);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = threadIdx.x + 256 * i, r = idx >> 3, ch = idx & 7;
+    *reinterpret_cast<uint4*>(tile + r * 64 + ((ch ^ (2 * (r >> 5))) << 3)) = v[i];
   }
   __syncthreads();
   const int cl = threadIdx.x >> 2, qb = threadIdx.x & 3;   // column, 32-row block
   const int64_t n = n0 + cl;
   if (n >= N) return;
+  float x[32];
   float amax = 0.f;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(tile[32 * qb + r][cl]));
+  for (int r = 0; r < 32; ++r) {
+    x[r] = bf16_to_f32(tile[(32 * qb + r) * 64 + (cl ^ (16 * qb))]);
+    amax = fmaxf(amax, fabsf(x[r]));
+  }
   const int sc = mx_scale_byte(amax);
   const float inv = mx_inv_scale(sc);
   uint32_t wds[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = 32 * qb + 4 * u;
-    wds[u] = e4m3_encode(tile[r][cl] * inv) | (e4m3_encode(tile[r + 1][cl] * inv) << 8) |
-             (e4m3_encode(tile[r + 2][cl] * inv) << 16) | (e4m3_encode(tile[r + 3][cl] * inv) << 24);
-  }
+  for (int u = 0; u < 8; ++u)
+    wds[u] = e4m3_encode(x[4 * u] * inv) | (e4m3_encode(x[4 * u + 1] * inv) << 8) |
+             (e4m3_encode(x[4 * u + 2] * inv) << 16) | (e4m3_encode(x[4 * u + 3] * inv) << 24);
   uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + r0 + 32 * qb);
   d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
   d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
@@ -289,8 +281,11 @@ __global__ __launch_bounds__(256) void token_quantize_kernel(
 
 // koff[e] = sum over e' < e of tok_pad(rows of e'), e = 0..E, by a Hillis-Steele
 // scan of up to kMaxExperts values in one workgroup (integer, exact).
+// It also fills blk_e[b] (b < nblk), the expert whose padded positions hold
+// [128b, 128b + 128), or -1 past the last expert, by a binary search of koff.
 __global__ __launch_bounds__(256) void token_offsets_kernel(const int32_t* __restrict__ offsets, int E,
-                                                            int32_t* __restrict__ koff) {
+                                                            int32_t* __restrict__ koff, int nblk,
+                                                            int32_t* __restrict__ blk_e) {
   __shared__ int v[2][kMaxExperts + 1];
   for (int i = threadIdx.x; i <= E; i += 256) v[0][i] = i == 0 ? 0 : tok_pad(offsets[i] - offsets[i - 1]);
   __syncthreads();
@@ -301,6 +296,19 @@ __global__ __launch_bounds__(256) void token_offsets_kernel(const int32_t* __res
     cur ^= 1;
   }
   for (int i = threadIdx.x; i <= E; i += 256) koff[i] = v[cur][i];
+  for (int b = threadIdx.x; b < nblk; b += 256) {
+    const int t0 = 128 * b;
+    int lo = -1;
+    if (t0 < v[cur][E]) {                        // largest e with koff[e] <= t0
+      int hi = E;
+      lo = 0;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (v[cur][mid] <= t0) lo = mid; else hi = mid;
+      }
+    }
+    blk_e[b] = lo;
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
@@ -371,17 +379,18 @@ hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K,
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
                                      const int32_t* offsets, const int32_t* koff, int E, int64_t R,
                                      int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st) {
-  const int64_t positions = R + 128 * (int64_t)E;          // bound of the padded token axis
   if (R <= 0 || N <= 0) return hipSuccess;
   if (E > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(token_quantize_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)((positions + 127) / 128)),
-                     dim3(256), 0, st, src, ld, perm, topk, offsets, koff, E, N, dst, dst_scales);
+  const int nblk = mok_token_blocks(R, E);
+  hipLaunchKernelGGL(token_quantize_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)nblk), dim3(256), 0, st,
+                     src, ld, perm, topk, offsets, koff, koff + E + 1, N, dst, dst_scales);
   return hipGetLastError();
 }
 
-hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int32_t* koff, hipStream_t st) {
+hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int64_t R, int32_t* koff, hipStream_t st) {
   if (E > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(token_offsets_kernel, dim3(1), dim3(256), 0, st, offsets, E, koff);
+  hipLaunchKernelGGL(token_offsets_kernel, dim3(1), dim3(256), 0, st, offsets, E, koff, mok_token_blocks(R, E),
+                     koff + E + 1);
   return hipGetLastError();
 }
 

@@ -169,7 +169,7 @@ BwdWs bwd_ws(const Resolved& r) {
     w.dabTs = o; o = align_up(o + 2 * I * (KT / 32));
     w.xT = o;    o = align_up(o + H * KT);
     w.xTs = o;   o = align_up(o + H * (KT / 32));
-    w.koff = o;  o = align_up(o + 4 * ((size_t)r.E + 1));
+    w.koff = o;  o = align_up(o + 4 * ((size_t)r.E + 1 + (size_t)mok_token_blocks(r.R, r.E)));
   }
   w.total = o;
   return w;
@@ -466,7 +466,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     a.dabT = ws + W.dabT; a.dabTs = ws + W.dabTs;
     a.xT = ws + W.xT;     a.xTs = ws + W.xTs;
     a.koff = reinterpret_cast<int32_t*>(ws + W.koff);
-    MOK_RUN("token_offsets", mok_launch_token_offsets(sp.offsets, r.E, a.koff, st));
+    MOK_RUN("token_offsets", mok_launch_token_offsets(sp.offsets, r.E, r.R, a.koff, st));
     if (r.T > 0) {
       // also quantizes the dO rows along H for dh
       MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,

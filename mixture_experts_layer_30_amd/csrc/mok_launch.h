@@ -136,7 +136,8 @@ struct mok_bwd_args {
   uint8_t* dabTs;
   uint8_t* xT;           // token-blocked x rows (N = H)
   uint8_t* xTs;
-  int32_t* koff;         // [E+1] start of each expert on the padded token axis
+  int32_t* koff;         // [E+1] start of each expert on the padded token axis, then the
+                         // expert of each 128-position block (mok_launch_token_offsets)
 };
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st);     // dh, SwiGLU bwd
@@ -154,5 +155,9 @@ hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st);
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
                                      const int32_t* offsets, const int32_t* koff, int E, int64_t R,
                                      int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st);
-// koff[0..E] of the padded token axis from the expert offsets (one workgroup)
-hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int32_t* koff, hipStream_t st);
+// 128-position blocks of the padded token axis (an upper bound: R + 128 E positions)
+inline int mok_token_blocks(int64_t R, int E) { return (int)((R + 128 * (int64_t)E + 127) / 128); }
+// koff[0..E] of the padded token axis from the expert offsets, followed in the
+// same buffer by the expert of each 128-position block (koff + E + 1, one int
+// per block, -1 past the end); one workgroup
+hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int64_t R, int32_t* koff, hipStream_t st);
