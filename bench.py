@@ -74,8 +74,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=1, help="reference workload id (0-4)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip)")

@@ -222,8 +222,10 @@ mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K,
  * Per-kernel timing for profiling ([MoK clip] How-to item 1: profile first to
  * see where the layer's time goes). While tracing is on, every kernel the
  * library launches is bracketed by two HIP events recorded on its launch
- * stream (host-side calls only; nothing waits). mok_trace_collect waits for
- * the recorded events (a host synchronisation, so never call it inside a
+ * stream (host-side calls only; nothing waits; timing-only events created
+ * with hipEventDisableSystemFence, so they add no cache writeback between
+ * kernels). mok_trace_collect synchronises the device and reads the recorded
+ * events (a host synchronisation, so never call it inside a
  * timed or captured region), returns per-kernel totals in launch order of
  * first appearance and clears the record. The library creates and reuses
  * the events itself. Not thread-safe across concurrent callers. */

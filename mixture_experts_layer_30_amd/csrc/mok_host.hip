@@ -217,22 +217,30 @@ mok_status check_device(int* cus = nullptr) {
 mok_status launched(hipError_t e) { return e == hipSuccess ? MOK_OK : MOK_ERR_DEVICE; }
 
 // Launch tracing: when on, each launch is bracketed by two events recorded on
-// its stream. Events come from a pool that is reused across collections.
+// its stream; within one API call, consecutive launches on one stream share
+// the event between them (the end of one is the start of the next), since
+// nothing else is enqueued there in between. Events come from a pool that is
+// reused across collections.
 struct Tracer {
   std::mutex mu;
   bool on = false;
   struct Rec {
     const char* name;
     hipEvent_t a, b;
+    bool shared_a;         // a is the previous record's b
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
+  hipEvent_t chain = nullptr;   // end event of the last launch of the current API call
+  hipStream_t chain_st = nullptr;
   hipEvent_t get() {
     hipEvent_t e = nullptr;
     if (!pool.empty()) {
       e = pool.back();
       pool.pop_back();
-    } else if (hipEventCreate(&e) != hipSuccess) {
+    } else if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
+      // timing-only events: no system-scope cache writeback and invalidation
+      // between the traced kernels (mok_trace_collect synchronises the device)
       e = nullptr;
     }
     return e;
@@ -240,23 +248,48 @@ struct Tracer {
 };
 Tracer g_tr;
 
+// One per API call that launches work: no event chain crosses its boundary
+// (the caller may enqueue its own work between calls).
+struct TraceCall {
+  TraceCall() { reset(); }
+  ~TraceCall() { reset(); }
+  static void reset() {
+    if (!g_tr.on && !g_tr.chain) return;
+    std::lock_guard<std::mutex> g(g_tr.mu);
+    g_tr.chain = nullptr;
+    g_tr.chain_st = nullptr;
+  }
+};
+
 struct TraceScope {
   const char* name;
   hipStream_t st;
   hipEvent_t a = nullptr;
+  bool shared = false;
   TraceScope(const char* n, hipStream_t s) : name(n), st(s) {
     if (!g_tr.on) return;
     std::lock_guard<std::mutex> g(g_tr.mu);
-    a = g_tr.get();
-    if (a) (void)hipEventRecord(a, st);
+    if (g_tr.chain && g_tr.chain_st == st) {
+      a = g_tr.chain;
+      shared = true;
+    } else {
+      a = g_tr.get();
+      if (a) (void)hipEventRecord(a, st);
+    }
   }
   ~TraceScope() {
     if (!a) return;
     std::lock_guard<std::mutex> g(g_tr.mu);
     hipEvent_t b = g_tr.get();
-    if (!b) return;
+    if (!b) {
+      if (!shared) g_tr.pool.push_back(a);
+      g_tr.chain = nullptr;
+      return;
+    }
     (void)hipEventRecord(b, st);
-    g_tr.recs.push_back({name, a, b});
+    g_tr.recs.push_back({name, a, b, shared});
+    g_tr.chain = b;
+    g_tr.chain_st = st;
   }
 };
 
@@ -322,6 +355,7 @@ mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config*
 mok_status mok_build_schedule(const mok_problem* problem, const mok_config* config,
                               const int32_t* topk_ids, void* schedule, size_t schedule_bytes,
                               void* stream) {
+  TraceCall tc;
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
@@ -341,6 +375,7 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
 mok_status mok_forward(const mok_problem* problem, const mok_config* config, const void* schedule,
                        const void* x, const float* topk_w, const mok_weights* weights, void* y,
                        void* fwd_ctx, void* workspace, size_t workspace_bytes, void* stream) {
+  TraceCall tc;
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
@@ -418,6 +453,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
                         const float* topk_w, const mok_weights* weights, const void* dy, void* dx,
                         void* dw_gate, void* dw_up, void* dw_down, float* d_topk_w,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  TraceCall tc;
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
@@ -509,6 +545,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
 
 mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K, uint8_t* q,
                               uint8_t* scales, void* stream) {
+  TraceCall tc;
   if (rows < 0 || K <= 0 || K % 32 != 0) return MOK_ERR_INVALID_ARG;
   if (rows > 0 && (!src || !q || !scales)) return MOK_ERR_INVALID_ARG;
   mok_status s = check_device();
@@ -531,6 +568,7 @@ mok_status mok_trace_collect(mok_trace_stat* out, int32_t capacity, int32_t* n_o
   std::vector<std::string> names;
   std::vector<mok_trace_stat> stats;
   mok_status st = MOK_OK;
+  if (!g_tr.recs.empty() && hipDeviceSynchronize() != hipSuccess) st = MOK_ERR_DEVICE;
   for (const auto& rec : g_tr.recs) {
     float ms = 0.f;
     if (hipEventSynchronize(rec.b) != hipSuccess || hipEventElapsedTime(&ms, rec.a, rec.b) != hipSuccess)
@@ -547,10 +585,12 @@ mok_status mok_trace_collect(mok_trace_stat* out, int32_t capacity, int32_t* n_o
     stats[k].launches += 1;
     stats[k].total_ms += ms;
     stats[k].max_ms = std::max(stats[k].max_ms, (double)ms);
-    g_tr.pool.push_back(rec.a);
+    if (!rec.shared_a) g_tr.pool.push_back(rec.a);
     g_tr.pool.push_back(rec.b);
   }
   g_tr.recs.clear();
+  g_tr.chain = nullptr;
+  g_tr.chain_st = nullptr;
   *n_out = (int32_t)stats.size();
   for (int32_t i = 0; i < capacity && i < (int32_t)stats.size(); ++i) out[i] = stats[i];
   return st;
