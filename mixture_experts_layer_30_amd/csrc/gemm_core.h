@@ -607,7 +607,7 @@ MOK_DEV void store_tile_bf16(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nro
       if (r >= rows || c >= ncols) continue;
       float v[8];
       HS::get8(lds, r, c, v);
-      *reinterpret_cast<uint4*>(dst(128 * half + r) + c) = pack_bf16x8(v);
+      store_nt(dst(128 * half + r) + c, pack_bf16x8(v));
     }
   }
 }
@@ -651,7 +651,7 @@ MOK_DEV void store_tile_bf16_t(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int n
     const int r = idx / CPR, c = idx % CPR;
     if (r >= nrows || 8 * c >= ncols) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + ((c ^ (r & 15)) << 4));
-    *reinterpret_cast<uint4*>(dst(r) + 8 * c) = v;
+    store_nt(dst(r) + 8 * c, v);
   }
 }
 

@@ -81,6 +81,16 @@ MOK_DEV uint32_t e4m3_encode(float q) {
 // 2^(127 - s) as a float multiplier (exact; s in 0..254).
 MOK_DEV float mx_inv_scale(int s) { return ldexpf(1.0f, 127 - s); }
 
+// ------------------------------------------------------------------ stores
+// Global stores with the nontemporal hint (global_store ... nt): GEMM outputs
+// are not read again while they would still sit in L2, and with the hint they
+// do not evict the operand lines other workgroups are still reading (measured
+// on a grouped GEMM with K = 512: main loop 20.6 -> 17.7 us per tile).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+MOK_DEV void store_nt(void* p, const uint4& v) {
+  __builtin_nontemporal_store((u32x4_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // ------------------------------------------------------------------ misc
 MOK_DEV int lane_id() { return (int)(threadIdx.x & 63); }
 
