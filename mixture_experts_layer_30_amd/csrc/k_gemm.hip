@@ -130,11 +130,6 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
             h[u + v] = av[v] * sigmoidf_(av[v]) * bv[v];
             amax = fmaxf(amax, fabsf(h[u + v]));
           }
-          if (abp) {                             // saved for the backward
-            const int64_t rr = 128 * half + r;
-            *reinterpret_cast<uint4*>(abp + rr * 2 * I + blk * 32 + u) = pack_bf16x8(av);
-            *reinterpret_cast<uint4*>(abp + rr * 2 * I + I + blk * 32 + u) = pack_bf16x8(bv);
-          }
         }
         const int sc = mx_scale_byte(amax);
         const float inv = mx_inv_scale(sc);
@@ -148,6 +143,22 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
         hsc[rr * (I / 32) + blk] = (uint8_t)sc;
+      }
+      // a, b saved for the backward: one 8-column chunk per thread, 16 threads
+      // per row, so each store instruction writes whole row segments and can
+      // carry the nontemporal hint
+      if (abp) {
+        for (int idx = threadIdx.x; idx < 128 * (HW / 8); idx += kThreads) {
+          const int r = idx / (HW / 8), c = (idx % (HW / 8)) * 8;
+          if (r >= rows || n0 + c >= I) continue;
+          float av[8], bv[8];
+          const int tc = (c >> 5) * 64 + (c & 31);
+          HS::get8(st, r, tc, av);
+          HS::get8(st, r, tc + 32, bv);
+          const int64_t rr = 128 * half + r;
+          store_nt(abp + rr * 2 * I + c, pack_bf16x8(av));
+          store_nt(abp + rr * 2 * I + I + c, pack_bf16x8(bv));
+        }
       }
     }
   }
