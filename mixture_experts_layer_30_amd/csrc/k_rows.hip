@@ -216,33 +216,37 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
 // expert's rows): expert e's rows [o_e, o_e + c_e) of the source, transposed
 // to [N][Kp_e] and quantized along the rows in blocks of 32 counted from o_e
 // (positions past c_e are zero, which decode to zero under the block's
-// scale). One workgroup per (64 columns x 128 positions of the padded token
-// axis, which never straddle two experts since every Kp is a multiple of
-// 128): it stages the 128 x 64 block in LDS (128-byte row segments in),
-// then 4 adjacent threads per column quantize its four 32-row blocks and
+// scale). One workgroup per (COLS columns x 128 positions of the padded
+// token axis, which never straddle two experts since every Kp is a multiple
+// of 128): it stages the 128 x COLS block in LDS (2*COLS-byte row segments
+// in), then 4 adjacent threads per column quantize its four 32-row blocks and
 // write them as one 128-byte segment of the transposed row.
+template <int COLS>
 __global__ __launch_bounds__(256) void token_quantize_kernel(
     const bf16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm, int topk,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ koffs,
     const int32_t* __restrict__ blk_e, int64_t N, uint8_t* __restrict__ dst, uint8_t* __restrict__ dsts) {
-  // the 128 x 64 block as bf16, row pitch 128 B; the 8-column chunk ch of row
-  // r sits at chunk ch ^ (2 * (r / 32)), so that the four 32-row blocks read
-  // by the four threads of one column fall in different banks
-  __shared__ __attribute__((aligned(16))) bf16_t tile[128 * 64];
-  // blockIdx.x: 64-column slice (adjacent workgroups read adjacent slices of
-  // the same rows); blockIdx.y: 128 positions of the padded token axis
+  static_assert(COLS == 64 || COLS == 128, "64 or 128 columns per workgroup");
+  constexpr int CH = COLS / 8;                   // 16-byte chunks per row
+  // the 128 x COLS block as bf16, row pitch 2*COLS bytes; the 8-column chunk
+  // ch of row r sits at chunk ch ^ (2 * (r / 32)), so that the four 32-row
+  // blocks read by the four threads of one column fall in different banks
+  __shared__ __attribute__((aligned(16))) bf16_t tile[128 * COLS];
+  // blockIdx.x: COLS-column slice (adjacent workgroups read adjacent slices
+  // of the same rows); blockIdx.y: 128 positions of the padded token axis
   const int e = blk_e[blockIdx.y];               // expert owning these positions, -1 past the end
   if (e < 0) return;
   const int koff = koffs[e], kp = koffs[e + 1] - koff;
   const int o = offsets[e], c = offsets[e + 1] - o;
   const int r0 = (int)blockIdx.y * 128 - koff;   // first row of the block within the expert
   const int nrow = min(128, c - r0);             // rows of this block that exist (may be <= 0)
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
-  uint4 v[4];
+  const int64_t n0 = (int64_t)blockIdx.x * COLS;
+  constexpr int NL = 128 * CH / 256;             // 16-byte loads per thread
+  uint4 v[NL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = threadIdx.x + 256 * i, r = idx >> 3;
-    const int64_t col = n0 + (idx & 7) * 8;
+  for (int i = 0; i < NL; ++i) {
+    const int idx = threadIdx.x + 256 * i, r = idx / CH;
+    const int64_t col = n0 + (idx % CH) * 8;
     v[i] = make_uint4(0u, 0u, 0u, 0u);
     if (r < nrow && col < N) {
       const int64_t p = o + r0 + r;
@@ -251,32 +255,35 @@ __global__ __launch_bounds__(256) void token_quantize_kernel(
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = threadIdx.x + 256 * i, r = idx >> 3, ch = idx & 7;
-    *reinterpret_cast<uint4*>(tile + r * 64 + ((ch ^ (2 * (r >> 5))) << 3)) = v[i];
+  for (int i = 0; i < NL; ++i) {
+    const int idx = threadIdx.x + 256 * i, r = idx / CH, ch = idx % CH;
+    *reinterpret_cast<uint4*>(tile + r * COLS + ((ch ^ (2 * (r >> 5))) << 3)) = v[i];
   }
   __syncthreads();
-  const int cl = threadIdx.x >> 2, qb = threadIdx.x & 3;   // column, 32-row block
-  const int64_t n = n0 + cl;
-  if (n >= N) return;
-  float x[32];
-  float amax = 0.f;
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    x[r] = bf16_to_f32(tile[(32 * qb + r) * 64 + (cl ^ (16 * qb))]);
-    amax = fmaxf(amax, fabsf(x[r]));
+  for (int pass = 0; pass < COLS / 64; ++pass) {
+    const int cl = (threadIdx.x >> 2) + 64 * pass, qb = threadIdx.x & 3;   // column, 32-row block
+    const int64_t n = n0 + cl;
+    if (n >= N) continue;
+    float x[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      x[r] = bf16_to_f32(tile[(32 * qb + r) * COLS + (cl ^ (16 * qb))]);
+      amax = fmaxf(amax, fabsf(x[r]));
+    }
+    const int sc = mx_scale_byte(amax);
+    const float inv = mx_inv_scale(sc);
+    uint32_t wds[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      wds[u] = e4m3_encode(x[4 * u] * inv) | (e4m3_encode(x[4 * u + 1] * inv) << 8) |
+               (e4m3_encode(x[4 * u + 2] * inv) << 16) | (e4m3_encode(x[4 * u + 3] * inv) << 24);
+    uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + r0 + 32 * qb);
+    d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+    dsts[N * (koff / 32) + n * (kp / 32) + r0 / 32 + qb] = (uint8_t)sc;
   }
-  const int sc = mx_scale_byte(amax);
-  const float inv = mx_inv_scale(sc);
-  uint32_t wds[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-    wds[u] = e4m3_encode(x[4 * u] * inv) | (e4m3_encode(x[4 * u + 1] * inv) << 8) |
-             (e4m3_encode(x[4 * u + 2] * inv) << 16) | (e4m3_encode(x[4 * u + 3] * inv) << 24);
-  uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + r0 + 32 * qb);
-  d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-  d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
-  dsts[N * (koff / 32) + n * (kp / 32) + r0 / 32 + qb] = (uint8_t)sc;
 }
 
 // koff[e] = sum over e' < e of tok_pad(rows of e'), e = 0..E, by a Hillis-Steele
@@ -382,8 +389,9 @@ hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_
   if (R <= 0 || N <= 0) return hipSuccess;
   if (E > kMaxExperts) return hipErrorInvalidValue;
   const int nblk = mok_token_blocks(R, E);
-  hipLaunchKernelGGL(token_quantize_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)nblk), dim3(256), 0, st,
-                     src, ld, perm, topk, offsets, koff, koff + E + 1, N, dst, dst_scales);
+  constexpr int kCols = 64;                       // measured: 128 columns per workgroup is 5-15% slower
+  hipLaunchKernelGGL(token_quantize_kernel<kCols>, dim3((unsigned)((N + kCols - 1) / kCols), (unsigned)nblk),
+                     dim3(256), 0, st, src, ld, perm, topk, offsets, koff, koff + E + 1, N, dst, dst_scales);
   return hipGetLastError();
 }
 
