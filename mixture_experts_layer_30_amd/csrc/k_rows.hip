@@ -65,13 +65,19 @@ __global__ __launch_bounds__(256) void gather_kernel(
 // One thread per (token, 8 columns). y = sum over j ascending of w*o in fp32.
 // The k rows are read 8 at a time before any is used, so their loads
 // overlap (rows of invalid ids and j >= k read a valid row and are dropped).
+// With WAVE_TOKEN (H/8 a multiple of 64) the 64 lanes of a wavefront share
+// one token, which is then read from lane 0 so that its dest and w entries
+// are loaded once per wavefront through the scalar unit.
+template <bool WAVE_TOKEN>
 __global__ __launch_bounds__(256) void combine_kernel(
     const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
     int64_t H, bf16_t* __restrict__ y) {
   const int64_t nch = H >> 3;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = idx / nch, c = idx - t * nch;
+  int64_t t = idx / nch;
+  if constexpr (WAVE_TOKEN) t = __builtin_amdgcn_readfirstlane((int)t);
+  const int64_t c = idx - t * nch;
   if (t >= T) return;
   const int nvalid = *offsets_E;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -113,7 +119,9 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
     int64_t H, float* __restrict__ dw, bf16_t* __restrict__ dO, uint8_t* __restrict__ dOq,
     uint8_t* __restrict__ dOs) {
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // the token of this wavefront, read from lane 0 so that its dest and w
+  // entries are loaded once per wavefront through the scalar unit
+  const int64_t t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int lane = lane_id();
   if (t >= T) return;
   const int nvalid = *offsets_E;
@@ -345,8 +353,12 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
                               bf16_t* y, hipStream_t st) {
   const int64_t n = T * (H / 8);
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, obuf, w, dest,
-                     offsets_E, T, topk, H, y);
+  if ((H / 8) % 64 == 0)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid_for(n, 256)), dim3(256), 0, st, obuf, w, dest,
+                       offsets_E, T, topk, H, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, st, obuf, w, dest,
+                       offsets_E, T, topk, H, y);
   return hipGetLastError();
 }
 
@@ -369,8 +381,12 @@ hipError_t mok_launch_reverse_dispatch(const bf16_t* dxrows, const int32_t* dest
                                        bf16_t* dx, hipStream_t st) {
   const int64_t n = T * (H / 8);
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, dxrows,
-                     (const float*)nullptr, dest, offsets_E, T, topk, H, dx);
+  if ((H / 8) % 64 == 0)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid_for(n, 256)), dim3(256), 0, st, dxrows,
+                       (const float*)nullptr, dest, offsets_E, T, topk, H, dx);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid_for(n, 256)), dim3(256), 0, st, dxrows,
+                       (const float*)nullptr, dest, offsets_E, T, topk, H, dx);
   return hipGetLastError();
 }
 
