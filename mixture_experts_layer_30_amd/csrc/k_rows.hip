@@ -30,13 +30,14 @@ MOK_DEV uint4 pack8(const float f[8]) {
 }
 
 // ------------------------------------------------------------------ gather
-// One wavefront per destination row.
+// One wavefront per destination row (its index read from lane 0, so the
+// perm entry loads once per wavefront through the scalar unit).
 __global__ __launch_bounds__(256) void gather_kernel(
     const uint8_t* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets_E, int topk, int64_t row_bytes, int64_t p_begin,
     int64_t rows, uint8_t* __restrict__ dst, const uint8_t* __restrict__ scales, int64_t sbytes,
     uint8_t* __restrict__ dst_scales) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int lane = lane_id();
   if (r >= rows) return;
   const int64_t p = p_begin + r;
