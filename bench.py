@@ -100,20 +100,19 @@ GEMM_KERNEL_NAMES = {
     "gateup_kernel<false>": "gateup_gemm", "down_kernel<false>": "down_gemm",
     "bwd_dh_kernel": "bwd_dh_gemm", "bwd_dwd_kernel": "bwd_dwd_gemm",
     "bwd_dwgu_kernel": "bwd_dwgu_gemm", "bwd_dx_kernel": "bwd_dx_gemm",
-    "gather_kernel": "gather", "reverse_combine_kernel": "reverse_combine",
+    "reverse_combine_kernel": "reverse_combine",
     "::combine_kernel": "combine+reverse_dispatch",
 }
 
 
 def permute_bytes(p):
     """Algorithmic HBM bytes per step of the row-moving kernels (rows moved in
-    + out; index and weight arrays included), summed over a step's launches
-    (the gather runs once per minibatch)."""
+    + out; index and weight arrays included). The dispatch gather has no
+    kernel of its own: the GEMMs read x and dY rows in place."""
     R, T, H = p.R, p.T, p.H
     return {
-        "gather": R * 2 * H * 2 + R * 4,                         # x row in, ring row out, perm
         "combine": R * 2 * H + R * 8 + T * 2 * H,                # obuf rows, w + dest, y rows
-        "reverse_combine": R * 2 * H * 2 + T * 2 * H + R * 12,   # obuf in, dO out, dY, w/dest/dw
+        "reverse_combine": R * 2 * H + T * 2 * H + R * 12,       # obuf rows, dY, w/dest/dw
         "reverse_dispatch": R * 2 * H + R * 4 + T * 2 * H,       # dX rows, dest, dx rows
     }
 

@@ -76,13 +76,17 @@ MOK_DEV void wait_vm_lds() {
 // barriers instead. The compiler does not count these operations in its own
 // vmcnt bookkeeping either; that only makes its waits for ordinary loads
 // stricter, never weaker.
-MOK_DEV void copy16_to_lds(const void* g, const uint8_t* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_cptr)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(m0) : "memory");
+// `lds` is the 32-bit LDS byte address (wave-uniform, see lds_addr).
+MOK_DEV void copy16_to_lds(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(lds) : "memory");
 }
-MOK_DEV void copy4_to_lds(const void* g, const uint8_t* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_cptr)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "{m0}"(m0) : "memory");
+MOK_DEV void copy4_to_lds(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(g), "{m0}"(lds) : "memory");
+}
+// 32-bit LDS address of a pointer into a __shared__ array (formed once per
+// tile: the generic-to-LDS conversion carries a null check)
+MOK_DEV uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_cptr)p);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads: a workgroup-
@@ -122,10 +126,20 @@ struct RowsGateUp {
 
 // ------------------------------------------------------------------ loaders
 // Every loader copies one pair of stages (slot j = stages 2j, 2j+1) with kDma
-// direct copies per wavefront (dma(j, t)), and supplies this lane's MFMA
+// direct copies per wavefront (dma(j, slot)), and supplies this lane's MFMA
 // fragment of 32 rows/columns starting at r0 for half h (stage parity) and
 // 16-wide bf16 K step kk (frag). Every wavefront issues exactly kDma copies
-// per pair (positions past the end are clamped, never skipped).
+// per pair (positions past the end are clamped or read zeros, never skipped).
+//
+// The copies are spread one per MFMA through the main loop, and with one
+// wavefront per SIMD only a few other instructions issue in an MFMA's
+// shadow, so a copy has to cost almost nothing besides itself: every loader
+// keeps this lane's per-copy address offsets in registers (set up once per
+// tile), adds a wave-uniform base for the pair, and takes the LDS address
+// (m0) as a 32-bit offset formed on the scalar unit. (Computing the addresses
+// per copy measured 20% slower on the K-outer GEMMs.)
+
+MOK_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // K-contiguous operand. One copy instruction fills a 1 KiB window (8
 // physical rows x 128 B); lane l writes bytes 16*l .. +16 of it, so each lane
@@ -135,16 +149,18 @@ struct LoadKD {
   static constexpr int kDma = R / 32;
   static constexpr int kReads = 1;               // LDS reads per fragment
   Rows src;
-  MOK_DEV void dma1(int j, uint8_t* t, int q) const {  // copy q of pair j
+  mutable uint32_t mb;     // LDS address of this wavefront's first window in the pair's slot
+  MOK_DEV void dma1(int j, uint32_t slot, int q) const {  // copy q of pair j
+    if (q == 0) mb = slot + wave_id() * 1024;
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
     const int g = w + 4 * q;                     // window g = physical rows 8g .. 8g+7
     const int row = swap03(8 * g + (l >> 3));    // logical row stored there
     const int lc = (l & 7) ^ (row & 7);          // logical chunk at physical chunk l&7
-    copy16_to_lds(src.row(row) + j * kSlotRow + lc * 16, t + g * 1024);
+    copy16_to_lds(src.row(row) + j * kSlotRow + lc * 16, mb + q * 4096);
   }
-  MOK_DEV void dma(int j, uint8_t* t) const {
+  MOK_DEV void dma(int j, uint32_t slot) const {
 #pragma unroll
-    for (int q = 0; q < kDma; ++q) dma1(j, t, q);
+    for (int q = 0; q < kDma; ++q) dma1(j, slot, q);
   }
   MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id();
@@ -153,9 +169,11 @@ struct LoadKD {
 };
 
 // K-outer bf16 operand: element (k, n) at src0 + k*ld + 2n bytes for k <
-// ksplit and src1 + (k - ksplit)*ld + 2n beyond; k-rows >= K read as zero,
-// columns past ncols are clamped (their products land in unstored output).
-// A slot is 64 k-rows of 256 columns; one copy fills 2 k-rows.
+// ksplit and src1 + (k - ksplit)*ld + 2n beyond (ksplit a multiple of 64, so
+// a pair never straddles it); k-rows >= K read as zero, columns past ncols
+// are clamped (their products land in unstored output). A slot is 64 k-rows
+// of 256 columns; copy q of wavefront w fills window g = w + 4q, i.e. k-rows
+// 2g (lanes 0-31) and 2g+1 (lanes 32-63).
 template <int R>
 struct LoadKO {
   static_assert(R == 256, "K-outer tiles have 256 columns");
@@ -167,20 +185,44 @@ struct LoadKO {
   int64_t ld;              // bytes between k-rows
   int K;
   int ncols;               // valid columns (multiple of 8, >= 8)
-  MOK_DEV void dma1(int j, uint8_t* t, int q) const {  // copy q of pair j
+  int64_t off[kDma];       // this lane's byte offset from k-row 0 of the pair, per copy
+  mutable const uint8_t* pb;   // k-row 0 of the current pair
+  mutable uint32_t mb;         // LDS address of this wavefront's first window in the slot
+  mutable int kr;              // k-rows of the current pair inside K
+  MOK_DEV LoadKO(const uint8_t* s0, const uint8_t* s1, int ksplit_, int64_t ld_, int K_, int ncols_)
+      : src0(s0), src1(s1), ksplit(ksplit_), ld(ld_), K(K_), ncols(ncols_) {
     const int w = (int)(threadIdx.x >> 6), l = lane_id();
-    const int g = w + 4 * q;                     // window g = k-rows 2g, 2g+1
-    const int kl = 2 * g + (l >> 5);
-    const int c = (l & 31) ^ ((kl & 3) << 2);    // logical chunk at physical chunk l&31
-    const int k = j * 64 + kl;
-    const int cc = min(c, (ncols >> 3) - 1);
-    const uint8_t* gp = k >= K ? kZeroRow + c * 16
-                      : (k < ksplit ? src0 + (int64_t)k * ld : src1 + (int64_t)(k - ksplit) * ld) + cc * 16;
-    copy16_to_lds(gp, t + g * 1024);
-  }
-  MOK_DEV void dma(int j, uint8_t* t) const {
 #pragma unroll
-    for (int q = 0; q < kDma; ++q) dma1(j, t, q);
+    for (int q = 0; q < kDma; ++q) {
+      const int kl = 2 * (w + 4 * q) + (l >> 5);
+      const int c = (l & 31) ^ ((kl & 3) << 2);  // logical chunk at physical chunk l&31
+      const int cc = min(c, (ncols >> 3) - 1);   // (< 32: also inside the zero row)
+      off[q] = (int64_t)kl * ld + cc * 16;
+    }
+  }
+  // this lane's chunk in the zero row for copy window g (tail pair only)
+  MOK_DEV static const uint8_t* zero_chunk(int kl, int ncols) {
+    const int c = (lane_id() & 31) ^ ((kl & 3) << 2);
+    return kZeroRow + min(c, (ncols >> 3) - 1) * 16;
+  }
+  MOK_DEV void dma1(int j, uint32_t slot, int q) const {
+    if (q == 0) {                                // wave-uniform state of the pair
+      const int k0 = j * 64;
+      pb = k0 < ksplit ? src0 + (int64_t)k0 * ld : src1 + (int64_t)(k0 - ksplit) * ld;
+      mb = slot + wave_id() * 1024;
+      kr = K - k0;
+    }
+    const uint8_t* gp = pb + off[q];
+    if (kr < 64) {                               // tail pair (wave-uniform branch)
+      asm volatile("");                          // a branch, not a select on every copy
+      const int kl = 2 * ((int)(threadIdx.x >> 6) + 4 * q) + (lane_id() >> 5);
+      if (kl >= kr) gp = zero_chunk(kl, ncols);
+    }
+    copy16_to_lds(gp, mb + q * 4096);
+  }
+  MOK_DEV void dma(int j, uint32_t slot) const {
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) dma1(j, slot, q);
   }
   MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
     const int l = lane_id(), g = l >> 4, L = l & 15;
@@ -195,6 +237,107 @@ struct LoadKO {
   }
 };
 
+// Gathered operands: the operand's row r (K-contiguous) or k-row k (K-outer)
+// is row tok[r] of a token-major source, tok being the schedule's token of
+// each permuted row. The GEMMs thereby read x and dY rows in place; no
+// gathered copy of them is ever written.
+
+// K-contiguous gathered operand (rows past nrows clamp to the last row):
+// this lane's row address per copy is formed once per tile.
+template <int R>
+struct LoadKDG {
+  static constexpr int kDma = R / 32;
+  static constexpr int kReads = 1;
+  const uint8_t* rowp[kDma];
+  mutable uint32_t mb;
+  MOK_DEV LoadKDG(const uint8_t* base, const int32_t* tok, int64_t stride, int nrows) {
+    const int w = (int)(threadIdx.x >> 6), l = lane_id();
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) {
+      const int row = swap03(8 * (w + 4 * q) + (l >> 3));
+      const int lc = (l & 7) ^ (row & 7);
+      rowp[q] = base + (int64_t)tok[min(row, nrows - 1)] * stride + lc * 16;
+    }
+  }
+  MOK_DEV void dma1(int j, uint32_t slot, int q) const {
+    if (q == 0) mb = slot + wave_id() * 1024;
+    copy16_to_lds(rowp[q] + j * kSlotRow, mb + q * 4096);
+  }
+  MOK_DEV void dma(int j, uint32_t slot) const {
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) dma1(j, slot, q);
+  }
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
+    return LoadKD<R, RowsStrided>::frag(t, r0, h, kk);
+  }
+};
+
+// K-outer gathered bf16 operand: k-row k is src + tok[k]*ld (k < K), zero
+// beyond. Wavefront w copies the 16 k-rows 16w .. 16w+15 of a pair (window g
+// = 8w + q holds k-rows 2g, 2g+1), so the 16 token indices it needs are one
+// wave-uniform scalar load of 64 bytes, issued with the first copy of the
+// pair before (pairs are copied in ascending order) and used one pair later,
+// when it has long arrived. tok must stay readable 128 entries past K.
+typedef __attribute__((ext_vector_type(16))) int i32x16_t;
+typedef const __attribute__((address_space(4))) i32x16_t* tok16_cptr;
+
+template <int R>
+struct LoadKOG {
+  static_assert(R == 256, "K-outer tiles have 256 columns");
+  static constexpr int kDma = 8;
+  static constexpr int kReads = 2;
+  const int32_t* tok;      // token of k-row 0
+  uint32_t ld;             // bytes between token rows
+  int K;
+  int ncols;
+  const uint8_t* colp[kDma];   // this lane's column chunk in token row 0, per copy
+  mutable i32x16_t cur, nxt;
+  mutable uint32_t mb;         // LDS address of this wavefront's first window in the slot
+  mutable int kr;              // k-rows of the current pair inside K
+  MOK_DEV i32x16_t load16(int j) const {
+    return *(tok16_cptr)(const void*)(tok + 64 * j + 16 * wave_id());
+  }
+  MOK_DEV LoadKOG(const uint8_t* src, const int32_t* tok_, int64_t ld_, int K_, int ncols)
+      : tok(tok_), ld((uint32_t)ld_), K(K_), ncols(ncols) {
+    const int l = lane_id();
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) {
+      const int kl = 2 * q + (l >> 5);           // k-row within the wavefront's 16, mod 4 as 2g+hi
+      const int c = (l & 31) ^ ((kl & 3) << 2);
+      const int cc = min(c, (ncols >> 3) - 1);
+      colp[q] = src + cc * 16;
+    }
+    nxt = load16(0);
+  }
+  MOK_DEV void dma1(int j, uint32_t slot, int q) const {
+    if (q == 0) {
+      cur = nxt;
+      nxt = load16(j + 1);
+      mb = slot + wave_id() * 8192;
+      kr = K - j * 64;
+    }
+    const int hi = lane_id() >> 5;
+    // (readfirstlane keeps the two uniform picks apart: folded into one
+    // lane-dependent vector index, the index vector would go to scratch)
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readfirstlane(cur[2 * q]);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readfirstlane(cur[2 * q + 1]);
+    const uint8_t* gp = colp[q] + (uint64_t)(hi ? t1 : t0) * ld;
+    if (kr < 64) {                               // tail pair (wave-uniform branch)
+      asm volatile("");                          // a branch, not a select on every copy
+      const int kl = 16 * (int)(threadIdx.x >> 6) + 2 * q + hi;
+      if (kl >= kr) gp = LoadKO<R>::zero_chunk(kl, ncols);
+    }
+    copy16_to_lds(gp, mb + q * 1024);
+  }
+  MOK_DEV void dma(int j, uint32_t slot) const {
+#pragma unroll
+    for (int q = 0; q < kDma; ++q) dma1(j, slot, q);
+  }
+  MOK_DEV static bf16x8_t frag(const uint8_t* t, int r0, int h, int kk) {
+    return LoadKO<R>::frag(t, r0, h, kk);
+  }
+};
+
 // E8M0 block scales of a 256-row fp8 operand, copied into LDS as one 32-bit
 // word per row holding the scales of K blocks 4j .. 4j+3 (the two stages of
 // slot j; K is a multiple of 128, so the word never runs past the row). Lane
@@ -204,17 +347,33 @@ struct LoadScalesD {
   static_assert(R == 256, "scale tiles have 256 rows");
   static constexpr int kDma = 1;
   Rows src;                                      // byte address of each row's scale 0
-  MOK_DEV void dma(int j, uint8_t* t) const {
-    const int w = (int)(threadIdx.x >> 6), l = lane_id();
+  MOK_DEV void dma(int j, uint32_t slot) const {
+    const int w = wave_id(), l = lane_id();
     const uint8_t* gp = src.row(64 * w + l) + j * 4;
-    copy4_to_lds(gp, t + 256 * w);
+    copy4_to_lds(gp, slot + 256 * w);
+  }
+};
+
+// Scales of a gathered fp8 operand: lane l of wavefront w copies the word of
+// row 64w + l, i.e. of source row tok[64w + l] (clamped to nrows - 1).
+template <int R>
+struct LoadScalesDG {
+  static_assert(R == 256, "scale tiles have 256 rows");
+  static constexpr int kDma = 1;
+  const uint8_t* rowp;
+  MOK_DEV LoadScalesDG(const uint8_t* base, const int32_t* tok, int64_t stride, int nrows) {
+    rowp = base + (int64_t)tok[min((int)threadIdx.x, nrows - 1)] * stride;
+  }
+  MOK_DEV void dma(int j, uint32_t slot) const {
+    copy4_to_lds(rowp + j * 4, slot + 256 * wave_id());
   }
 };
 
 struct NoScales {
   static constexpr int kDma = 0;
-  MOK_DEV void dma(int, uint8_t*) const {}
+  MOK_DEV void dma(int, uint32_t) const {}
 };
+
 
 // ------------------------------------------------------------------ accumulators
 template <int FM, int FN>
@@ -372,35 +531,50 @@ MOK_DEV void mfma_f8(const FragsF8<G>& f, int i, int j, int sh, Acc<G::FM, G::FN
 template <class SM, class LA, class LB, class SA, class SB>
 struct Pipe {
   static constexpr int kD = LA::kDma + LB::kDma + SA::kDma + SB::kDma;
-  SM& sm;
   const LA& la;
   const LB& lb;
   const SA& sa;
   const SB& sb;
-  MOK_DEV void dma(int j) const {                // pair j into slot j%2
+  // LDS addresses of slot 0 of each side; slot b is b slot sizes further
+  // (arithmetic, not an array: an array indexed by j & 1 would live in
+  // scratch memory)
+  uint32_t oa, ob, osa, osb;
+  static constexpr uint32_t kSa = sizeof(SM::a[0]), kSb = sizeof(SM::b[0]);
+  MOK_DEV Pipe(SM& sm, const LA& la_, const LB& lb_, const SA& sa_, const SB& sb_)
+      : la(la_), lb(lb_), sa(sa_), sb(sb_), oa(lds_addr(sm.a[0])), ob(lds_addr(sm.b[0])), osa(0), osb(0) {
+    if constexpr (SA::kDma > 0) osa = lds_addr(sm.sa[0]);
+    if constexpr (SB::kDma > 0) osb = lds_addr(sm.sb[0]);
+  }
+  MOK_DEV uint32_t a_at(int b) const { return oa + b * kSa; }
+  MOK_DEV uint32_t b_at(int b) const { return ob + b * kSb; }
+  MOK_DEV uint32_t sa_at(int b) const { return osa + b * (uint32_t)sizeof(SM::sa[0]); }
+  MOK_DEV uint32_t sb_at(int b) const { return osb + b * (uint32_t)sizeof(SM::sb[0]); }
+  // pair j into slot j%2; the B side first, so that a gathered A operand's
+  // token loads complete while B's copies are issued (prologue only)
+  MOK_DEV void dma(int j) const {
     const int b = j & 1;
-    la.dma(j, sm.a[b]);
-    lb.dma(j, sm.b[b]);
-    if constexpr (SA::kDma > 0) sa.dma(j, reinterpret_cast<uint8_t*>(sm.sa[b]));
-    if constexpr (SB::kDma > 0) sb.dma(j, reinterpret_cast<uint8_t*>(sm.sb[b]));
+    lb.dma(j, b_at(b));
+    if constexpr (SB::kDma > 0) sb.dma(j, sb_at(b));
+    la.dma(j, a_at(b));
+    if constexpr (SA::kDma > 0) sa.dma(j, sa_at(b));
   }
   // copy u (0 .. 2*kDma-1) of pair j: A copies first, then B (bf16 only)
   MOK_DEV void dma_unit(int j, int u) const {
     const int b = j & 1;
-    if (u < LA::kDma) la.dma1(j, sm.a[b], u);
-    else lb.dma1(j, sm.b[b], u - LA::kDma);
+    if (u < LA::kDma) la.dma1(j, a_at(b), u);
+    else lb.dma1(j, b_at(b), u - LA::kDma);
   }
   // fp8: copy u of one side of pair j (u < 8: a K-contiguous window; u == 8:
   // the side's scale words)
   MOK_DEV void dma_a1(int j, int u) const {
     const int s = j & 1;
-    if (u < LA::kDma) la.dma1(j, sm.a[s], u);
-    else if constexpr (SA::kDma > 0) sa.dma(j, reinterpret_cast<uint8_t*>(sm.sa[s]));
+    if (u < LA::kDma) la.dma1(j, a_at(s), u);
+    else if constexpr (SA::kDma > 0) sa.dma(j, sa_at(s));
   }
   MOK_DEV void dma_b1(int j, int u) const {
     const int s = j & 1;
-    if (u < LB::kDma) lb.dma1(j, sm.b[s], u);
-    else if constexpr (SB::kDma > 0) sb.dma(j, reinterpret_cast<uint8_t*>(sm.sb[s]));
+    if (u < LB::kDma) lb.dma1(j, b_at(s), u);
+    else if constexpr (SB::kDma > 0) sb.dma(j, sb_at(s));
   }
   MOK_DEV void publish() const {                 // all copies landed, all LDS reads done
     wait_vm_lds<0>();
@@ -419,7 +593,7 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
   constexpr int kD = P::kD;
   static_assert(kD < 64, "vmcnt range");
   static_assert(G::FM == 4 && G::FN == 4, "schedule written for 4 x 4 fragments");
-  const P p{sm, la, lb, sa, sb};
+  const P p(sm, la, lb, sa, sb);
   acc.zero();
   __syncthreads();                               // previous users of the LDS buffers are done
   if (nk <= 0) return;

@@ -26,7 +26,6 @@ struct FwdTile {
   mok_tile t;
   int nrows;
   int64_t slot_row0;     // ring row of the tile's first row
-  int64_t x_row0;        // row of the tile's first row in ring_x
 };
 
 MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int ti, FwdTile& ft) {
@@ -34,10 +33,11 @@ MOK_DEV void fwd_tile_at(const mok_fwd_args& a, int ti, FwdTile& ft) {
   ft.nrows = ft.t.p1 - ft.t.p0;
   const int m = ft.t.m;
   ft.slot_row0 = (int64_t)(m % a.n_slots) * a.M + (ft.t.p0 - (int64_t)m * a.M);
-  ft.x_row0 = a.x_resident ? ft.t.p0 : ft.slot_row0;
 }
 
-// gate/up GEMM + SwiGLU of one row tile x 128 h-columns. The B tile holds 32-row
+// gate/up GEMM + SwiGLU of one row tile x 128 h-columns. The A operand is the
+// tile's x rows read in place through the token table (the dispatch gather
+// fused into the operand copies). The B tile holds 32-row
 // groups alternating Wg and Wu, so accumulator column blocks j = 2jj (gate) and
 // 2jj + 1 (up) cover the same 32 h-columns.
 template <bool F8>
@@ -51,12 +51,12 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
   const int64_t xrow = F8 ? H : 2 * H;                       // bytes per X row
   const int64_t wrow = F8 ? H : 2 * H;                       // bytes per weight row
   const int64_t eoff = (int64_t)ft.t.e * I * wrow;
-  LoadKD<G::BM, RowsStrided> la{{a.ring_x + ft.x_row0 * xrow, xrow, ft.nrows}};
+  const LoadKDG<G::BM> la(a.x, a.tok + ft.t.p0, xrow, ft.nrows);
   LoadKD<G::BN, RowsGateUp> lb{{(const uint8_t*)a.wg + eoff, (const uint8_t*)a.wu + eoff, wrow, n0, (int)I}};
   Acc<G::FM, G::FN> acc;
   if constexpr (F8) {
     const int64_t sx = H / 32;
-    LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_xs + ft.x_row0 * sx, sx, ft.nrows}};
+    const LoadScalesDG<G::BM> lsa(a.xs, a.tok + ft.t.p0, sx, ft.nrows);
     const int64_t se = (int64_t)ft.t.e * I * sx;
     LoadScalesD<G::BN, RowsGateUp> lsb{{a.sg + se, a.su + se, sx, n0, (int)I}};
     mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);
@@ -68,7 +68,6 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
   // SwiGLU on the accumulators; h (and a, b) staged in LDS for row-wise stores.
   constexpr int HW = G::BN / 2;                               // 128 h columns
   uint8_t* st = lds_raw;
-  const int hcol0 = G::wn() * (G::WTN / 2);
   if constexpr (!F8) {
     // h = silu(a) * b per element from an fp32 half-tile in LDS. Tile column
     // (c/32)*64 + c%32 holds gate column c of the tile, +32 its up column.
@@ -250,6 +249,10 @@ MOK_DEV bool bwd_tile(const mok_bwd_args& a, int ncol, mok_tile& t, int& ny) {
 
 // dh = dO . Wd[e] (K = H), then the SwiGLU backward from the saved a, b:
 // dA = dh*b*s*(1 + a*(1-s)), dB = dh*a*s, h = a*s*b with s = sigmoid(a).
+// dO row p is w_p * dy[tok[p]] (w_p = topk_w at the row's flat position): the
+// A operand is the dy rows read in place and w_p scales the fp32 dh row in
+// the epilogue. h is stored as w_p * h, the operand that takes w_p's place in
+// dWd = sum_p dO[p]^T h[p] = sum_p dy[tok[p]]^T (w_p h[p]).
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
@@ -260,13 +263,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
   const int nrows = t.p1 - t.p0;
   const int64_t H = a.H, I = a.I;
   const int n0 = ny * G::BN;
-  LoadKD<G::BM, RowsStrided> la{{reinterpret_cast<const uint8_t*>(a.dO + (int64_t)t.p0 * H), 2 * H, nrows}};
+  const LoadKDG<G::BM> la(reinterpret_cast<const uint8_t*>(a.dy), a.tok + t.p0, 2 * H, nrows);
   const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(a.wd + (int64_t)t.e * H * I + n0),
                         reinterpret_cast<const uint8_t*>(a.wd + (int64_t)t.e * H * I + n0), 0x7FFFFFFF,
                         2 * I, (int)H, (int)min<int64_t>(G::BN, I - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
   mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
+  // w_p of the tile's rows in the top 1 KiB of LDS (outside the bf16 ring and
+  // the fp32 half-tile; published by the barrier after the first staging)
+  float* wrow = reinterpret_cast<float*>(tile_rows<Smem<G, false>>(lds_raw));
+  for (int r = threadIdx.x; r < G::BM; r += kThreads) wrow[r] = r < nrows ? a.topk_w[a.perm[t.p0 + r]] : 0.f;
   // dA, dB and h per element from an fp32 half-tile of dh in LDS and the
   // saved a, b (16-byte loads and stores along the row). A thread keeps one
   // 8-column group c and takes rows r0, r0 + 8, ..., r0 + 120 of each half,
@@ -303,6 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
         const int r = r0 + 64 * grp + 8 * u;
         if (!colok || r >= rows) continue;
         const int64_t p = t.p0 + 128 * half + r;
+        const float wp = wrow[128 * half + r];
         float dh[8], av[8], bv[8], da[8], db[8], h[8];
         HS::get8(lds_raw, r, c, dh);
         unpack_bf16x8(va[u], av);
@@ -310,9 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
           const float sg = sigmoidf_(av[v]);
-          da[v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
-          db[v] = dh[v] * av[v] * sg;
-          h[v] = av[v] * sg * bv[v];
+          const float d = wp * dh[v];
+          da[v] = d * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
+          db[v] = d * av[v] * sg;
+          h[v] = wp * (av[v] * sg * bv[v]);
         }
         store_nt(a.dab + p * 2 * I + n0 + c, pack_bf16x8(da));
         store_nt(a.dab + p * 2 * I + I + n0 + c, pack_bf16x8(db));
@@ -350,21 +359,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
 }
 
 // Weight gradients out[m][n] = sum over the expert's rows p (ascending) of
-// A[p][m] * B[p][n]; both operands K-outer.
-MOK_DEV void dw_tile(uint8_t* lds_raw, const bf16_t* A, int64_t lda, int mlimit, const bf16_t* B,
-                     int64_t ldb, int nlimit, int K, bf16_t* out, int64_t ldo) {
+// A[p][m] * B[p][n]; both operands K-outer (one of them gathered: its k-row p
+// is a token row of dy or x, read in place through the token table).
+template <class LA, class LB>
+MOK_DEV void dw_tile(uint8_t* lds_raw, const LA& la, int mlimit, const LB& lb, int nlimit, int K,
+                     bf16_t* out, int64_t ldo) {
   using G = G256;
   Smem<G, false>& sm = *reinterpret_cast<Smem<G, false>*>(lds_raw);
-  const LoadKO<G::BM> la{reinterpret_cast<const uint8_t*>(A), reinterpret_cast<const uint8_t*>(A),
-                        0x7FFFFFFF, 2 * lda, K, mlimit};
-  const LoadKO<G::BN> lb{reinterpret_cast<const uint8_t*>(B), reinterpret_cast<const uint8_t*>(B),
-                        0x7FFFFFFF, 2 * ldb, K, nlimit};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
   mainloop_x<kTrDw, G, false>(sm, la, lb, ns, ns, (K + 31) / 32, acc);
   store_bf16_x<kTrDw, G>(lds_raw, acc, mlimit, nlimit, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
+// dWd[e] = sum_p dO[p]^T h[p] = sum_p dy[tok[p]]^T (w_p h[p]) (hb holds w_p h)
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
@@ -375,11 +383,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, in
   const int ntn = (int)((I + G::BN - 1) / G::BN);
   const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
   const int o = a.offsets[e], c = a.offsets[e + 1] - o;
-  dw_tile(lds_raw, a.dO + (int64_t)o * H + m0, H, (int)min<int64_t>(G::BM, H - m0),
-          a.hb + (int64_t)o * I + n0, I, (int)min<int64_t>(G::BN, I - n0), c,
-          a.dwd + (int64_t)e * H * I + (int64_t)m0 * I + n0, I);
+  const int mlim = (int)min<int64_t>(G::BM, H - m0), nlim = (int)min<int64_t>(G::BN, I - n0);
+  const LoadKOG<G::BM> la(reinterpret_cast<const uint8_t*>(a.dy + m0), a.tok + o, 2 * H, c, mlim);
+  const uint8_t* hp = reinterpret_cast<const uint8_t*>(a.hb + (int64_t)o * I + n0);
+  const LoadKO<G::BN> lb{hp, hp, 0x7FFFFFFF, 2 * I, c, nlim};
+  dw_tile(lds_raw, la, mlim, lb, nlim, c, a.dwd + (int64_t)e * H * I + (int64_t)m0 * I + n0, I);
 }
 
+// [dWg; dWu][e] = sum_p [dA dB][p]^T x[tok[p]]
 __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, int tiles_per_e) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
@@ -396,11 +407,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, i
   const int tiles_g = (int)((I + G::BM - 1) / G::BM);
   const bool up = mt >= tiles_g;
   const int m0 = (up ? mt - tiles_g : mt) * G::BM;
-  const int mlim = (int)min<int64_t>(G::BM, I - m0);
+  const int mlim = (int)min<int64_t>(G::BM, I - m0), nlim = (int)min<int64_t>(G::BN, H - n0);
   const int o = a.offsets[e], c = a.offsets[e + 1] - o;
   bf16_t* out = (up ? a.dwu : a.dwg) + (int64_t)e * I * H + (int64_t)m0 * H + n0;
-  dw_tile(lds_raw, a.dab + (int64_t)o * 2 * I + (up ? I : 0) + m0, 2 * I, mlim,
-          a.xg + (int64_t)o * H + n0, H, (int)min<int64_t>(G::BN, H - n0), c, out, H);
+  const uint8_t* dp = reinterpret_cast<const uint8_t*>(a.dab + (int64_t)o * 2 * I + (up ? I : 0) + m0);
+  const LoadKO<G::BM> la{dp, dp, 0x7FFFFFFF, 4 * I, c, mlim};
+  const LoadKOG<G::BN> lb(reinterpret_cast<const uint8_t*>(a.x + n0), a.tok + o, 2 * H, c, nlim);
+  dw_tile(lds_raw, la, mlim, lb, nlim, c, out, H);
 }
 
 // ================================================================== MXFP8 backward

@@ -1,10 +1,12 @@
-// Row-wise, HBM-bound kernels of the MoE layer: token gather (dispatch),
-// weighted combine, reverse-combine, reverse-dispatch and MXFP8 quantization.
+// Row-wise, HBM-bound kernels of the MoE layer: weighted combine,
+// reverse-combine, reverse-dispatch and MXFP8 quantization.
 //
 // [MoK clip] How-to item 2: forward = pull dispatch + push combine, backward =
 // pull reverse-combine + push reverse-dispatch, all four from one schedule.
-// On one GPU the exchange is a local gather/scatter through HBM; each kernel
-// moves whole rows with 16-byte accesses so a wavefront touches contiguous
+// On one GPU the exchange is local: the pull dispatch is fused into the GEMMs'
+// operand copies (x and dy rows read in place through the token table), the
+// push combine is the down GEMM's row scatter into obuf, and the kernels here
+// move whole rows with 16-byte accesses so a wavefront touches contiguous
 // 1 KiB spans.
 #include "mok_device.h"
 #include "mok_launch.h"
@@ -27,39 +29,6 @@ MOK_DEV uint4 pack8(const float f[8]) {
   r.z = pack_bf16x2(f[4], f[5]);
   r.w = pack_bf16x2(f[6], f[7]);
   return r;
-}
-
-// ------------------------------------------------------------------ gather
-// One wavefront per destination row (its index read from lane 0, so the
-// perm entry loads once per wavefront through the scalar unit).
-__global__ __launch_bounds__(256) void gather_kernel(
-    const uint8_t* __restrict__ x, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets_E, int topk, int64_t row_bytes, int64_t p_begin,
-    int64_t rows, uint8_t* __restrict__ dst, const uint8_t* __restrict__ scales, int64_t sbytes,
-    uint8_t* __restrict__ dst_scales) {
-  const int64_t r = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  const int lane = lane_id();
-  if (r >= rows) return;
-  const int64_t p = p_begin + r;
-  if (p >= *offsets_E) return;                   // rows of invalid ids: no tile reads them
-  const int64_t t = perm[p] / topk;
-  const uint4* src = reinterpret_cast<const uint4*>(x + t * row_bytes);
-  uint4* d = reinterpret_cast<uint4*>(dst + r * row_bytes);
-  const int64_t n16 = row_bytes >> 4;
-  int64_t c = lane;
-  for (; c + 192 < n16; c += 256) {              // four loads in flight per lane
-    const uint4 v0 = src[c], v1 = src[c + 64], v2 = src[c + 128], v3 = src[c + 192];
-    d[c] = v0;
-    d[c + 64] = v1;
-    d[c + 128] = v2;
-    d[c + 192] = v3;
-  }
-  for (; c < n16; c += 64) d[c] = src[c];
-  if (scales) {
-    const uint32_t* ss = reinterpret_cast<const uint32_t*>(scales + t * sbytes);
-    uint32_t* ds = reinterpret_cast<uint32_t*>(dst_scales + r * sbytes);
-    for (int64_t c = lane; c < (sbytes >> 2); c += 64) ds[c] = ss[c];
-  }
 }
 
 // ------------------------------------------------------------------ combine
@@ -108,12 +77,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 // ------------------------------------------------------------------ reverse-combine
 // One wavefront per token: dw[t][j] = <dy[t], obuf[t*k+j]> reduced in a fixed
-// order (each lane sums its columns in ascending order, then a xor butterfly),
-// and dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order. The k rows go 8 at
-// a time through one pass over the columns, so their loads overlap.
-// With dOq (MXFP8 backward) each dO row is also quantized along H from its
-// bf16 values: a 32-column block is the 4 chunks of 4 adjacent lanes
-// (QUANT = true; the bf16 backward launches the variant without it).
+// order (each lane sums its columns in ascending order, then a xor butterfly).
+// The k rows go 8 at a time through one pass over the columns, so their loads
+// overlap. The bf16 backward needs nothing more (its GEMMs read dy rows in
+// place and apply w themselves); the MXFP8 backward (QUANT) also writes
+// dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order and quantizes each dO
+// row along H from those bf16 values: a 32-column block is the 4 chunks of 4
+// adjacent lanes.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
@@ -158,9 +128,9 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
           part[u] = fmaf(g[q], o[q], part[u]);
           d[q] = wv[u] * g[q];
         }
-        const uint4 packed = pack8(d);
-        reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = packed;
         if constexpr (QUANT) {
+          const uint4 packed = pack8(d);
+          reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = packed;
           float b[8];
           unpack8(packed, b);                    // the stored bf16 values
           float amax = 0.f;
@@ -337,17 +307,6 @@ inline unsigned grid_for(int64_t n, int64_t per_block) {
 }
 
 }  // namespace
-
-hipError_t mok_launch_gather(const void* x, const int32_t* perm, const int32_t* offsets_E,
-                             int topk, int64_t row_bytes, int64_t p_begin, int64_t rows,
-                             void* dst, const uint8_t* scales, int64_t sbytes,
-                             uint8_t* dst_scales, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(rows, 4)), dim3(256), 0, st,
-                     (const uint8_t*)x, perm, offsets_E, topk, row_bytes, p_begin, rows,
-                     (uint8_t*)dst, scales, sbytes, dst_scales);
-  return hipGetLastError();
-}
 
 hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t* dest,
                               const int32_t* offsets_E, int64_t T, int topk, int64_t H,

@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs
                 start_f);
     write_tiles(s.bwd_tiles + start_b, max_b - start_b, tid, lo_e, hi_e, 0x7FFFFFFF, bm_b, nullptr, 0);
   }
+  for (int q = tid; q < kTokPad; q += kScanThreads) s.tok[R + q] = 0;
   if (tid == 0) {
     *s.n_fwd_tiles = total_f;
     *s.n_bwd_tiles = total_b;
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(mok_sched_ptrs
 // 3. scatter: replay the chunk's ranking from its bases
 __global__ __launch_bounds__(kChunkThreads) void sched_scatter_kernel(const int32_t* __restrict__ ids,
                                                                     mok_sched_ptrs s, int R, int E,
-                                                                    int chunk,
+                                                                    int topk, int chunk,
                                                                     const int32_t* __restrict__ bh) {
   __shared__ int h[kChunkWaves][kMaxBuckets];
   const int nb = E + 1, nbits = 32 - __clz(E);
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(kChunkThreads) void sched_scatter_kernel(const int3
       if (act[u] && (unsigned)p < (unsigned)R) {   // always true for a consistent ranking
         s.perm[p] = i;
         s.dest[i] = p;
+        s.tok[p] = i / topk;
       }
     }
   }
@@ -286,7 +288,7 @@ int mok_schedule_chunk_rows(int64_t R) {
 }
 
 hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E,
-                               int M, int bm_f, int bm_b, int n_mb, int max_f, int max_b,
+                               int topk, int M, int bm_f, int bm_b, int n_mb, int max_f, int max_b,
                                int32_t* chunk_counts, hipStream_t st) {
   const int chunk = mok_schedule_chunk_rows(R);
   const int nchunks = (R + chunk - 1) / chunk;
@@ -297,6 +299,6 @@ hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int 
                      chunk_counts, M, bm_f, bm_b, n_mb, max_f, max_b);
   if (nchunks > 0)
     hipLaunchKernelGGL(sched_scatter_kernel, dim3(nchunks), dim3(kChunkThreads), 0, st, ids, s, R, E,
-                       chunk, chunk_counts);
+                       topk, chunk, chunk_counts);
   return hipGetLastError();
 }

@@ -76,8 +76,8 @@ mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
 }
 
 struct SchedLayout {
-  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, chunk_counts,
-      total;
+  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, tok,
+      chunk_counts, total;
 };
 
 SchedLayout sched_layout(const Resolved& r) {
@@ -93,6 +93,8 @@ SchedLayout sched_layout(const Resolved& r) {
   L.mb_start = o;  o = align_up(o + 4 * (size_t)(r.n_mb + 1));
   L.n_bwd = o;     o = align_up(o + 4);
   L.bwd_tiles = o; o = align_up(o + sizeof(mok_tile) * (size_t)r.max_bwd_tiles);
+  // token of each permuted row (perm[p] / k), read by the GEMMs' row loaders
+  L.tok = o;       o = align_up(o + 4 * ((size_t)r.R + kTokPad));
   // scratch of the build: per-chunk counts per bucket
   const int64_t chunk = mok_schedule_chunk_rows(r.R);
   L.chunk_counts = o; o = align_up(o + 4 * (size_t)((r.R + chunk - 1) / chunk) * (r.E + 1));
@@ -109,6 +111,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
   s.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
   s.perm = reinterpret_cast<int32_t*>(b + L.perm);
   s.dest = reinterpret_cast<int32_t*>(b + L.dest);
+  s.tok = reinterpret_cast<int32_t*>(b + L.tok);
   s.n_fwd_tiles = reinterpret_cast<int32_t*>(b + L.n_fwd);
   s.fwd_tiles = reinterpret_cast<mok_tile*>(b + L.fwd_tiles);
   s.mb_tile_start = reinterpret_cast<int32_t*>(b + L.mb_start);
@@ -120,7 +123,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
 // Workspace carve-up. Forward and backward never run inside one call, so
 // they share the same bytes.
 struct FwdWs {
-  size_t ring_x, ring_xs, ring_h, ring_hs, obuf, xq, xqs, total;
+  size_t ring_h, ring_hs, obuf, xq, xqs, total;
 };
 struct BwdWs {
   size_t dO, dab, hb, dxrows;
@@ -133,8 +136,6 @@ FwdWs fwd_ws(const Resolved& r) {
   FwdWs w;
   const size_t slots = (size_t)r.n_slots * r.M;
   size_t o = 0;
-  w.ring_x = o;  o = align_up(o + slots * (r.mx ? r.H : 2 * r.H));
-  w.ring_xs = o; o = align_up(o + (r.mx ? slots * (r.H / 32) : 0));
   w.ring_h = o;  o = align_up(o + slots * (r.mx ? r.I : 2 * r.I));
   w.ring_hs = o; o = align_up(o + (r.mx ? slots * (r.I / 32) : 0));
   w.obuf = o;    o = align_up(o + (size_t)r.R * 2 * r.H);
@@ -147,7 +148,7 @@ FwdWs fwd_ws(const Resolved& r) {
 BwdWs bwd_ws(const Resolved& r) {
   BwdWs w;
   size_t o = 0;
-  w.dO = o;     o = align_up(o + (size_t)r.R * 2 * r.H);
+  w.dO = o;     o = align_up(o + (r.mx ? (size_t)r.R * 2 * r.H : 0));   // MXFP8 only
   w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
@@ -177,18 +178,17 @@ BwdWs bwd_ws(const Resolved& r) {
 
 size_t ws_bytes(const Resolved& r) { return std::max(fwd_ws(r).total, bwd_ws(r).total); }
 
-// fwd_ctx: the down outputs in flat row order [R][H], the gate/up
-// pre-activations a | b [R][2I] and (bf16 only) the gathered x in permuted
-// order [R][H]; the MXFP8 backward token-blocks x from x itself.
+// fwd_ctx: the down outputs in flat row order [R][H] and the gate/up
+// pre-activations a | b [R][2I] (permuted order). The backward reads x rows
+// in place, so no gathered copy of x is kept.
 struct CtxLayout {
-  size_t obuf, ab, xg, total;
+  size_t obuf, ab, total;
 };
 CtxLayout ctx_layout(const Resolved& r) {
   CtxLayout c;
   c.obuf = 0;
   c.ab = align_up((size_t)r.R * 2 * r.H);
-  c.xg = c.ab + align_up((size_t)r.R * 4 * r.I);
-  c.total = c.xg + (r.mx ? 0 : align_up((size_t)r.R * 2 * r.H));
+  c.total = c.ab + align_up((size_t)r.R * 4 * r.I);
   return c;
 }
 
@@ -366,7 +366,7 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
   hipStream_t st = (hipStream_t)stream;
   int32_t* chunk_counts =
       reinterpret_cast<int32_t*>(static_cast<uint8_t*>(schedule) + sched_layout(r).chunk_counts);
-  MOK_RUN("schedule", mok_launch_schedule(topk_ids, p, (int)r.R, r.E, r.M, kTileRowsFwd,
+  MOK_RUN("schedule", mok_launch_schedule(topk_ids, p, (int)r.R, r.E, r.k, r.M, kTileRowsFwd,
                                           kTileRowsBwd, r.n_mb, r.max_fwd_tiles,
                                           r.max_bwd_tiles, chunk_counts, st));
   return MOK_OK;
@@ -402,30 +402,24 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   a.mb_tile_start = sp.mb_tile_start;
   a.wg = weights->w_gate; a.wu = weights->w_up; a.wd = weights->w_down;
   a.sg = weights->s_gate; a.su = weights->s_up; a.sd = weights->s_down;
-  a.ring_x = ws + W.ring_x; a.ring_xs = ws + W.ring_xs;
+  a.tok = sp.tok;
   a.ring_h = ws + W.ring_h; a.ring_hs = ws + W.ring_hs;
   uint8_t* ctx = static_cast<uint8_t*>(fwd_ctx);
   const CtxLayout C = ctx_layout(r);
   a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx + C.obuf : ws + W.obuf);
   a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + C.ab) : nullptr;
-  // With a context the gathered rows go straight to their permuted
-  // positions in it (the backward's weight gradients read them there), so
-  // X ring slots are not reused; h still cycles through the ring.
-  a.x_resident = ctx && !r.mx ? 1 : 0;
-  if (a.x_resident) a.ring_x = ctx + C.xg;
 
-  // MXFP8: x is quantized once per token (blocks lie inside a row, so this is
-  // bitwise the same as quantizing each gathered row), then fp8 rows and their
-  // scale rows are gathered like bf16 rows.
-  const void* xsrc = x;
-  const uint8_t* xscales = nullptr;
-  const int64_t xrow = r.mx ? r.H : 2 * r.H;
-  const int64_t srow = r.H / 32;
+  // Dispatch: the gate/up GEMM reads each routed row's x row in place through
+  // the token table. MXFP8: x is quantized once per token (blocks lie inside a
+  // row, so this is bitwise the same as quantizing each gathered row) and the
+  // GEMM reads the fp8 rows and their scale rows the same way.
+  a.x = static_cast<const uint8_t*>(x);
+  a.xs = nullptr;
   if (r.mx) {
     MOK_RUN("mxfp8_quantize_x", mok_launch_mxfp8_quantize(static_cast<const bf16_t*>(x), r.T, r.H,
                                                           ws + W.xq, ws + W.xqs, st));
-    xsrc = ws + W.xq;
-    xscales = ws + W.xqs;
+    a.x = ws + W.xq;
+    a.xs = ws + W.xqs;
   }
   // Minibatches go through the ring N_s at a time: the group [m0, m1) with
   // m0 a multiple of N_s occupies slots 0 .. m1-m0-1, i.e. one contiguous
@@ -437,9 +431,6 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
     const int64_t rows = std::min<int64_t>((int64_t)m1 * r.M, r.R) - p0;
     const int max_tiles = (int)std::min<int64_t>(cdiv(rows, kTileRowsFwd) + r.E + (m1 - m0),
                                                  r.max_fwd_tiles);
-    uint8_t* xdst = a.x_resident ? a.ring_x + p0 * xrow : a.ring_x;
-    MOK_RUN("gather", mok_launch_gather(xsrc, sp.perm, sp.offsets + r.E, r.k, xrow, p0, rows,
-                                        xdst, xscales, srow, r.mx ? a.ring_xs : nullptr, st));
     MOK_RUN("gateup_gemm", mok_launch_gateup(a, m0, m1, max_tiles, r.mx, st));
     MOK_RUN("down_gemm", mok_launch_down(a, m0, m1, max_tiles, r.mx, st));
   }
@@ -481,8 +472,11 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   const CtxLayout C = ctx_layout(r);
   const bf16_t* obuf = reinterpret_cast<const bf16_t*>(ctx + C.obuf);
   a.ab = reinterpret_cast<const bf16_t*>(ctx + C.ab);
-  a.xg = r.mx ? nullptr : reinterpret_cast<const bf16_t*>(ctx + C.xg);
-  a.dO = reinterpret_cast<bf16_t*>(ws + W.dO);
+  a.tok = sp.tok;
+  a.topk_w = topk_w;
+  a.dy = static_cast<const bf16_t*>(dy);
+  a.x = static_cast<const bf16_t*>(x);
+  a.dO = r.mx ? reinterpret_cast<bf16_t*>(ws + W.dO) : nullptr;
   a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
   a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
@@ -530,7 +524,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   if (r.T > 0) {
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
                                        sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
-                                       const_cast<bf16_t*>(a.dO), nullptr, nullptr, st));
+                                       nullptr, nullptr, nullptr, st));
     MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
   }
   MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));

@@ -11,12 +11,17 @@ struct mok_sched_ptrs {
   int32_t* offsets;
   int32_t* perm;
   int32_t* dest;
+  int32_t* tok;          // [R + kTokPad]: token of permuted row p (perm[p] / topk), then zeros
   int32_t* n_fwd_tiles;
   mok_tile* fwd_tiles;
   int32_t* mb_tile_start;
   int32_t* n_bwd_tiles;
   mok_tile* bwd_tiles;
 };
+
+// Zero entries after the R entries of the token table: the GEMM loaders read
+// token indices up to two 64-row pairs of K past an expert's last row.
+constexpr int kTokPad = 256;
 
 // Row-tile sizes of the grouped GEMMs.
 constexpr int kTileRowsFwd = 256;
@@ -25,25 +30,17 @@ constexpr int kTileRowsBwd = 256;
 // Rows per chunk of the schedule's count/scatter passes, and the launches.
 // chunk_counts holds ceil(R / chunk) * (E + 1) ints.
 int mok_schedule_chunk_rows(int64_t R);
-hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E, int M,
+hipError_t mok_launch_schedule(const int32_t* ids, const mok_sched_ptrs& s, int R, int E, int topk, int M,
                                int bm_f, int bm_b, int n_mb, int max_f, int max_b,
                                int32_t* chunk_counts, hipStream_t st);
-
-// Gather: for permuted rows p in [p_begin, p_begin + rows) that are valid
-// (p < offsets[E]), copy x[perm[p] / topk] to dst row (p - p_begin).
-// row_bytes = bytes per row (2H for bf16, H for E4M3 codes); if scales != NULL
-// the E8M0 rows (sbytes each) are gathered to dst_scales the same way.
-hipError_t mok_launch_gather(const void* x, const int32_t* perm, const int32_t* offsets_E,
-                             int topk, int64_t row_bytes, int64_t p_begin, int64_t rows,
-                             void* dst, const uint8_t* scales, int64_t sbytes,
-                             uint8_t* dst_scales, hipStream_t st);
 
 // y[t] = sum_j w[t][j] * obuf[t*k+j] (valid rows only), fp32, j ascending.
 hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t* dest,
                               const int32_t* offsets_E, int64_t T, int topk, int64_t H,
                               bf16_t* y, hipStream_t st);
 
-// dw[t][j] = <dy[t], obuf[t*k+j]>; dO[dest[t*k+j]] = bf16(w[t][j] * dy[t]).
+// dw[t][j] = <dy[t], obuf[t*k+j]>; with dOq (MXFP8) also dO[dest[t*k+j]] =
+// bf16(w[t][j] * dy[t]) and its rows quantized along H (dOq, dOs).
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
                                       int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
@@ -76,12 +73,13 @@ struct mok_fwd_args {
   const uint8_t* sg;
   const uint8_t* su;
   const uint8_t* sd;
-  // ring: slot s holds X rows at ring_x + s*M*xrow_bytes, h rows at ring_h + ...
-  // With x_resident, ring_x instead holds every gathered X row at its
-  // permuted position p (kept for the backward in fwd_ctx).
-  int x_resident;
-  uint8_t* ring_x;
-  uint8_t* ring_xs;      // MXFP8 scales of ring_x rows
+  // operand rows of the gate/up GEMM: permuted row p is row tok[p] of x (bf16
+  // [T][H]) or, for MXFP8, of its E4M3 codes [T][H] with scales xs [T][H/32]
+  const int32_t* tok;
+  const uint8_t* x;
+  const uint8_t* xs;
+  // ring: slot s holds the h rows of minibatch m (s = m mod N_s) at
+  // ring_h + s*M*hrow_bytes
   uint8_t* ring_h;
   uint8_t* ring_hs;      // MXFP8 scales of ring_h rows
   // outputs
@@ -108,11 +106,14 @@ struct mok_bwd_args {
   const bf16_t* wg;
   const bf16_t* wu;
   const bf16_t* wd;
-  const bf16_t* dO;      // [R][H] permuted
-  const bf16_t* ab;      // [R][2I] permuted (saved by forward)
-  const bf16_t* xg;      // [R][H] gathered x, permuted (saved by the forward)
+  const int32_t* tok;     // token of each permuted row (schedule)
+  const float* topk_w;    // [T][k] combine weights
+  const bf16_t* dy;       // [T][H] upstream gradient
+  const bf16_t* x;        // [T][H] layer input
+  const bf16_t* dO;       // MXFP8 only: [R][H] permuted rows w * dy
+  const bf16_t* ab;       // [R][2I] permuted (saved by forward)
   bf16_t* dab;           // [R][2I] permuted: dA | dB
-  bf16_t* hb;            // [R][I] permuted: recomputed h
+  bf16_t* hb;            // [R][I] permuted: recomputed h (bf16: w * h)
   bf16_t* dxrows;        // [R][H] flat row order
   bf16_t* dwg;
   bf16_t* dwu;

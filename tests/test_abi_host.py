@@ -117,7 +117,7 @@ def test_calls_reject_bad_arguments_before_any_launch():
     pm = P(dtype=mok.MOK_MXFP8)
     wsm, _, cbm = mok.buffer_sizes(pm)
     _, _, cb = mok.buffer_sizes(prob)
-    assert 0 < cbm < cb                      # outputs and a, b; no gathered x
+    assert 0 < cbm == cb                     # obuf and a, b in both formats (x is read in place)
     assert L.mok_forward(ctypes.byref(pm), None, fake, fake, fake, ctypes.byref(w), fake, None,
                          fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
     wm = mok.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)

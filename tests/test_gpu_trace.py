@@ -35,7 +35,7 @@ def test_trace_counts_launches_and_times_fit_the_step():
     stats = mok.trace_collect()
     elapsed = e0.elapsed_time(e1)
 
-    expect = {"schedule", "gather", "gateup_gemm", "down_gemm", "combine", "reverse_combine",
+    expect = {"schedule", "gateup_gemm", "down_gemm", "combine", "reverse_combine",
               "bwd_dh_gemm", "bwd_dwd_gemm", "bwd_dwgu_gemm", "bwd_dx_gemm", "reverse_dispatch"}
     assert expect <= set(stats), sorted(stats)
     for name in expect:
