@@ -61,6 +61,37 @@ def test_empty_experts_exact_zero_gradients():
     assert_close_bf16(from_dev_bf16(dx), ref["dx"], "dx")
 
 
+def test_backward_one_hot_expert_invalid_ids_and_ragged_token_axis():
+    """The weight-gradient GEMMs read x and dY rows in place through the
+    schedule's token table, 64 token rows per pair: experts here hold 199
+    rows (3 full pairs + 7), 64 and 65 rows (a pair boundary and one row past
+    it), 1 row, 69 rows, and none. Two ids are out of range: their rows get
+    no expert output, d topk_w 0 and no dx contribution."""
+    p = problem(200, 256, 384, 7, 2, seed=45)
+    x, ids, w, wg, wu, wd = host_inputs(p)
+    j1 = np.full(200, 6)
+    j1[:64] = 2
+    j1[64:129] = 3
+    j1[129] = 5
+    ids2 = np.stack([np.full(200, 4), j1], axis=1)
+    ids2[180, 1] = 99
+    ids2[150, 0] = -1
+    dy = make_dy(p)
+    _, (dx, dwg, dwu, dwd, dtw) = gpu_fwd_bwd(p, device_inputs(p, ids2), dy)
+    ref = oracle.backward(f64(x), ids2, w.astype(np.float64), ExpertsF64(wg, wu, wd), f64(dy))
+    got_dw = dtw.cpu().numpy()
+    assert got_dw[180, 1] == 0.0 and got_dw[150, 0] == 0.0
+    assert_close_bf16(from_dev_bf16(dx), ref["dx"], "dx")
+    assert_close_bf16(got_dw.astype(np.float64), ref["dw"], "d topk_w")
+    for e in range(p.E):
+        for name, got in (("dWg", dwg), ("dWu", dwu), ("dWd", dwd)):
+            g = from_dev_bf16(got[e])
+            if not ref[name][e].any():
+                assert not g.any(), f"{name}[{e}] of an empty expert must be exactly zero"
+            else:
+                assert_close_bf16(g, ref[name][e], f"{name}[{e}]")
+
+
 @pytest.mark.timeout(900)
 def test_large_hidden_fwd_bwd_sampled():
     """T=16384, H=7168, E=32, top-4, I=2048, Zipf(0.8) loads."""
