@@ -441,13 +441,18 @@ struct FragsB16 {
   bf16x8_t a[G::FM], b[G::FN];
 };
 
-template <class G, class LA, class LB>
+// VM x VN: the fragment rows x columns of this wavefront that hold valid
+// rows (the others are skipped: no LDS reads, no MFMAs; their accumulators
+// stay zero and are never stored).
+template <class G, class LA, class LB, int VM = 4, int VN = 4>
 MOK_DEV void read_b16(const uint8_t* ta, const uint8_t* tb, int h, int kk, FragsB16<G>& f) {
   const int r0 = G::wm() * G::WTM, c0 = G::wn() * G::WTN;
 #pragma unroll
-  for (int i = 0; i < G::FM; ++i) f.a[i] = LA::frag(ta, r0 + i * 32, h, kk);
+  for (int i = 0; i < G::FM; ++i)
+    if (i < VM) f.a[i] = LA::frag(ta, r0 + i * 32, h, kk);
 #pragma unroll
-  for (int j = 0; j < G::FN; ++j) f.b[j] = LB::frag(tb, c0 + j * 32, h, kk);
+  for (int j = 0; j < G::FN; ++j)
+    if (j < VN) f.b[j] = LB::frag(tb, c0 + j * 32, h, kk);
 }
 
 // LDS read instructions per fragment, averaged over the two operands
@@ -456,9 +461,10 @@ struct RdPerFrag {
   static constexpr int kAvg = (LA::kReads + LB::kReads + 1) / 2;
 };
 
-template <class G>
+template <class G, int VM = 4, int VN = 4>
 MOK_DEV void mfma_b16_1(const FragsB16<G>& f, int i, int j, Acc<G::FM, G::FN>& acc) {
-  acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+  if (i < VM && j < VN)
+    acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
 }
 
 template <class G>
@@ -585,7 +591,7 @@ struct Pipe {
 // scheduling-group masks (llvm.amdgcn.sched.group.barrier)
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
-template <class G, bool F8, class LA, class LB, class SA, class SB>
+template <class G, bool F8, int VM = 4, int VN = 4, class LA, class LB, class SA, class SB>
 MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
                       Acc<G::FM, G::FN>& acc) {
   using SM = Smem<G, F8>;
@@ -612,7 +618,7 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
   if constexpr (!F8) {
     static_assert(LA::kDma == 8 && LB::kDma == 8, "16 copies per pair");
     FragsB16<G> f0, f1;
-    read_b16<G, LA, LB>(sm.a[0], sm.b[0], 0, 0, f0);
+    read_b16<G, LA, LB, VM, VN>(sm.a[0], sm.b[0], 0, 0, f0);
     // One region: the 16 MFMAs of fragments f while the 8 fragments of the
     // next K step are read into n; the reads go with the first 8 MFMAs, and
     // with CP >= 0 copies 8*CP' .. 8*CP'+7 of pair cp follow the last 8, one
@@ -620,9 +626,9 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
     auto region = [&](const FragsB16<G>& f, FragsB16<G>& n, const uint8_t* ta, const uint8_t* tb, int h,
                       int kk, int cp, int half) {
       __builtin_amdgcn_sched_barrier(0);
-      read_b16<G, LA, LB>(ta, tb, h, kk, n);
+      read_b16<G, LA, LB, VM, VN>(ta, tb, h, kk, n);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) mfma_b16_1<G>(f, t >> 2, t & 3, acc);
+      for (int t = 0; t < 8; ++t) mfma_b16_1<G, VM, VN>(f, t >> 2, t & 3, acc);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * RdPerFrag<LA, LB>::kAvg, 0);
@@ -631,7 +637,7 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        mfma_b16_1<G>(f, 2 + (t >> 2), t & 3, acc);
+        mfma_b16_1<G, VM, VN>(f, 2 + (t >> 2), t & 3, acc);
         if (cp >= 0) p.dma_unit(cp, 8 * half + t);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -661,9 +667,11 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
     const int sh_lane = 8 * (lane_id() >> 5);
     FragsF8<G> f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) read_f8_a<G>(sm.a[0], sm.sa[0], 0, i, f);
+    for (int i = 0; i < 4; ++i)
+      if (i < VM) read_f8_a<G>(sm.a[0], sm.sa[0], 0, i, f);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) read_f8_b<G>(sm.b[0], sm.sb[0], 0, jj, f);
+    for (int jj = 0; jj < 4; ++jj)
+      if (jj < VN) read_f8_b<G>(sm.b[0], sm.sb[0], 0, jj, f);
     // the copies of one side of pair cp go one after each of a region's 8
     // MFMAs, the side's scale words with the last (cp < 0: none)
     auto copy_after = [&](int t, int cp, bool bside) {
@@ -689,8 +697,8 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        mfma_f8<G>(f, t >> 2, t & 3, sh, acc);
-        if (t < 2) read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 2 + t, f);
+        if ((t >> 2) < VM && (t & 3) < VN) mfma_f8<G>(f, t >> 2, t & 3, sh, acc);
+        if (t < 2 && 2 + t < VM) read_f8_a<G>(sm.a[slot], sm.sa[slot], h, 2 + t, f);
         copy_after(t, pend, true);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -700,15 +708,15 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       // of the next stage go into the registers region A freed
       const int nslot = ODD ? (slot ^ 1) : slot, nh = ODD ? 0 : 1;
       const FragsF8<G> g = f;
-      read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 0, f);
-      read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 1, f);
+      if (0 < VM) read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 0, f);
+      if (1 < VM) read_f8_a<G>(sm.a[nslot], sm.sa[nslot], nh, 1, f);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        mfma_f8<G>(g, 2, jj, sh, acc);
+        if (2 < VM && jj < VN) mfma_f8<G>(g, 2, jj, sh, acc);
         copy_after(2 * jj, cpy, false);
-        mfma_f8<G>(g, 3, jj, sh, acc);
+        if (3 < VM && jj < VN) mfma_f8<G>(g, 3, jj, sh, acc);
         copy_after(2 * jj + 1, cpy, false);
-        read_f8_b<G>(sm.b[nslot], sm.sb[nslot], nh, jj, f);
+        if (jj < VN) read_f8_b<G>(sm.b[nslot], sm.sb[nslot], nh, jj, f);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -721,6 +729,37 @@ MOK_DEV void mainloop(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa,
       const bool odd = (kt & 1) != 0;
       stage(kt, odd, odd && (kt >> 1) + 2 < np, !odd && kt >= 2 && (kt >> 1) + 1 < np);
     }
+  }
+}
+
+// The main loop with only this wavefront's fragments that hold valid rows:
+// nvalid rows of the A operand (ON_B = false; fragment rows of the
+// wavefront's 128) or of the B operand (ON_B = true; fragment columns).
+// The last row tile of an expert usually holds few rows; its wavefronts then
+// skip the MFMAs and LDS reads of the padding rows (a quarter of the work per
+// 32 valid rows) while copies and barriers stay the same in every wavefront.
+// The variant is chosen per wavefront from a wave-uniform value, so every
+// branch here is a scalar branch.
+template <bool ON_B, class G, bool F8, class LA, class LB, class SA, class SB>
+MOK_DEV void mainloop_rows(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
+                           int nvalid, Acc<G::FM, G::FN>& acc) {
+  static_assert(G::FM == 4 && G::FN == 4, "four fragments per side");
+  const int w0 = ON_B ? G::wn() * G::WTN : G::wm() * G::WTM;
+  const int v = __builtin_amdgcn_readfirstlane(min(4, max(0, (nvalid - w0 + 31) / 32)));
+  if (v >= 4) {
+    mainloop<G, F8, 4, 4>(sm, la, lb, sa, sb, nk, acc);
+  } else if (v == 3) {
+    if constexpr (ON_B) mainloop<G, F8, 4, 3>(sm, la, lb, sa, sb, nk, acc);
+    else mainloop<G, F8, 3, 4>(sm, la, lb, sa, sb, nk, acc);
+  } else if (v == 2) {
+    if constexpr (ON_B) mainloop<G, F8, 4, 2>(sm, la, lb, sa, sb, nk, acc);
+    else mainloop<G, F8, 2, 4>(sm, la, lb, sa, sb, nk, acc);
+  } else if (v == 1) {
+    if constexpr (ON_B) mainloop<G, F8, 4, 1>(sm, la, lb, sa, sb, nk, acc);
+    else mainloop<G, F8, 1, 4>(sm, la, lb, sa, sb, nk, acc);
+  } else {
+    if constexpr (ON_B) mainloop<G, F8, 4, 0>(sm, la, lb, sa, sb, nk, acc);
+    else mainloop<G, F8, 0, 4>(sm, la, lb, sa, sb, nk, acc);
   }
 }
 

@@ -59,10 +59,10 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
     const LoadScalesDG<G::BM> lsa(a.xs, a.tok + ft.t.p0, sx, ft.nrows);
     const int64_t se = (int64_t)ft.t.e * I * sx;
     LoadScalesD<G::BN, RowsGateUp> lsb{{a.sg + se, a.su + se, sx, n0, (int)I}};
-    mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);
+    mainloop_rows<false, G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), ft.nrows, acc);
   } else {
     NoScales ns;
-    mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
+    mainloop_rows<false, G, false>(sm, la, lb, ns, ns, (int)(H / 32), ft.nrows, acc);
   }
 
   // SwiGLU on the accumulators; h (and a, b) staged in LDS for row-wise stores.
@@ -168,11 +168,12 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
 // (store_tile_bf16_t); chosen per kernel family from measurements.
 constexpr bool kTrDown = true, kTrDx = true, kTrDw = true;
 
+// (na: valid rows of la, the tile's row operand)
 template <bool TR, class G, bool F8, class LA, class LB, class SA, class SB>
 MOK_DEV void mainloop_x(Smem<G, F8>& sm, const LA& la, const LB& lb, const SA& sa, const SB& sb, int nk,
-                        Acc<G::FM, G::FN>& acc) {
-  if constexpr (TR) mainloop<G, F8>(sm, lb, la, sb, sa, nk, acc);
-  else mainloop<G, F8>(sm, la, lb, sa, sb, nk, acc);
+                        int na, Acc<G::FM, G::FN>& acc) {
+  if constexpr (TR) mainloop_rows<true, G, F8>(sm, lb, la, sb, sa, nk, na, acc);
+  else mainloop_rows<false, G, F8>(sm, la, lb, sa, sb, nk, na, acc);
 }
 
 template <bool TR, class G, class Dst>
@@ -200,10 +201,10 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) 
     const int64_t sx = I / 32;
     LoadScalesD<G::BM, RowsStrided> lsa{{a.ring_hs + ft.slot_row0 * sx, sx, ft.nrows}};
     LoadScalesD<G::BN, RowsStrided> lsb{{a.sd + ((int64_t)ft.t.e * H + n0) * sx, sx, (int)(H - n0)}};
-    mainloop_x<kTrDown, G, true>(sm, la, lb, lsa, lsb, (int)(I / 64), acc);
+    mainloop_x<kTrDown, G, true>(sm, la, lb, lsa, lsb, (int)(I / 64), ft.nrows, acc);
   } else {
     NoScales ns;
-    mainloop_x<kTrDown, G, false>(sm, la, lb, ns, ns, (int)(I / 32), acc);
+    mainloop_x<kTrDown, G, false>(sm, la, lb, ns, ns, (int)(I / 32), ft.nrows, acc);
   }
   // destination rows, staged in the top 1 KiB of LDS once every wavefront
   // has left the main loop
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
                         2 * I, (int)H, (int)min<int64_t>(G::BN, I - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop<G, false>(sm, la, lb, ns, ns, (int)(H / 32), acc);
+  mainloop_rows<false, G, false>(sm, la, lb, ns, ns, (int)(H / 32), nrows, acc);
   // w_p of the tile's rows in the top 1 KiB of LDS (outside the bf16 ring and
   // the fp32 half-tile; published by the barrier after the first staging)
   float* wrow = reinterpret_cast<float*>(tile_rows<Smem<G, false>>(lds_raw));
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
                         2 * H, (int)(2 * I), (int)min<int64_t>(G::BN, H - n0)};
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop_x<kTrDx, G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), acc);
+  mainloop_x<kTrDx, G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), nrows, acc);
   int* rows = tile_rows<Smem<G, false>>(lds_raw);
   __syncthreads();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
@@ -368,7 +369,7 @@ MOK_DEV void dw_tile(uint8_t* lds_raw, const LA& la, int mlimit, const LB& lb, i
   Smem<G, false>& sm = *reinterpret_cast<Smem<G, false>*>(lds_raw);
   NoScales ns;
   Acc<G::FM, G::FN> acc;
-  mainloop_x<kTrDw, G, false>(sm, la, lb, ns, ns, (K + 31) / 32, acc);
+  mainloop_x<kTrDw, G, false>(sm, la, lb, ns, ns, (K + 31) / 32, mlimit, acc);
   store_bf16_x<kTrDw, G>(lds_raw, acc, mlimit, nlimit, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
   const LoadScalesD<G::BM, RowsStrided> lsa{{a.dOs + (int64_t)t.p0 * sH, sH, nrows}};
   const LoadScalesD<G::BN, RowsStrided> lsb{{a.wdt_s + wrow * sH, sH, (int)(I - n0)}};
   Acc<G::FM, G::FN> acc;
-  mainloop<G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), acc);
+  mainloop_rows<false, G, true>(sm, la, lb, lsa, lsb, (int)(H / 64), nrows, acc);
   // per row and 32-column block: dA, dB, h from dh and the saved a, b;
   // the 32 dA (and dB) values of the block share one scale along I
   using HS = HalfF32<G>;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx8_kernel(mok_bwd_args a, in
   const LoadScalesD<G::BM, RowsStrided> lsa{{a.dabs + (int64_t)t.p0 * sK, sK, nrows}};
   const LoadScalesD<G::BN, RowsStrided> lsb{{a.wgut_s + wrow * sK, sK, (int)(H - n0)}};
   Acc<G::FM, G::FN> acc;
-  mainloop_x<kTrDx, G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), acc);
+  mainloop_x<kTrDx, G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), nrows, acc);
   int* rows = tile_rows<Smem<G, true>>(lds_raw);
   __syncthreads();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
@@ -560,7 +561,7 @@ MOK_DEV void dw8_tile(uint8_t* lds_raw, const uint8_t* A, const uint8_t* As, int
   const LoadScalesD<G::BM, RowsStrided> lsa{{As, kp / 32, mlim}};
   const LoadScalesD<G::BN, RowsStrided> lsb{{Bs, kp / 32, nlim}};
   Acc<G::FM, G::FN> acc;
-  mainloop_x<kTrDw, G, true>(sm, la, lb, lsa, lsb, kp / 64, acc);
+  mainloop_x<kTrDw, G, true>(sm, la, lb, lsa, lsb, kp / 64, mlim, acc);
   store_bf16_x<kTrDw, G>(lds_raw, acc, mlim, nlim, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
