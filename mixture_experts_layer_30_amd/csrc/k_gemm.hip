@@ -135,8 +135,8 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
         uint32_t w[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          w[u] = e4m3_encode(h[4 * u] * inv) | (e4m3_encode(h[4 * u + 1] * inv) << 8) |
-                 (e4m3_encode(h[4 * u + 2] * inv) << 16) | (e4m3_encode(h[4 * u + 3] * inv) << 24);
+          w[u] = e4m3_pack4(h[4 * u] * inv, h[4 * u + 1] * inv, h[4 * u + 2] * inv,
+                          h[4 * u + 3] * inv);
         const int64_t rr = 128 * half + r;
         uint4* d = reinterpret_cast<uint4*>(hq + rr * I + blk * 32);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -511,8 +511,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
           uint32_t w[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            w[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
-                   (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
+            w[u] = e4m3_pack4(v[4 * u] * inv, v[4 * u + 1] * inv, v[4 * u + 2] * inv,
+                          v[4 * u + 3] * inv);
           const int64_t col = (side ? I : 0) + n0 + c0;
           uint4* d = reinterpret_cast<uint4*>(a.dabq + p * 2 * I + col);
           d[0] = make_uint4(w[0], w[1], w[2], w[3]);

@@ -140,10 +140,10 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
           amax = fmaxf(amax, __shfl_xor(amax, 2));
           const int sc = mx_scale_byte(amax);
           const float inv = mx_inv_scale(sc);
-          const uint32_t lo = e4m3_encode(b[0] * inv) | (e4m3_encode(b[1] * inv) << 8) |
-                              (e4m3_encode(b[2] * inv) << 16) | (e4m3_encode(b[3] * inv) << 24);
-          const uint32_t hi = e4m3_encode(b[4] * inv) | (e4m3_encode(b[5] * inv) << 8) |
-                              (e4m3_encode(b[6] * inv) << 16) | (e4m3_encode(b[7] * inv) << 24);
+          const uint32_t lo = e4m3_pack4(b[0] * inv, b[1] * inv, b[2] * inv,
+                          b[3] * inv);
+          const uint32_t hi = e4m3_pack4(b[4] * inv, b[5] * inv, b[6] * inv,
+                          b[7] * inv);
           reinterpret_cast<uint2*>(dOq + (int64_t)pos[u] * H)[c] = make_uint2(lo, hi);
           if ((c & 3) == 0) dOs[(int64_t)pos[u] * (H / 32) + (c >> 2)] = (uint8_t)sc;
         }
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
   uint32_t wds[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    wds[u] = e4m3_encode(v[4 * u] * inv) | (e4m3_encode(v[4 * u + 1] * inv) << 8) |
-             (e4m3_encode(v[4 * u + 2] * inv) << 16) | (e4m3_encode(v[4 * u + 3] * inv) << 24);
+    wds[u] = e4m3_pack4(v[4 * u] * inv, v[4 * u + 1] * inv, v[4 * u + 2] * inv,
+                          v[4 * u + 3] * inv);
   }
   uint4* d = reinterpret_cast<uint4*>(q + r * K + b * 32);
   d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
@@ -256,8 +256,8 @@ __global__ __launch_bounds__(256) void token_quantize_kernel(
     uint32_t wds[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      wds[u] = e4m3_encode(x[4 * u] * inv) | (e4m3_encode(x[4 * u + 1] * inv) << 8) |
-               (e4m3_encode(x[4 * u + 2] * inv) << 16) | (e4m3_encode(x[4 * u + 3] * inv) << 24);
+      wds[u] = e4m3_pack4(x[4 * u] * inv, x[4 * u + 1] * inv, x[4 * u + 2] * inv,
+                          x[4 * u + 3] * inv);
     uint4* d = reinterpret_cast<uint4*>(dst + N * koff + n * kp + r0 + 32 * qb);
     d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
     d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
