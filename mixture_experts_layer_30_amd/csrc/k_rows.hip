@@ -80,15 +80,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // order (each lane sums its columns in ascending order, then a xor butterfly).
 // The k rows go 8 at a time through one pass over the columns, so their loads
 // overlap. The bf16 backward needs nothing more (its GEMMs read dy rows in
-// place and apply w themselves); the MXFP8 backward (QUANT) also writes
-// dO[dest[i]] = bf16(w[i] * dy[t]) in permuted order and quantizes each dO
-// row along H from those bf16 values: a 32-column block is the 4 chunks of 4
-// adjacent lanes.
+// place and apply w themselves); the MXFP8 backward (QUANT) also quantizes
+// each row dO[dest[i]] = bf16(w[i] * dy[t]) along H from those bf16 values
+// into permuted order (a 32-column block is the 4 chunks of 4 adjacent
+// lanes); the bf16 dO rows themselves are never stored.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
-    int64_t H, float* __restrict__ dw, bf16_t* __restrict__ dO, uint8_t* __restrict__ dOq,
+    int64_t H, float* __restrict__ dw, uint8_t* __restrict__ dOq,
     uint8_t* __restrict__ dOs) {
   // the token of this wavefront, read from lane 0 so that its dest and w
   // entries are loaded once per wavefront through the scalar unit
@@ -129,8 +129,7 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
           d[q] = wv[u] * g[q];
         }
         if constexpr (QUANT) {
-          const uint4 packed = pack8(d);
-          reinterpret_cast<uint4*>(dO + (int64_t)pos[u] * H)[c] = packed;
+          const uint4 packed = pack8(d);               // the bf16 dO row values
           float b[8];
           unpack8(packed, b);                    // the stored bf16 values
           float amax = 0.f;
@@ -200,9 +199,13 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
 // of 128): it stages the 128 x COLS block in LDS (2*COLS-byte row segments
 // in), then 4 adjacent threads per column quantize its four 32-row blocks and
 // write them as one 128-byte segment of the transposed row.
+// With perm, row p of the source is the token row perm[p] / topk (x, dy read
+// in place); with w as well, its values are first scaled by w[perm[p]] and
+// rounded to bf16 (the dO rows w * dy, the same bits as a stored dO row).
 template <int COLS>
 __global__ __launch_bounds__(256) void token_quantize_kernel(
     const bf16_t* __restrict__ src, int64_t ld, const int32_t* __restrict__ perm, int topk,
+    const float* __restrict__ w,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ koffs,
     const int32_t* __restrict__ blk_e, int64_t N, uint8_t* __restrict__ dst, uint8_t* __restrict__ dsts) {
   static_assert(COLS == 64 || COLS == 128, "64 or 128 columns per workgroup");
@@ -229,8 +232,17 @@ __global__ __launch_bounds__(256) void token_quantize_kernel(
     v[i] = make_uint4(0u, 0u, 0u, 0u);
     if (r < nrow && col < N) {
       const int64_t p = o + r0 + r;
-      const int64_t row = perm ? (int64_t)(perm[p] / topk) : p;
+      const int32_t i_flat = perm ? perm[p] : 0;
+      const int64_t row = perm ? (int64_t)(i_flat / topk) : p;
       v[i] = *reinterpret_cast<const uint4*>(src + row * ld + col);
+      if (w) {
+        const float wv = w[i_flat];
+        float f[8];
+        unpack8(v[i], f);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) f[q] *= wv;
+        v[i] = pack8(f);
+      }
     }
   }
 #pragma unroll
@@ -324,15 +336,15 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
 
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
+                                      int topk, int64_t H, float* dw, uint8_t* dOq,
                                       uint8_t* dOs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (dOq)
     hipLaunchKernelGGL(reverse_combine_kernel<true>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf,
-                       w, dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
+                       w, dest, offsets_E, T, topk, H, dw, dOq, dOs);
   else
     hipLaunchKernelGGL(reverse_combine_kernel<false>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy,
-                       obuf, w, dest, offsets_E, T, topk, H, dw, dO, dOq, dOs);
+                       obuf, w, dest, offsets_E, T, topk, H, dw, dOq, dOs);
   return hipGetLastError();
 }
 
@@ -360,14 +372,14 @@ hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K,
 }
 
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
-                                     const int32_t* offsets, const int32_t* koff, int E, int64_t R,
+                                     const float* w, const int32_t* offsets, const int32_t* koff, int E, int64_t R,
                                      int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st) {
   if (R <= 0 || N <= 0) return hipSuccess;
   if (E > kMaxExperts) return hipErrorInvalidValue;
   const int nblk = mok_token_blocks(R, E);
   constexpr int kCols = 64;                       // measured: 128 columns per workgroup is 5-15% slower
   hipLaunchKernelGGL(token_quantize_kernel<kCols>, dim3((unsigned)((N + kCols - 1) / kCols), (unsigned)nblk),
-                     dim3(256), 0, st, src, ld, perm, topk, offsets, koff, koff + E + 1, N, dst, dst_scales);
+                     dim3(256), 0, st, src, ld, perm, topk, w, offsets, koff, koff + E + 1, N, dst, dst_scales);
   return hipGetLastError();
 }
 

@@ -126,7 +126,7 @@ struct FwdWs {
   size_t ring_h, ring_hs, obuf, xq, xqs, total;
 };
 struct BwdWs {
-  size_t dO, dab, hb, dxrows;
+  size_t dab, hb, dxrows;
   // MXFP8 only
   size_t dOq, dOs, dabq, dabs, dOT, dOTs, hT, hTs, dabT, dabTs, xT, xTs, koff;
   size_t total;
@@ -148,7 +148,6 @@ FwdWs fwd_ws(const Resolved& r) {
 BwdWs bwd_ws(const Resolved& r) {
   BwdWs w;
   size_t o = 0;
-  w.dO = o;     o = align_up(o + (r.mx ? (size_t)r.R * 2 * r.H : 0));   // MXFP8 only
   w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
@@ -476,7 +475,6 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   a.topk_w = topk_w;
   a.dy = static_cast<const bf16_t*>(dy);
   a.x = static_cast<const bf16_t*>(x);
-  a.dO = r.mx ? reinterpret_cast<bf16_t*>(ws + W.dO) : nullptr;
   a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
   a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
@@ -500,17 +498,18 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     if (r.T > 0) {
       // also quantizes the dO rows along H for dh
       MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
-                                         sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
-                                         const_cast<bf16_t*>(a.dO), a.dOq, a.dOs, st));
+                                         sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, a.dOq, a.dOs, st));
       MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh8(a, st));
-      MOK_RUN("token_quantize_dO", mok_launch_token_quantize(a.dO, r.H, nullptr, r.k, sp.offsets, a.koff, r.E, r.R, r.H,
+      // dO rows w * dy formed from the dy rows in place (bitwise the stored rows' values)
+      MOK_RUN("token_quantize_dO", mok_launch_token_quantize(static_cast<const bf16_t*>(dy), r.H, sp.perm, r.k,
+                                                          topk_w, sp.offsets, a.koff, r.E, r.R, r.H,
                                                           a.dOT, a.dOTs, st));
-      MOK_RUN("token_quantize_h", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, sp.offsets, a.koff, r.E, r.R, r.I,
+      MOK_RUN("token_quantize_h", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, nullptr, sp.offsets, a.koff, r.E, r.R, r.I,
                                                           a.hT, a.hTs, st));
-      MOK_RUN("token_quantize_dAB", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, sp.offsets, a.koff, r.E, r.R,
+      MOK_RUN("token_quantize_dAB", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, nullptr, sp.offsets, a.koff, r.E, r.R,
                                                           2 * r.I, a.dabT, a.dabTs, st));
       MOK_RUN("token_quantize_x", mok_launch_token_quantize(static_cast<const bf16_t*>(x), r.H, sp.perm, r.k,
-                                                          sp.offsets, a.koff, r.E, r.R, r.H, a.xT, a.xTs, st));
+                                                          nullptr, sp.offsets, a.koff, r.E, r.R, r.H, a.xT, a.xTs, st));
     }
     MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd8(a, st));
     MOK_RUN("bwd_dwgu_gemm", mok_launch_bwd_dwgu8(a, st));
@@ -523,8 +522,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   }
   if (r.T > 0) {
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
-                                       sp.offsets + r.E, r.T, r.k, r.H, d_topk_w,
-                                       nullptr, nullptr, nullptr, st));
+                                       sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, nullptr, nullptr, st));
     MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
   }
   MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));

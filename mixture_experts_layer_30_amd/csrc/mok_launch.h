@@ -39,11 +39,11 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
                               const int32_t* offsets_E, int64_t T, int topk, int64_t H,
                               bf16_t* y, hipStream_t st);
 
-// dw[t][j] = <dy[t], obuf[t*k+j]>; with dOq (MXFP8) also dO[dest[t*k+j]] =
-// bf16(w[t][j] * dy[t]) and its rows quantized along H (dOq, dOs).
+// dw[t][j] = <dy[t], obuf[t*k+j]>; with dOq (MXFP8) also the rows
+// dO[dest[t*k+j]] = bf16(w[t][j] * dy[t]) quantized along H (dOq, dOs).
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, bf16_t* dO, uint8_t* dOq,
+                                      int topk, int64_t H, float* dw, uint8_t* dOq,
                                       uint8_t* dOs, hipStream_t st);
 
 // dx[t] = sum_j dxrows[t*k+j] (valid rows only), fp32, j ascending.
@@ -110,7 +110,6 @@ struct mok_bwd_args {
   const float* topk_w;    // [T][k] combine weights
   const bf16_t* dy;       // [T][H] upstream gradient
   const bf16_t* x;        // [T][H] layer input
-  const bf16_t* dO;       // MXFP8 only: [R][H] permuted rows w * dy
   const bf16_t* ab;       // [R][2I] permuted (saved by forward)
   bf16_t* dab;           // [R][2I] permuted: dA | dB
   bf16_t* hb;            // [R][I] permuted: recomputed h (bf16: w * h)
@@ -152,9 +151,10 @@ hipError_t mok_launch_bwd_dwd8(const mok_bwd_args& a, hipStream_t st);
 hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st);
 // Token-blocked MXFP8 copy of the rows of every expert (layout as in
 // mok_bwd_args): row p of the source is src + p*ld, or with perm the token
-// row src + (perm[p] / topk)*ld; N columns; R routed rows.
+// row src + (perm[p] / topk)*ld, scaled by w[perm[p]] and rounded to bf16
+// when w is given; N columns; R routed rows.
 hipError_t mok_launch_token_quantize(const bf16_t* src, int64_t ld, const int32_t* perm, int topk,
-                                     const int32_t* offsets, const int32_t* koff, int E, int64_t R,
+                                     const float* w, const int32_t* offsets, const int32_t* koff, int E, int64_t R,
                                      int64_t N, uint8_t* dst, uint8_t* dst_scales, hipStream_t st);
 // 128-position blocks of the padded token axis (an upper bound: R + 128 E positions)
 inline int mok_token_blocks(int64_t R, int E) { return (int)((R + 128 * (int64_t)E + 127) / 128); }
