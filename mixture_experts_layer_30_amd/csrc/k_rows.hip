@@ -129,9 +129,9 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
           d[q] = wv[u] * g[q];
         }
         if constexpr (QUANT) {
-          const uint4 packed = pack8(d);               // the bf16 dO row values
+          const uint4 packed = pack8(d);
           float b[8];
-          unpack8(packed, b);                    // the stored bf16 values
+          unpack8(packed, b);                    // the bf16 values of the dO row
           float amax = 0.f;
 #pragma unroll
           for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(b[q]));
