@@ -93,7 +93,8 @@ typedef struct {
                                     row count T*topk is always used.              */
   int32_t num_cus;               /* S for the default M; 0 = 256 (MI355X).        */
   int32_t driver;                /* 0 = default (= 1), 1 = one launch per
-                                    minibatch stage (gather, gate/up, down),
+                                    stage (gate/up, down) per ring group of
+                                    N_s minibatches,
                                     2 = one persistent launch for all minibatches
                                     (not provided: MOK_ERR_UNSUPPORTED).          */
 } mok_config;
@@ -172,18 +173,17 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
                               void* schedule, size_t schedule_bytes, void* stream);
 
 /* Forward ([MoK clip] Conclusion and key chart: dispatch -> expert SwiGLU
- * FFN -> combine -> weighted sum). Per minibatch, in order: gather the rows
- * x[perm[p] / k] into a ring slot, gate/up grouped GEMM with the SwiGLU in
- * its epilogue, down grouped GEMM writing each expert output to its flat row
- * i; then y[t] = sum_{j=0..k-1} topk_w[t][j] * out[t*k + j], accumulated in
- * fp32 in ascending j and rounded once to bf16.
+ * FFN -> combine -> weighted sum). Per minibatch, in order: gate/up grouped
+ * GEMM over the rows x[perm[p] / k] (the dispatch: the GEMM reads them in
+ * place), with the SwiGLU in its epilogue writing h to a ring slot; down
+ * grouped GEMM writing each expert output to its flat row i; then
+ * y[t] = sum_{j=0..k-1} topk_w[t][j] * out[t*k + j], accumulated in fp32 in
+ * ascending j and rounded once to bf16.
  * fwd_ctx: NULL for inference; else receives what mok_backward needs: the
- * expert outputs and the gate/up pre-activations (bf16), and for bf16 the
- * gathered x rows in permuted order (so with a context, bf16 X rows are
- * gathered straight to their permuted positions there and the ring reuses
- * only the h slots). MXFP8 ([MoK card] "Core concepts": weights pre-quantized with
- * mok_mxfp8_quantize): x rows are quantized along H and h along I the same
- * way on the fly; accumulation is fp32, y is bf16. */
+ * expert outputs and the gate/up pre-activations (bf16). MXFP8 ([MoK card]
+ * "Core concepts": weights pre-quantized with mok_mxfp8_quantize): x rows are
+ * quantized along H (once per token) and h along I the same way on the fly;
+ * accumulation is fp32, y is bf16. */
 mok_status mok_forward(const mok_problem* problem, const mok_config* config,
                        const void* schedule, const void* x, const float* topk_w,
                        const mok_weights* weights, void* y, void* fwd_ctx,
@@ -191,8 +191,8 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config,
 
 /* Backward. [MoK clip] How-to item 2: reverse-combine then reverse-dispatch
  * with the same schedule; [MoK card] "What it is": forward and backward in
- * BF16 and MXFP8. x must be the forward's input (bf16: the weight gradients
- * read its gathered rows from fwd_ctx). MXFP8 (fwd_ctx from an MXFP8
+ * BF16 and MXFP8. x and dy rows are read in place through the schedule
+ * (x must be the forward's input). MXFP8 (fwd_ctx from an MXFP8
  * forward, weights with the transposed copies of mok_weights): every
  * backward GEMM takes MXFP8 operands blocked by 32 along its contraction
  * axis -- dO along H, dA|dB along 2I, and for the weight gradients dO, h,
