@@ -27,6 +27,8 @@ SMALL = [
     problem(37, 256, 256, 5, 2, seed=41),
     problem(300, 128, 384, 16, 4, seed=42),
     problem(200, 384, 256, 12, 3, seed=43),
+    problem(300, 128, 128, 512, 8, seed=46),    # the most experts: ~5 rows each, many empty
+    problem(37, 256, 128, 4, 4, seed=47),       # k = E: every token routed to every expert
 ]
 
 

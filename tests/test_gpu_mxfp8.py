@@ -81,7 +81,8 @@ def gpu_mx_forward(p, d, **cfg):
     return y, qw
 
 
-SMALL_MX = [problem(37, 256, 256, 5, 2, seed=51), problem(300, 512, 384, 16, 4, seed=52)]
+SMALL_MX = [problem(37, 256, 256, 5, 2, seed=51), problem(300, 512, 384, 16, 4, seed=52),
+            problem(300, 128, 128, 512, 8, seed=53)]   # the most experts: ~5 rows each
 
 
 @pytest.mark.parametrize("p", SMALL_MX, ids=lambda p: p.name)
