@@ -425,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, i
 // token-blocked (weight gradients, K = an expert's rows).
 
 // dh = dO . Wd[e] (K = H) from dO rows and Wd^T rows, then the SwiGLU
-// backward; writes dA|dB (bf16, for the token-blocked copies), dA|dB rows
-// quantized along 2I (for dX) and h (bf16).
+// backward; writes dA|dB rows quantized along 2I (for dX), dA|dB token-blocked
+// (for dWg/dWu) and h (bf16, token-blocked by token_quantize_kernel).
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
@@ -499,9 +499,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
             amaxa = fmaxf(amaxa, fabsf(da[u + v]));
             amaxb = fmaxf(amaxb, fabsf(db[u + v]));
           }
-          *reinterpret_cast<uint4*>(a.dab + p * 2 * I + n0 + c0 + u) = pack_bf16x8(da + u);
-          *reinterpret_cast<uint4*>(a.dab + p * 2 * I + I + n0 + c0 + u) = pack_bf16x8(db + u);
           *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
+        }
+        // the row's bf16 dA and dB values replace its fp32 dh block in the
+        // staging area (this thread alone reads that block): 64 bytes of dA,
+        // then 64 of dB, for the token-blocked pass below
+        {
+          uint4* stash = reinterpret_cast<uint4*>(lds_raw + r * HS::PITCH + c0 * 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            stash[u] = pack_bf16x8(da + 8 * u);
+            stash[4 + u] = pack_bf16x8(db + 8 * u);
+          }
         }
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
@@ -519,6 +528,50 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
           d[1] = make_uint4(w[4], w[5], w[6], w[7]);
           a.dabs[p * s2I + col / 32] = (uint8_t)sc;
         }
+      }
+    }
+    // token-blocked dA | dB of this half ([MoK card] MXFP8 backward operands
+    // of dWg/dWu, blocked by 32 along the expert's rows counted from its
+    // first row): one 32-row block x two adjacent columns per item, read from
+    // the stashed bf16 values; rows past the tile's end are zero up to the
+    // expert's padded length. Same bits as quantizing stored bf16 rows.
+    __syncthreads();
+    const int64_t N = 2 * I;
+    const int koffe = a.koff[t.e], kp = a.koff[t.e + 1] - koffe;
+    const int rbase = t.p0 - a.offsets[t.e] + 128 * half;   // padded-axis position of row 0 of the half
+    for (int item = threadIdx.x; item < 4 * 256; item += kThreads) {
+      const int rb = item >> 8, cpair = item & 255;
+      const int q = cpair >> 7, cc = (cpair & 127) * 2;     // q: dA or dB; tile columns cc, cc + 1
+      const int pos0 = rbase + 32 * rb;
+      if (pos0 >= kp || n0 + cc >= I) continue;
+      float x0[32], x1[32];
+      float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 32; ++rr) {
+        const int row = 32 * rb + rr;
+        uint32_t wv = 0u;
+        if (row < rows)
+          wv = *reinterpret_cast<const uint32_t*>(lds_raw + row * HS::PITCH + (cc >> 5) * 128 + q * 64 +
+                                                  (cc & 31) * 2);
+        x0[rr] = __uint_as_float(wv << 16);
+        x1[rr] = __uint_as_float(wv & 0xFFFF0000u);
+        m0 = fmaxf(m0, fabsf(x0[rr]));
+        m1 = fmaxf(m1, fabsf(x1[rr]));
+      }
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        const float* v = side ? x1 : x0;
+        const int sc = mx_scale_byte(side ? m1 : m0);
+        const float inv = mx_inv_scale(sc);
+        uint32_t wds[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          wds[u] = e4m3_pack4(v[4 * u] * inv, v[4 * u + 1] * inv, v[4 * u + 2] * inv, v[4 * u + 3] * inv);
+        const int64_t n = (int64_t)q * I + n0 + cc + side;
+        uint4* d = reinterpret_cast<uint4*>(a.dabT + N * koffe + n * kp + pos0);
+        d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+        a.dabTs[N * (koffe / 32) + n * (kp / 32) + pos0 / 32] = (uint8_t)sc;
       }
     }
   }

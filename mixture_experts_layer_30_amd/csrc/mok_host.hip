@@ -506,8 +506,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
                                                           a.dOT, a.dOTs, st));
       MOK_RUN("token_quantize_h", mok_launch_token_quantize(a.hb, r.I, nullptr, r.k, nullptr, sp.offsets, a.koff, r.E, r.R, r.I,
                                                           a.hT, a.hTs, st));
-      MOK_RUN("token_quantize_dAB", mok_launch_token_quantize(a.dab, 2 * r.I, nullptr, r.k, nullptr, sp.offsets, a.koff, r.E, r.R,
-                                                          2 * r.I, a.dabT, a.dabTs, st));
+      // (dA|dB token-blocked by the dh GEMM's epilogue)
       MOK_RUN("token_quantize_x", mok_launch_token_quantize(static_cast<const bf16_t*>(x), r.H, sp.perm, r.k,
                                                           nullptr, sp.offsets, a.koff, r.E, r.R, r.H, a.xT, a.xTs, st));
     }
