@@ -148,7 +148,7 @@ FwdWs fwd_ws(const Resolved& r) {
 BwdWs bwd_ws(const Resolved& r) {
   BwdWs w;
   size_t o = 0;
-  w.dab = o;    o = align_up(o + (size_t)r.R * 4 * r.I);
+  w.dab = o;    o = align_up(o + (r.mx ? 0 : (size_t)r.R * 4 * r.I));   // bf16 dA|dB (bf16 path only)
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
   w.dOq = w.dOs = w.dabq = w.dabs = w.dOT = w.dOTs = w.hT = w.hTs = w.dabT = w.dabTs = w.xT = w.xTs = w.koff = 0;
@@ -475,7 +475,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   a.topk_w = topk_w;
   a.dy = static_cast<const bf16_t*>(dy);
   a.x = static_cast<const bf16_t*>(x);
-  a.dab = reinterpret_cast<bf16_t*>(ws + W.dab);
+  a.dab = r.mx ? nullptr : reinterpret_cast<bf16_t*>(ws + W.dab);   // bf16 path only
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
   a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
   a.dwg = static_cast<bf16_t*>(dw_gate);
