@@ -297,8 +297,8 @@ struct LoadKOG {
   MOK_DEV i32x16_t load16(int j) const {
     return *(tok16_cptr)(const void*)(tok + 64 * j + 16 * wave_id());
   }
-  MOK_DEV LoadKOG(const uint8_t* src, const int32_t* tok_, int64_t ld_, int K_, int ncols)
-      : tok(tok_), ld((uint32_t)ld_), K(K_), ncols(ncols) {
+  MOK_DEV LoadKOG(const uint8_t* src, const int32_t* tok_, int64_t ld_, int K_, int ncols_)
+      : tok(tok_), ld((uint32_t)ld_), K(K_), ncols(ncols_) {
     const int l = lane_id();
 #pragma unroll
     for (int q = 0; q < kDma; ++q) {

@@ -60,7 +60,9 @@ MOK_DEV int mx_scale_byte(float amax) {
 }
 
 // E4M3 code of q (|q| < 2^9 after block scaling), round to nearest even,
-// saturating to +-448; the sign bit is copied from q (so -0 -> 0x80).
+// saturating to +-448; the sign bit is copied from q (so -0 -> 0x80). The
+// kernels encode with e4m3_pack4 (hardware conversion, the same codes); this
+// integer form states the rounding and saturation rule it was checked against.
 // Branch-free: for |q| >= 2^-6 the float's 23-bit mantissa is rounded to 3
 // bits in the integer domain (adding 2^19 - 1 plus the lowest kept bit
 // carries exactly when the dropped part is above half, or half with an odd
