@@ -12,5 +12,6 @@ from .moe_oracle import (  # noqa: F401
     e4m3_decode, e4m3_encode, mxfp8_quantize, mxfp8_dequantize, mxfp8_roundtrip,
     forward_mxfp8, forward_mxfp8_tokens, backward_mxfp8, backward_mxfp8_expert_weights,
     backward_mxfp8_tokens,
+    router_forward, router_backward,
     STATUS_BAD_EXPERT_ID,
 )

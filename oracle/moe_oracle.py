@@ -546,3 +546,49 @@ def backward_mxfp8_tokens(x_rows, ids_rows, w_rows, experts, dy_rows):
         dw[t, j] = np.sum(dy_rows[t] * out, axis=1)
         np.add.at(dx, t, dxr)
     return dx, dw
+
+
+# ============================================================================ router front end
+# [MoK clip] key chart, "Router picks top-k": the router scores every expert
+# for a token and hands the layer its k experts and their combine weights.
+# The pages give no formula; the plainest reading, the one the workloads use:
+#   * logits = x . Wr^T with Wr [E][H] (one row per expert), no bias term in
+#     the logits themselves;
+#   * an optional per-expert bias shifts the selection score only
+#     (score = logit + bias_e), as the skewed workloads shape expert loads;
+#   * the k experts with the largest scores, in descending score, equal scores
+#     in ascending expert id;
+#   * combine weights = softmax over the k selected *unbiased* logits.
+# The backward runs from d topk_w: the selection is piecewise constant, so
+# only the selected logits get gradients, through the softmax Jacobian.
+
+def router_forward(x, wr, bias, k):
+    """(logits [T][E], topk_ids int32 [T][k], topk_w [T][k]) in float64."""
+    logits = x @ wr.T
+    score = logits if bias is None else logits + np.asarray(bias)[None, :]
+    T, E = logits.shape
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        # descending score, ties to the lower id: sort on (-score, id)
+        order = sorted(range(E), key=lambda e: (-score[t, e], e))
+        ids[t] = order[:k]
+    sel = np.take_along_axis(logits, ids.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return logits, ids, ex / ex.sum(axis=1, keepdims=True)
+
+
+def router_backward(x, wr, topk_ids, topk_w, d_topk_w):
+    """d of sum(d_topk_w * topk_w) through the softmax of the selected logits.
+
+    Returns (d_sel [T][k]: gradient of each selected logit,
+             d_logits [T][E]: the same scattered, zero for unselected experts,
+             d_wr [E][H] = d_logits^T . x, dx [T][H] = d_logits . Wr)."""
+    w = np.asarray(topk_w, np.float64)
+    g = np.asarray(d_topk_w, np.float64)
+    d_sel = w * (g - (w * g).sum(axis=1, keepdims=True))
+    T, k = topk_ids.shape
+    d_logits = np.zeros((T, wr.shape[0]))
+    for t in range(T):
+        for j in range(k):
+            d_logits[t, topk_ids[t, j]] += d_sel[t, j]
+    return d_sel, d_logits, d_logits.T @ x, d_logits @ wr

@@ -161,13 +161,18 @@ def expert_bias(p: Problem) -> np.ndarray:
     return bias
 
 
-def make_routing(p: Problem, x_bits: np.ndarray, chunk: int = 2048):
-    """(topk_ids int32 [T][k], topk_w float32 [T][k]) from the seeded router."""
+def router_weights(p: Problem):
+    """(Wr [H][E] float32, selection bias [E] float64) of the seeded router."""
     rng = np.random.Generator(np.random.PCG64(_children(p)[1]))
     wr = rng.standard_normal((p.H, p.E), dtype=np.float32)
     wr *= np.float32(1.0 / math.sqrt(p.H))
+    return wr, expert_bias(p)
+
+
+def make_routing(p: Problem, x_bits: np.ndarray, chunk: int = 2048):
+    """(topk_ids int32 [T][k], topk_w float32 [T][k]) from the seeded router."""
+    wr, bias = router_weights(p)
     wr64 = wr.astype(np.float64)
-    bias = expert_bias(p)
     ids = np.empty((p.T, p.k), np.int32)
     w = np.empty((p.T, p.k), np.float32)
     for t0 in range(0, p.T, chunk):
