@@ -218,6 +218,37 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
 mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K,
                               uint8_t* q, uint8_t* scales, void* stream);
 
+/* ---------------------------------------------------------------- router
+ * Router front end ([MoK clip] key chart: "Router picks top-k", upstream of
+ * the layer; the pages give no formula, this is the plainest reading):
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h]   (fp32, fixed order)
+ *   score = logit + bias[e] (bias optional, NULL = none; it moves the
+ *   selection only), topk_ids[t] = the k largest scores in descending
+ *   order, equal scores in ascending expert id, and
+ *   topk_w[t][j] = softmax over the k selected (unbiased) logits, fp32.
+ * x [T][H] bf16, w_router [E][H] fp32 (device), bias [E] fp32 or NULL;
+ * outputs topk_ids [T][k] int32 and topk_w [T][k] fp32, overwritten.
+ * Requires k <= 64 and H <= 9216 (the 8 tokens of a workgroup's rows and
+ * logits stay in LDS): MOK_ERR_UNSUPPORTED otherwise. NaN logits are not
+ * supported. */
+mok_status mok_router_forward(const mok_problem* problem, const void* x, const float* w_router,
+                              const float* bias, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Router backward from g = d topk_w [T][k] (fp32): the selection is held
+ * fixed, so only the selected logits get gradient, through the softmax:
+ *   d_sel[t][j] = w_j * (g_j - sum_i w_i g_i)               [T][k] fp32
+ *   dx[t] = sum_j d_sel[t][j] * w_router[topk_ids[t][j]]     [T][H] bf16
+ *   d_w_router[e] = sum over the rows routed to e of d_sel * x[t]   [E][H] fp32
+ * (the caller adds dx to the layer's dx). schedule is the one built by
+ * mok_build_schedule for these topk_ids (its permutation orders the dWr
+ * sums: each expert's rows in 4 fixed interleaved groups of ascending rows,
+ * added in group order; an expert with no rows gets exact zeros). Ids
+ * outside [0, E) contribute nothing. All outputs are overwritten. */
+mok_status mok_router_backward(const mok_problem* problem, const mok_config* config, const void* schedule,
+                               const void* x, const float* w_router, const int32_t* topk_ids,
+                               const float* topk_w, const float* d_topk_w, float* d_sel, void* dx,
+                               float* d_w_router, void* stream);
+
 /* ---------------------------------------------------------------- tracing
  * Per-kernel timing for profiling ([MoK clip] How-to item 1: profile first to
  * see where the layer's time goes). While tracing is on, every kernel the

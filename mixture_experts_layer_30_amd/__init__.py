@@ -64,7 +64,7 @@ _lib = None
 
 EXPORTS = ("mok_version", "mok_status_string", "mok_buffer_sizes", "mok_get_schedule_layout",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
-           "mok_trace_enable", "mok_trace_collect")
+           "mok_router_forward", "mok_router_backward", "mok_trace_enable", "mok_trace_collect")
 
 
 class TraceStat(ctypes.Structure):
@@ -99,6 +99,10 @@ def lib():
                                    vp, vp, vp, vp, vp, sz, vp]
         L.mok_mxfp8_quantize.restype = ctypes.c_int
         L.mok_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+        L.mok_router_forward.restype = ctypes.c_int
+        L.mok_router_forward.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
+        L.mok_router_backward.restype = ctypes.c_int
+        L.mok_router_backward.argtypes = [P(Problem), P(Config), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.mok_trace_enable.restype = ctypes.c_int
         L.mok_trace_enable.argtypes = [ctypes.c_int32]
         L.mok_trace_collect.restype = ctypes.c_int
@@ -199,6 +203,23 @@ def mxfp8_quantize(src, q, scales, stream=None):
     _check(lib().mok_mxfp8_quantize(_ptr(src), int(rows) if src.dim() == 2 else int(src.numel() // K),
                                     int(K), _ptr(q), _ptr(scales), _stream(stream)),
            "mok_mxfp8_quantize")
+
+
+def router_forward(problem, x, w_router, bias, topk_ids, topk_w, stream=None):
+    """x [T][H] bf16, w_router [E][H] fp32, bias [E] fp32 or None -> topk_ids [T][k] int32,
+    topk_w [T][k] fp32 (overwritten)."""
+    _check(lib().mok_router_forward(ctypes.byref(problem), _ptr(x), _ptr(w_router), _ptr(bias),
+                                    _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "mok_router_forward")
+
+
+def router_backward(problem, schedule, x, w_router, topk_ids, topk_w, d_topk_w, d_sel, dx, d_w_router,
+                    config=None, stream=None):
+    """-> d_sel [T][k] fp32, dx [T][H] bf16, d_w_router [E][H] fp32 (overwritten); schedule built
+    by build_schedule for these topk_ids."""
+    _check(lib().mok_router_backward(ctypes.byref(problem), _cfg(config), _ptr(schedule), _ptr(x),
+                                     _ptr(w_router), _ptr(topk_ids), _ptr(topk_w), _ptr(d_topk_w),
+                                     _ptr(d_sel), _ptr(dx), _ptr(d_w_router), _stream(stream)),
+           "mok_router_backward")
 
 
 def trace_enable(on=True):

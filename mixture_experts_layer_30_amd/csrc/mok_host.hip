@@ -547,6 +547,43 @@ mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K, uint8_t*
   return MOK_OK;
 }
 
+// [MoK clip] key chart "Router picks top-k" (reading stated in include/mok.h)
+mok_status mok_router_forward(const mok_problem* problem, const void* x, const float* w_router,
+                              const float* bias, int32_t* topk_ids, float* topk_w, void* stream) {
+  TraceCall tc;
+  Resolved r;
+  mok_status s = resolve(problem, nullptr, &r);
+  if (s != MOK_OK) return s;
+  if (r.T > 0 && (!x || !w_router || !topk_ids || !topk_w)) return MOK_ERR_INVALID_ARG;
+  if (r.k > 64 || mok_router_lds_bytes((int)r.H, r.E) > 160 * 1024) return MOK_ERR_UNSUPPORTED;
+  if ((s = check_device()) != MOK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN("router_forward", mok_launch_router_forward(static_cast<const bf16_t*>(x), w_router, bias, r.T,
+                                                      (int)r.H, r.E, r.k, topk_ids, topk_w, st));
+  return MOK_OK;
+}
+
+mok_status mok_router_backward(const mok_problem* problem, const mok_config* config, const void* schedule,
+                               const void* x, const float* w_router, const int32_t* topk_ids,
+                               const float* topk_w, const float* d_topk_w, float* d_sel, void* dx,
+                               float* d_w_router, void* stream) {
+  TraceCall tc;
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || !d_w_router) return MOK_ERR_INVALID_ARG;
+  if (r.T > 0 && (!x || !w_router || !topk_ids || !topk_w || !d_topk_w || !d_sel || !dx))
+    return MOK_ERR_INVALID_ARG;
+  if ((s = check_device()) != MOK_OK) return s;
+  const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN("router_backward", mok_launch_router_backward(static_cast<const bf16_t*>(x), w_router, topk_ids,
+                                                        topk_w, d_topk_w, r.T, (int)r.H, r.E, r.k, sp.offsets,
+                                                        sp.perm, sp.tok, d_sel, static_cast<bf16_t*>(dx),
+                                                        d_w_router, st));
+  return MOK_OK;
+}
+
 mok_status mok_trace_enable(int32_t on) {
   std::lock_guard<std::mutex> g(g_tr.mu);
   g_tr.on = on != 0;

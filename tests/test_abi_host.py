@@ -130,3 +130,23 @@ def test_calls_reject_bad_arguments_before_any_launch():
     assert L.mok_mxfp8_quantize(fake, 4, 48, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_mxfp8_quantize(fake, -1, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_mxfp8_quantize(None, 4, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
+
+
+def test_router_calls_reject_bad_arguments():
+    L = mok.lib()
+    fake = ctypes.c_void_p(0x1000)
+    prob = P()
+    assert L.mok_router_forward(ctypes.byref(prob), None, fake, None, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_router_forward(ctypes.byref(prob), fake, fake, None, fake, None, None) == mok.MOK_ERR_INVALID_ARG
+    assert L.mok_router_forward(None, fake, fake, None, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
+    # x rows of 8 tokens plus 8 logit rows must fit the workgroup's 160 KiB of LDS
+    big = mok.make_problem(16, 10240, 128, 8, 2)
+    assert L.mok_router_forward(ctypes.byref(big), fake, fake, None, fake, fake, None) == mok.MOK_ERR_UNSUPPORTED
+    assert L.mok_router_forward(ctypes.byref(mok.make_problem(16, 256, 128, 128, 65)), fake, fake, None, fake,
+                                fake, None) == mok.MOK_ERR_UNSUPPORTED
+    args = [fake] * 9
+    assert L.mok_router_backward(ctypes.byref(prob), None, None, *args[:8], None) == mok.MOK_ERR_INVALID_ARG
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        assert L.mok_router_backward(ctypes.byref(prob), None, *a, None) == mok.MOK_ERR_INVALID_ARG, i
