@@ -253,7 +253,7 @@ def main():
 
     import mixture_experts_layer_30_amd as mok
     from mixture_experts_layer_30_amd import functional as F
-    from synthetic import CONFIGS, make_all_experts, make_dy, make_routing, make_x
+    from synthetic import CONFIGS, make_all_experts, make_dy, make_routing, make_x, router_weights
 
     assert torch.cuda.is_available(), "no GPU visible"
     p = CONFIGS[args.config]
@@ -312,7 +312,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     ms_step, stats = timed(step, args.steps, trace=True)
-    ms_fwd = ms_mx = ms_mxs = ms_wq = None
+    ms_fwd = ms_mx = ms_mxs = ms_wq = ms_rf = ms_rb = None
     mxstats = mxsstats = {}
     if not args.only_step:
         log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
@@ -356,6 +356,32 @@ def main():
         ms_wq, _ = timed(lambda: (F.quantize_weights(*weights), F.quantize_weights_backward(*weights)), 3,
                          trace=False)
         del wst
+
+        # router front end on the same tokens (outside the layer step: the
+        # layer takes topk_ids / topk_w as inputs)
+        log("[bench] router timing")
+        wr, rbias = router_weights(p)
+        dwr = torch.from_numpy(np.ascontiguousarray(wr.T)).cuda()
+        drb = torch.from_numpy(np.where(np.isfinite(rbias), rbias, -1e30).astype(np.float32)).cuda()
+        rids, rw = torch.empty_like(dids), torch.empty_like(dw_)
+        rsel, rgw = torch.empty_like(dw_), torch.empty_like(dwr)
+        rg = torch.from_numpy(np.random.default_rng(p.seed + 11).standard_normal((p.T, p.k)).astype(np.float32)).cuda()
+
+        def router_fwd():
+            mok.router_forward(ws.problem, dx_, dwr, drb, rids, rw, stream)
+
+        def router_bwd():
+            mok.router_backward(ws.problem, ws.schedule, dx_, dwr, rids, rw, rg, rsel, gx, rgw, ws.config, stream)
+
+        router_fwd()
+        mok.build_schedule(ws.problem, rids, ws.schedule, ws.config, stream)
+        router_bwd()
+        # GPU time per call from the per-launch HIP events (back-to-back calls
+        # of a ~10 us kernel are bound by the host's enqueue rate otherwise)
+        _, rfstats = timed(router_fwd, args.steps, trace=True)
+        _, rstats = timed(router_bwd, args.steps, trace=True)
+        ms_rf = rfstats["router_forward"][1] / rfstats["router_forward"][0]
+        ms_rb = rstats["router_backward"][1] / rstats["router_backward"][0]
 
     R, H, I = p.R, p.H, p.I
     flops_step = p.fwd_flops() + p.bwd_flops()
@@ -444,6 +470,20 @@ def main():
                             for k, v in mxsstats.items() if k in GEMM_FLOPS_PER_ROW},
             "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in mxsstats.items()},
             "weight_quantize_ms": round(ms_wq, 4),
+        }
+    if ms_rf is not None:
+        # algorithmic bytes: forward reads x and Wr once and writes ids, w;
+        # backward reads ids, w, d topk_w, Wr and x, writes d_sel, dx, dWr
+        # (d_sel read back once by the dWr pass)
+        b_f = p.T * 2 * H + p.E * H * 4 + p.T * p.k * 8
+        b_b = 2 * p.T * 2 * H + 2 * p.E * H * 4 + p.T * p.k * 20
+        out["router"] = {
+            "forward_ms": round(ms_rf, 4), "backward_ms": round(ms_rb, 4),
+            "forward_gbs": round(b_f / (ms_rf * 1e-3) / 1e9, 1),
+            "backward_gbs": round(b_b / (ms_rb * 1e-3) / 1e9, 1),
+            "forward_bytes": b_f, "backward_bytes": b_b,
+            "logit_tflops": round(2 * p.T * p.E * H / (ms_rf * 1e-3) / 1e12, 3),
+            "timing": "HIP events around each call on the launch stream (mok_trace), averaged over the calls",
         }
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")

@@ -221,16 +221,17 @@ mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K,
 /* ---------------------------------------------------------------- router
  * Router front end ([MoK clip] key chart: "Router picks top-k", upstream of
  * the layer; the pages give no formula, this is the plainest reading):
- *   logits[t][e] = sum_h x[t][h] * w_router[e][h]   (fp32, fixed order)
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h]   (fp32, fixed order:
+ *   on the matrix cores, with w_router split exactly into three bf16 parts
+ *   so that every product is exact)
  *   score = logit + bias[e] (bias optional, NULL = none; it moves the
  *   selection only), topk_ids[t] = the k largest scores in descending
  *   order, equal scores in ascending expert id, and
  *   topk_w[t][j] = softmax over the k selected (unbiased) logits, fp32.
  * x [T][H] bf16, w_router [E][H] fp32 (device), bias [E] fp32 or NULL;
  * outputs topk_ids [T][k] int32 and topk_w [T][k] fp32, overwritten.
- * Requires k <= 64 and H <= 9216 (the 8 tokens of a workgroup's rows and
- * logits stay in LDS): MOK_ERR_UNSUPPORTED otherwise. NaN logits are not
- * supported. */
+ * Requires k <= 64 (one wavefront holds the picks): MOK_ERR_UNSUPPORTED
+ * otherwise. NaN logits are not supported. */
 mok_status mok_router_forward(const mok_problem* problem, const void* x, const float* w_router,
                               const float* bias, int32_t* topk_ids, float* topk_w, void* stream);
 

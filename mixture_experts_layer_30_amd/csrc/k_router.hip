@@ -17,8 +17,10 @@
 
 namespace {
 
-constexpr int kRouterTokens = 8;                 // tokens per forward workgroup
+constexpr int kRouterTokens = 32;                // tokens per forward workgroup (one MFMA row tile)
 constexpr int kRouterThreads = 256;
+constexpr int kRouterMaxE = 512;
+constexpr int kRouterGroup = 128;                // experts per accumulation group (4 column tiles)
 
 MOK_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOK_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -26,53 +28,103 @@ MOK_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // (score, expert) a beats b: higher score, or equal score and lower id
 MOK_DEV bool beats(float sa, int ea, float sb, int eb) { return sa > sb || (sa == sb && ea < eb); }
 
-// Forward: one workgroup per 8 tokens. The tokens' x rows sit in LDS; for
-// each expert, thread (token = tid / 32, slice = tid % 32) sums its 8-wide
-// chunks c = slice, slice + 32, ... in ascending order and the 32 slices are
-// combined by a xor butterfly (a fixed tree), so every logit is a fixed
-// function of its inputs. Then each wavefront selects the top-k of two
+// Exact three-way split of fp32 values into bf16: w = hi + mid + lo, each
+// part the truncation of what remains (8 significant bits each, 24 in all),
+// so x * part is exact in fp32 for bf16 x and the MFMA sums exact products.
+// Pairs are packed two bf16 per dword (element 2i in the low half).
+MOK_DEV void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t u0 = __float_as_uint(w0), u1 = __float_as_uint(w1);
+  const float r0 = w0 - __uint_as_float(u0 & 0xFFFF0000u), r1 = w1 - __uint_as_float(u1 & 0xFFFF0000u);
+  const uint32_t v0 = __float_as_uint(r0), v1 = __float_as_uint(r1);
+  const float q0 = r0 - __uint_as_float(v0 & 0xFFFF0000u), q1 = r1 - __uint_as_float(v1 & 0xFFFF0000u);
+  hi = (u0 >> 16) | (u1 & 0xFFFF0000u);
+  mid = (v0 >> 16) | (v1 & 0xFFFF0000u);
+  lo = (__float_as_uint(q0) >> 16) | (__float_as_uint(q1) & 0xFFFF0000u);
+}
+
+// Forward: one workgroup per 32 tokens. The logits x . Wr^T are a dense
+// contraction (32 token rows x E expert columns x H), done on the matrix
+// cores with v_mfma_f32_32x32x16_bf16: x is bf16 already and Wr is split
+// exactly into three bf16 parts, so every product is exact and the fp32
+// sums run in the MFMA's fixed order. Wave v sums K = [vH/4, (v+1)H/4) for
+// up to 128 experts at a time; the four partial sums are added in the order
+// v = 0..3 through LDS. Then each wavefront selects the top-k of eight
 // tokens: lane l holds experts l, l + 64, ...; each of k rounds takes the
-// best unselected pair (score, expert) of the wavefront.
+// best unselected (score, expert) pair of the wavefront.
 __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                           // [8][H]
-  float* lg = reinterpret_cast<float*>(smem + (size_t)kRouterTokens * H * 2);   // [8][E]
+  __shared__ float lg[kRouterTokens * kRouterMaxE];                       // [32][E] logits
+  __shared__ float part[3][kRouterTokens * kRouterGroup];                 // waves 1..3 partials
   const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
-  const int nch = H / 8;                                                  // 16-byte chunks per row
-  for (int i = threadIdx.x; i < kRouterTokens * nch; i += kRouterThreads) {
-    const int tk = i / nch, c = i % nch;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (t0 + tk < T) v = reinterpret_cast<const uint4*>(x + (t0 + tk) * H)[c];
-    reinterpret_cast<uint4*>(xs + (int64_t)tk * H)[c] = v;
-  }
-  __syncthreads();
-  const int tk = threadIdx.x >> 5, sl = threadIdx.x & 31;
-  const uint4* xrow = reinterpret_cast<const uint4*>(xs + (int64_t)tk * H);
-  for (int e = 0; e < E; ++e) {
-    const float4* wrow = reinterpret_cast<const float4*>(wr + (int64_t)e * H);
-    float acc = 0.f;
-    for (int c = sl; c < nch; c += 32) {
-      const uint4 xv = xrow[c];
-      const float4 a = wrow[2 * c], b = wrow[2 * c + 1];
-      acc = fmaf(bf16_lo(xv.x), a.x, acc);
-      acc = fmaf(bf16_hi(xv.x), a.y, acc);
-      acc = fmaf(bf16_lo(xv.y), a.z, acc);
-      acc = fmaf(bf16_hi(xv.y), a.w, acc);
-      acc = fmaf(bf16_lo(xv.z), b.x, acc);
-      acc = fmaf(bf16_hi(xv.z), b.y, acc);
-      acc = fmaf(bf16_lo(xv.w), b.z, acc);
-      acc = fmaf(bf16_hi(xv.w), b.w, acc);
-    }
+  const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
+  const int r32 = lane & 31, kh = 8 * (lane >> 5);
+  const int kq = H / 4, kbeg = v * kq;
+  const bool trow = t0 + r32 < T;
+  const bf16_t* xrow = x + (t0 + (trow ? r32 : 0)) * H + kh;
+  for (int g0 = 0; g0 < E; g0 += kRouterGroup) {
+    const int nb = min(4, (E - g0 + 31) / 32);                           // column tiles in this group
+    f32x16_t acc[4];
 #pragma unroll
-    for (int s = 16; s >= 1; s >>= 1) acc += __shfl_xor(acc, s);
-    if (sl == 0) lg[tk * E + e] = acc;
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[b][q] = 0.f;
+    for (int kk = kbeg; kk < kbeg + kq; kk += 16) {
+      uint4 xa = make_uint4(0u, 0u, 0u, 0u);
+      if (trow) xa = *reinterpret_cast<const uint4*>(xrow + kk);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nb) break;
+        const int e = g0 + 32 * b + r32;
+        float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
+        if (e < E) {
+          const float4* src = reinterpret_cast<const float4*>(wr + (int64_t)e * H + kk + kh);
+          p = src[0];
+          q = src[1];
+        }
+        uint4 hi, mid, lo;
+        split3(p.x, p.y, hi.x, mid.x, lo.x);
+        split3(p.z, p.w, hi.y, mid.y, lo.y);
+        split3(q.x, q.y, hi.z, mid.z, lo.z);
+        split3(q.z, q.w, hi.w, mid.w, lo.w);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
+      }
+    }
+    // accumulator element q: token row 8(q/4) + 4(lane/32) + q%4, expert column lane%32
+    if (v > 0) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nb) break;
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          part[v - 1][(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * kRouterGroup + 32 * b + r32] = acc[b][q];
+      }
+    }
+    __syncthreads();
+    if (v == 0) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nb) break;
+        const int e = g0 + 32 * b + r32;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          const int pi = row * kRouterGroup + 32 * b + r32;
+          float s = acc[b][q];
+          s += part[0][pi];
+          s += part[1][pi];
+          s += part[2][pi];
+          if (e < E) lg[row * E + e] = s;
+        }
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  const int wv = threadIdx.x >> 6, lane = lane_id();
-  for (int q = 0; q < 2; ++q) {
-    const int tt = 2 * wv + q;
+  for (int q = 0; q < kRouterTokens / 4; ++q) {
+    const int tt = (kRouterTokens / 4) * v + q;
     const int64_t t = t0 + tt;
     if (t >= T) break;
     uint64_t taken = 0;                          // bit i: expert lane + 64 i selected
@@ -145,8 +197,10 @@ __global__ __launch_bounds__(256) void router_bwd_rows_kernel(
 // x[tok[p]][h], fp32. Workgroup (e, 512 columns): wavefront v sums the rows
 // p = o_e + v, o_e + v + 4, ... in ascending order (8 columns per lane), then
 // the four partial sums are added in the order v = 0..3: a fixed partition
-// of the expert's rows, so the result is bitwise reproducible. Experts with
-// no rows get exact zeros.
+// of the expert's rows, so the result is bitwise reproducible. Each
+// wavefront first loads the (d_sel, token) pairs of its next 64 rows, one
+// per lane, then walks them in order, so the x row loads do not wait on the
+// table loads. Experts with no rows get exact zeros.
 __global__ __launch_bounds__(256) void router_dwr_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ d_sel, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tok, int H, int ncol,
@@ -157,17 +211,28 @@ __global__ __launch_bounds__(256) void router_dwr_kernel(
   const int col = cb * 512 + 8 * lane;
   const bool ok = col < H;
   const int o = offsets[e], n = offsets[e + 1] - o;
+  const int nv = n > v ? (n - v + 3) / 4 : 0;    // rows of this wavefront
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r = v; r < n; r += 4) {
-    const int p = o + r;
-    const float dl = d_sel[perm[p]];             // wave-uniform loads
-    const int64_t tr = tok[p];
-    if (!ok) continue;
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + tr * H + col);
-    acc[0] = fmaf(dl, bf16_lo(xv.x), acc[0]); acc[1] = fmaf(dl, bf16_hi(xv.x), acc[1]);
-    acc[2] = fmaf(dl, bf16_lo(xv.y), acc[2]); acc[3] = fmaf(dl, bf16_hi(xv.y), acc[3]);
-    acc[4] = fmaf(dl, bf16_lo(xv.z), acc[4]); acc[5] = fmaf(dl, bf16_hi(xv.z), acc[5]);
-    acc[6] = fmaf(dl, bf16_lo(xv.w), acc[6]); acc[7] = fmaf(dl, bf16_hi(xv.w), acc[7]);
+  for (int base = 0; base < nv; base += 64) {
+    float dl_l = 0.f;
+    int tr_l = 0;
+    if (base + lane < nv) {
+      const int p = o + v + 4 * (base + lane);
+      dl_l = d_sel[perm[p]];
+      tr_l = tok[p];
+    }
+    const int cnt = min(64, nv - base);
+#pragma unroll 8
+    for (int i = 0; i < cnt; ++i) {
+      const float dl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dl_l), i));
+      const int64_t tr = __builtin_amdgcn_readlane(tr_l, i);
+      if (!ok) continue;
+      const uint4 xv = *reinterpret_cast<const uint4*>(x + tr * H + col);
+      acc[0] = fmaf(dl, bf16_lo(xv.x), acc[0]); acc[1] = fmaf(dl, bf16_hi(xv.x), acc[1]);
+      acc[2] = fmaf(dl, bf16_lo(xv.y), acc[2]); acc[3] = fmaf(dl, bf16_hi(xv.y), acc[3]);
+      acc[4] = fmaf(dl, bf16_lo(xv.z), acc[4]); acc[5] = fmaf(dl, bf16_hi(xv.z), acc[5]);
+      acc[6] = fmaf(dl, bf16_lo(xv.w), acc[6]); acc[7] = fmaf(dl, bf16_hi(xv.w), acc[7]);
+    }
   }
   if (v > 0) {
 #pragma unroll
@@ -192,16 +257,11 @@ __global__ __launch_bounds__(256) void router_dwr_kernel(
 
 }  // namespace
 
-size_t mok_router_lds_bytes(int H, int E) {
-  return (size_t)kRouterTokens * H * 2 + (size_t)kRouterTokens * E * 4;
-}
-
 hipError_t mok_launch_router_forward(const bf16_t* x, const float* wr, const float* bias, int64_t T, int H,
                                      int E, int k, int32_t* ids, float* w, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((T + kRouterTokens - 1) / kRouterTokens);
-  hipLaunchKernelGGL(router_fwd_kernel, dim3(grid), dim3(kRouterThreads), mok_router_lds_bytes(H, E), st, x, wr,
-                     bias, T, H, E, k, ids, w);
+  hipLaunchKernelGGL(router_fwd_kernel, dim3(grid), dim3(kRouterThreads), 0, st, x, wr, bias, T, H, E, k, ids, w);
   return hipGetLastError();
 }
 

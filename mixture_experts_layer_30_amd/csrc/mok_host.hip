@@ -555,7 +555,7 @@ mok_status mok_router_forward(const mok_problem* problem, const void* x, const f
   mok_status s = resolve(problem, nullptr, &r);
   if (s != MOK_OK) return s;
   if (r.T > 0 && (!x || !w_router || !topk_ids || !topk_w)) return MOK_ERR_INVALID_ARG;
-  if (r.k > 64 || mok_router_lds_bytes((int)r.H, r.E) > 160 * 1024) return MOK_ERR_UNSUPPORTED;
+  if (r.k > 64) return MOK_ERR_UNSUPPORTED;
   if ((s = check_device()) != MOK_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   MOK_RUN("router_forward", mok_launch_router_forward(static_cast<const bf16_t*>(x), w_router, bias, r.T,

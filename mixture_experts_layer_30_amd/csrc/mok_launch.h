@@ -164,7 +164,6 @@ inline int mok_token_blocks(int64_t R, int E) { return (int)((R + 128 * (int64_t
 hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int64_t R, int32_t* koff, hipStream_t st);
 
 // ---------------------------------------------------------------- router
-size_t mok_router_lds_bytes(int H, int E);
 hipError_t mok_launch_router_forward(const bf16_t* x, const float* wr, const float* bias, int64_t T, int H,
                                      int E, int k, int32_t* ids, float* w, hipStream_t st);
 hipError_t mok_launch_router_backward(const bf16_t* x, const float* wr, const int32_t* ids, const float* w,
