@@ -17,8 +17,9 @@
 
 namespace {
 
-constexpr int kRouterTokens = 32;                // tokens per forward workgroup (one MFMA row tile)
-constexpr int kRouterThreads = 256;
+constexpr int kRouterTokens = 16;                // tokens per forward workgroup (rows 0..15 of the MFMA tile)
+constexpr int kRouterWaves = 8;                  // K split across the workgroup's wavefronts
+constexpr int kRouterThreads = 64 * kRouterWaves;
 constexpr int kRouterMaxE = 512;
 constexpr int kRouterGroup = 128;                // experts per accumulation group (4 column tiles)
 
@@ -42,26 +43,30 @@ MOK_DEV void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& l
   lo = (__float_as_uint(q0) >> 16) | (__float_as_uint(q1) & 0xFFFF0000u);
 }
 
-// Forward: one workgroup per 32 tokens. The logits x . Wr^T are a dense
-// contraction (32 token rows x E expert columns x H), done on the matrix
-// cores with v_mfma_f32_32x32x16_bf16: x is bf16 already and Wr is split
-// exactly into three bf16 parts, so every product is exact and the fp32
-// sums run in the MFMA's fixed order. Wave v sums K = [vH/4, (v+1)H/4) for
-// up to 128 experts at a time; the four partial sums are added in the order
-// v = 0..3 through LDS. Then each wavefront selects the top-k of eight
-// tokens: lane l holds experts l, l + 64, ...; each of k rounds takes the
-// best unselected (score, expert) pair of the wavefront.
+// Forward: one workgroup per 16 tokens. The logits x . Wr^T are a dense
+// contraction (token rows x E expert columns x H), done on the matrix cores
+// with v_mfma_f32_32x32x16_bf16 (rows 16..31 of its tile unused: 16-token
+// workgroups put every CU to work at T = 4096): x is bf16 already and Wr is
+// split exactly into three bf16 parts, so every product is exact and the
+// fp32 sums run in the MFMA's fixed order. Wave v sums K = [vH/8, (v+1)H/8)
+// for up to 128 experts at a time; the eight partial sums are added in the
+// order v = 0..7 through LDS. Then each wavefront selects the top-k of two
+// tokens: with E <= 64 by ranking each lane's expert against all others;
+// otherwise lane l holds experts l, l + 64, ... and each of k rounds takes
+// the best unselected (score, expert) pair of the wavefront.
 __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ float lg[kRouterTokens * kRouterMaxE];                       // [32][E] logits
-  __shared__ float part[3][kRouterTokens * kRouterGroup];                 // waves 1..3 partials
+  __shared__ float part[kRouterWaves - 1][kRouterTokens * kRouterGroup];  // waves 1..7 partials
+  __shared__ float bsh[kRouterMaxE];                                      // bias (0 if none)
   const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
   const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
   const int r32 = lane & 31, kh = 8 * (lane >> 5);
-  const int kq = H / 4, kbeg = v * kq;
-  const bool trow = t0 + r32 < T;
-  const bf16_t* xrow = x + (t0 + (trow ? r32 : 0)) * H + kh;
+  const int kq = H / kRouterWaves, kbeg = v * kq, kend = kbeg + kq;
+  const bool trow = r32 < kRouterTokens && t0 + r32 < T;
+  const bf16_t* xrow = x + (t0 + (trow ? r32 : 0)) * H + kh;   // row t0 exists: t0 < T
+  for (int e = threadIdx.x; e < E; e += kRouterThreads) bsh[e] = bias ? bias[e] : 0.f;
   for (int g0 = 0; g0 < E; g0 += kRouterGroup) {
     const int nb = min(4, (E - g0 + 31) / 32);                           // column tiles in this group
     f32x16_t acc[4];
@@ -69,37 +74,57 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[b][q] = 0.f;
-    for (int kk = kbeg; kk < kbeg + kq; kk += 16) {
-      uint4 xa = make_uint4(0u, 0u, 0u, 0u);
-      if (trow) xa = *reinterpret_cast<const uint4*>(xrow + kk);
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa);
+    // batches of up to 4 K steps: every load of a batch is issued before
+    // its first MFMA
+    for (int kk = kbeg; kk < kend; kk += 64) {
+      const int nu = min(4, (kend - kk) / 16);
+      uint4 xa[4];
+      float4 wv[4][4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (u < nu && trow) xa[u] = *reinterpret_cast<const uint4*>(xrow + kk + 16 * u);
+      }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        if (b >= nb) break;
         const int e = g0 + 32 * b + r32;
-        float4 p = make_float4(0.f, 0.f, 0.f, 0.f), q = p;
-        if (e < E) {
-          const float4* src = reinterpret_cast<const float4*>(wr + (int64_t)e * H + kk + kh);
-          p = src[0];
-          q = src[1];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wv[b][u][0] = wv[b][u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (b < nb && u < nu && e < E) {
+            const float4* src = reinterpret_cast<const float4*>(wr + (int64_t)e * H + kk + 16 * u + kh);
+            wv[b][u][0] = src[0];
+            wv[b][u][1] = src[1];
+          }
         }
-        uint4 hi, mid, lo;
-        split3(p.x, p.y, hi.x, mid.x, lo.x);
-        split3(p.z, p.w, hi.y, mid.y, lo.y);
-        split3(q.x, q.y, hi.z, mid.z, lo.z);
-        split3(q.z, q.w, hi.w, mid.w, lo.w);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u >= nu) break;
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[u]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b >= nb) break;
+          const float4 p = wv[b][u][0], q = wv[b][u][1];
+          uint4 hi, mid, lo;
+          split3(p.x, p.y, hi.x, mid.x, lo.x);
+          split3(p.z, p.w, hi.y, mid.y, lo.y);
+          split3(q.x, q.y, hi.z, mid.z, lo.z);
+          split3(q.z, q.w, hi.w, mid.w, lo.w);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
+        }
       }
     }
-    // accumulator element q: token row 8(q/4) + 4(lane/32) + q%4, expert column lane%32
+    // accumulator element q: token row 8(q/4) + 4(lane/32) + q%4, expert
+    // column lane%32; rows 0..15 are q = 0..7
     if (v > 0) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b >= nb) break;
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
+        for (int q = 0; q < 8; ++q)
           part[v - 1][(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * kRouterGroup + 32 * b + r32] = acc[b][q];
       }
     }
@@ -110,21 +135,47 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
         if (b >= nb) break;
         const int e = g0 + 32 * b + r32;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < 8; ++q) {
           const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
           const int pi = row * kRouterGroup + 32 * b + r32;
           float s = acc[b][q];
-          s += part[0][pi];
-          s += part[1][pi];
-          s += part[2][pi];
+          for (int i = 0; i < kRouterWaves - 1; ++i) s += part[i][pi];
           if (e < E) lg[row * E + e] = s;
         }
       }
     }
     __syncthreads();
   }
-  for (int q = 0; q < kRouterTokens / 4; ++q) {
-    const int tt = (kRouterTokens / 4) * v + q;
+  if (E <= 64) {
+    // one expert per lane: its rank is the number of experts that beat it
+    // (LDS broadcast reads, no cross-lane traffic); the k lanes of rank < k
+    // write their own slot. The softmax runs over the selected experts in
+    // ascending id, the same order in every lane.
+    for (int q = 0; q < kRouterTokens / kRouterWaves; ++q) {
+      const int tt = (kRouterTokens / kRouterWaves) * v + q;
+      const int64_t t = t0 + tt;
+      if (t >= T) break;
+      const float* row = lg + tt * E;
+      const int e = lane < E ? lane : 0;
+      const float me = row[e] + bsh[e];
+      int rank = 0;
+#pragma unroll 8
+      for (int e2 = 0; e2 < E; ++e2) rank += beats(row[e2] + bsh[e2], e2, me, e) ? 1 : 0;
+      const bool sel = lane < E && rank < k;
+      uint64_t msk = __ballot(sel);
+      float m = -INFINITY;
+      for (uint64_t r = msk; r; r &= r - 1) m = fmaxf(m, row[__builtin_ctzll(r)]);
+      float den = 0.f;
+      for (uint64_t r = msk; r; r &= r - 1) den += expf(row[__builtin_ctzll(r)] - m);
+      if (sel) {
+        ids[t * k + rank] = lane;
+        w[t * k + rank] = expf(row[lane] - m) / den;
+      }
+    }
+    return;
+  }
+  for (int q = 0; q < kRouterTokens / kRouterWaves; ++q) {
+    const int tt = (kRouterTokens / kRouterWaves) * v + q;
     const int64_t t = t0 + tt;
     if (t >= T) break;
     uint64_t taken = 0;                          // bit i: expert lane + 64 i selected
@@ -137,7 +188,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
       for (int i = 0; lane + 64 * i < E; ++i) {
         const int e = lane + 64 * i;
         if ((taken >> i) & 1) continue;
-        const float s = lg[tt * E + e] + (bias ? bias[e] : 0.f);
+        const float s = lg[tt * E + e] + bsh[e];
         if (be == 0x7FFFFFFF || beats(s, e, bs, be)) { bs = s; be = e; }
       }
 #pragma unroll
@@ -194,35 +245,36 @@ __global__ __launch_bounds__(256) void router_bwd_rows_kernel(
 }
 
 // dWr[e][h] = sum over the permuted rows p of expert e of d_sel[perm[p]] *
-// x[tok[p]][h], fp32. Workgroup (e, 512 columns): wavefront v sums the rows
-// p = o_e + v, o_e + v + 4, ... in ascending order (8 columns per lane), then
-// the four partial sums are added in the order v = 0..3: a fixed partition
-// of the expert's rows, so the result is bitwise reproducible. Each
-// wavefront first loads the (d_sel, token) pairs of its next 64 rows, one
-// per lane, then walks them in order, so the x row loads do not wait on the
-// table loads. Experts with no rows get exact zeros.
-__global__ __launch_bounds__(256) void router_dwr_kernel(
+// x[tok[p]][h], fp32. Workgroup (e, 512 columns) of 16 wavefronts:
+// wavefront v sums the rows p = o_e + v, o_e + v + 16, ... in ascending
+// order (8 columns per lane), then the 16 partial sums are added in the
+// order v = 0..15: a fixed partition of the expert's rows, so the result is
+// bitwise reproducible. Each wavefront first loads the (d_sel, token) pairs
+// of its next 64 rows, one per lane, then walks them in order, so the x row
+// loads do not wait on the table loads. Experts with no rows get exact zeros.
+constexpr int kDwrWaves = 16;
+__global__ __launch_bounds__(64 * kDwrWaves) void router_dwr_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ d_sel, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ tok, int H, int ncol,
     float* __restrict__ d_wr) {
-  __shared__ float part[3][512];
+  __shared__ float part[kDwrWaves - 1][512];
   const int e = (int)blockIdx.x / ncol, cb = (int)blockIdx.x % ncol;
   const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
   const int col = cb * 512 + 8 * lane;
   const bool ok = col < H;
   const int o = offsets[e], n = offsets[e + 1] - o;
-  const int nv = n > v ? (n - v + 3) / 4 : 0;    // rows of this wavefront
+  const int nv = n > v ? (n - v + kDwrWaves - 1) / kDwrWaves : 0;      // rows of this wavefront
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < nv; base += 64) {
     float dl_l = 0.f;
     int tr_l = 0;
     if (base + lane < nv) {
-      const int p = o + v + 4 * (base + lane);
+      const int p = o + v + kDwrWaves * (base + lane);
       dl_l = d_sel[perm[p]];
       tr_l = tok[p];
     }
     const int cnt = min(64, nv - base);
-#pragma unroll 8
+#pragma unroll 16
     for (int i = 0; i < cnt; ++i) {
       const float dl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dl_l), i));
       const int64_t tr = __builtin_amdgcn_readlane(tr_l, i);
@@ -244,9 +296,7 @@ __global__ __launch_bounds__(256) void router_dwr_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       float s = acc[u];
-      s += part[0][8 * lane + u];
-      s += part[1][8 * lane + u];
-      s += part[2][8 * lane + u];
+      for (int i = 0; i < kDwrWaves - 1; ++i) s += part[i][8 * lane + u];
       out[u] = s;
     }
     float4* d = reinterpret_cast<float4*>(d_wr + (int64_t)e * H + col);
@@ -275,7 +325,7 @@ hipError_t mok_launch_router_backward(const bf16_t* x, const float* wr, const in
                        T, H, E, k, d_sel, dx);
   }
   const int ncol = (H + 511) / 512;
-  hipLaunchKernelGGL(router_dwr_kernel, dim3((unsigned)(E * ncol)), dim3(256), 0, st, x, d_sel, offsets, perm, tok,
+  hipLaunchKernelGGL(router_dwr_kernel, dim3((unsigned)(E * ncol)), dim3(64 * kDwrWaves), 0, st, x, d_sel, offsets, perm, tok,
                      H, ncol, d_wr);
   return hipGetLastError();
 }
