@@ -17,11 +17,11 @@
 
 namespace {
 
-constexpr int kRouterTokens = 16;                // tokens per forward workgroup (rows 0..15 of the MFMA tile)
+constexpr int kRouterTokens = 16;                // tokens per forward workgroup (one 16-row MFMA tile)
 constexpr int kRouterWaves = 8;                  // K split across the workgroup's wavefronts
 constexpr int kRouterThreads = 64 * kRouterWaves;
 constexpr int kRouterMaxE = 512;
-constexpr int kRouterGroup = 128;                // experts per accumulation group (4 column tiles)
+constexpr int kRouterGroup = 64;                 // experts per accumulation group (4 column tiles)
 
 MOK_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOK_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -44,13 +44,13 @@ MOK_DEV void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& l
 }
 
 // Forward: one workgroup per 16 tokens. The logits x . Wr^T are a dense
-// contraction (token rows x E expert columns x H), done on the matrix cores
-// with v_mfma_f32_32x32x16_bf16 (rows 16..31 of its tile unused: 16-token
-// workgroups put every CU to work at T = 4096): x is bf16 already and Wr is
-// split exactly into three bf16 parts, so every product is exact and the
-// fp32 sums run in the MFMA's fixed order. Wave v sums K = [vH/8, (v+1)H/8)
-// for up to 128 experts at a time; the eight partial sums are added in the
-// order v = 0..7 through LDS. Then each wavefront selects the top-k of two
+// contraction (16 token rows x E expert columns x H), done on the matrix
+// cores with v_mfma_f32_16x16x32_bf16 (lane l supplies row l%16 and the 8 K
+// values from 8(l/16), so four lanes read one full 128-byte line of a Wr
+// row): x is bf16 already and Wr is split exactly into three bf16 parts, so
+// every product is exact and the fp32 sums run in the MFMA's fixed order.
+// Wave v sums the 32-wide K steps v, v + 8, ... for up to 64 experts at a
+// time; the eight partial sums are added in the order v = 0..7 through LDS. Then each wavefront selects the top-k of two
 // tokens: with E <= 64 by ranking each lane's expert against all others;
 // otherwise lane l holds experts l, l + 64, ... and each of k rounds takes
 // the best unselected (score, expert) pair of the wavefront.
@@ -62,37 +62,36 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
   __shared__ float bsh[kRouterMaxE];                                      // bias (0 if none)
   const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
   const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
-  const int r32 = lane & 31, kh = 8 * (lane >> 5);
-  const int kq = H / kRouterWaves, kbeg = v * kq, kend = kbeg + kq;
-  const bool trow = r32 < kRouterTokens && t0 + r32 < T;
-  const bf16_t* xrow = x + (t0 + (trow ? r32 : 0)) * H + kh;   // row t0 exists: t0 < T
+  const int r16 = lane & 15, kh = 8 * (lane >> 4);
+  const int nsteps = H / 32;                                              // 32-wide K steps
+  const bool trow = t0 + r16 < T;
+  const bf16_t* xrow = x + (t0 + (trow ? r16 : 0)) * H + kh;   // row t0 exists: t0 < T
   for (int e = threadIdx.x; e < E; e += kRouterThreads) bsh[e] = bias ? bias[e] : 0.f;
   for (int g0 = 0; g0 < E; g0 += kRouterGroup) {
-    const int nb = min(4, (E - g0 + 31) / 32);                           // column tiles in this group
-    f32x16_t acc[4];
+    const int nb = min(4, (E - g0 + 15) / 16);                           // column tiles in this group
+    f32x4_t acc[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[b][q] = 0.f;
-    // batches of up to 4 K steps: every load of a batch is issued before
-    // its first MFMA
-    for (int kk = kbeg; kk < kend; kk += 64) {
-      const int nu = min(4, (kend - kk) / 16);
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // wave v takes the K steps v, v + 8, v + 16, ... in ascending order, in
+    // batches of up to 4 whose loads are all issued before the first MFMA
+    for (int s0 = v; s0 < nsteps; s0 += 4 * kRouterWaves) {
+      const int nu = min(4, (nsteps - s0 + kRouterWaves - 1) / kRouterWaves);
       uint4 xa[4];
       float4 wv[4][4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         xa[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < nu && trow) xa[u] = *reinterpret_cast<const uint4*>(xrow + kk + 16 * u);
+        if (u < nu && trow) xa[u] = *reinterpret_cast<const uint4*>(xrow + 32 * (s0 + kRouterWaves * u));
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int e = g0 + 32 * b + r32;
+        const int e = g0 + 16 * b + r16;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           wv[b][u][0] = wv[b][u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (b < nb && u < nu && e < E) {
-            const float4* src = reinterpret_cast<const float4*>(wr + (int64_t)e * H + kk + 16 * u + kh);
+            const float4* src =
+                reinterpret_cast<const float4*>(wr + (int64_t)e * H + 32 * (s0 + kRouterWaves * u) + kh);
             wv[b][u][0] = src[0];
             wv[b][u][1] = src[1];
           }
@@ -111,21 +110,19 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
           split3(p.z, p.w, hi.y, mid.y, lo.y);
           split3(q.x, q.y, hi.z, mid.z, lo.z);
           split3(q.z, q.w, hi.w, mid.w, lo.w);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
         }
       }
     }
-    // accumulator element q: token row 8(q/4) + 4(lane/32) + q%4, expert
-    // column lane%32; rows 0..15 are q = 0..7
+    // accumulator element i: token row 4(lane/16) + i, expert column lane%16
     if (v > 0) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b >= nb) break;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          part[v - 1][(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * kRouterGroup + 32 * b + r32] = acc[b][q];
+        for (int i = 0; i < 4; ++i) part[v - 1][(4 * (lane >> 4) + i) * kRouterGroup + 16 * b + r16] = acc[b][i];
       }
     }
     __syncthreads();
@@ -133,13 +130,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b >= nb) break;
-        const int e = g0 + 32 * b + r32;
+        const int e = g0 + 16 * b + r16;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int row = 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          const int pi = row * kRouterGroup + 32 * b + r32;
-          float s = acc[b][q];
-          for (int i = 0; i < kRouterWaves - 1; ++i) s += part[i][pi];
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * (lane >> 4) + i;
+          const int pi = row * kRouterGroup + 16 * b + r16;
+          float s = acc[b][i];
+          for (int j = 0; j < kRouterWaves - 1; ++j) s += part[j][pi];
           if (e < E) lg[row * E + e] = s;
         }
       }
