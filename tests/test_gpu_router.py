@@ -75,7 +75,8 @@ def _check_selection(ids, w, logits, bias, k):
 
 CASES = [problem(37, 256, 128, 5, 2, seed=61), problem(300, 128, 128, 64, 8, seed=62),
          problem(200, 384, 128, 12, 3, seed=63), problem(64, 512, 128, 512, 8, seed=64),
-         problem(129, 256, 128, 32, 4, seed=66, zipf_s=1.2, empty_den=4), problem(9, 128, 128, 6, 6, seed=67)]
+         problem(129, 256, 128, 32, 4, seed=66, zipf_s=1.2, empty_den=4), problem(9, 128, 128, 6, 6, seed=67),
+         problem(40, 256, 128, 128, 64, seed=68)]      # E > 64 (round-based selection), maximum k
 
 
 @pytest.mark.parametrize("with_bias", [False, True], ids=["nobias", "bias"])
@@ -85,7 +86,8 @@ def test_router_forward_matches_oracle(p, with_bias):
     ids, w = _run(p, x, wr_eh, bias)
     logits, _, _ = oracle.router_forward(bf16_to_f32(x).astype(np.float64), wr_eh.astype(np.float64), None, p.k)
     n = _check_selection(ids, w, logits, bias, p.k)
-    assert n >= 0.8 * p.T                        # almost every token is far from a tie
+    if p.k <= 8:                                 # with k = 64 of 128 some gap is often tiny
+        assert n >= 0.8 * p.T                    # almost every token is far from a tie
 
 
 def test_router_forward_full_size_and_deterministic():
@@ -101,10 +103,11 @@ def test_router_forward_full_size_and_deterministic():
     assert _check_selection(ids, w, logits, bias, p.k) >= 0.95 * p.T
 
 
-def test_router_exact_ties_go_to_the_lower_id():
+@pytest.mark.parametrize("E,k", [(10, 3), (100, 40)])   # rank-count and round-based selection
+def test_router_exact_ties_go_to_the_lower_id(E, k):
     import torch
     import mixture_experts_layer_30_amd as mok
-    T, H, E, k = 16, 128, 10, 3
+    T, H = 16, 128
     rng = np.random.default_rng(65)
     x = make_x(problem(T, H, 128, E, k, seed=65))
     wr = rng.standard_normal((E, H)).astype(np.float32)
