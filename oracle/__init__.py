@@ -11,7 +11,7 @@ from .moe_oracle import (  # noqa: F401
     backward, backward_tokens, backward_expert_weights,
     e4m3_decode, e4m3_encode, mxfp8_quantize, mxfp8_dequantize, mxfp8_roundtrip,
     forward_mxfp8, forward_mxfp8_tokens, backward_mxfp8, backward_mxfp8_expert_weights,
-    backward_mxfp8_tokens,
+    backward_mxfp8_tokens, bf16_round,
     router_forward, router_backward,
     STATUS_BAD_EXPERT_ID,
 )

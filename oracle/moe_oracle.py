@@ -430,10 +430,29 @@ def forward_mxfp8_tokens(x_rows, ids_rows, w_rows, experts):
 #   dWg|u[e]  = Q_t(dA|dB)^T  . Q_t(X)           K = the expert's rows
 # Q_H / Q_I quantize along H / I; Q_t quantizes along the expert's rows in
 # blocks of 32 counted from its first permuted row (the last block is padded
-# with zeros, which changes no block maximum). a, b come from the MXFP8
-# forward; h = silu(a)*b, dA, dB and dO are the exact values the definition
-# gives, then quantized where they enter a GEMM. d topk_w and dx are as in the
-# bf16 backward.
+# with zeros, which changes no block maximum). Storage precision (the reading
+# that intermediates are kept in bf16, applied to the MXFP8 backward): the
+# forward saves a, b as bf16 values; h = silu(a)*b from those, dO = w*dy and
+# the SwiGLU gradients dA, dB are each rounded to bf16 once, and it is these
+# bf16 values that every quantization above takes (x is bf16 already). d
+# topk_w and dx are as in the bf16 backward.
+
+
+def bf16_round(v):
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps float32's 8-bit exponent and 8 significant bits (7 stored),
+    so a normal value m * 2^e with 0.5 <= |m| < 1 rounds to a multiple of
+    2^(e - 8); below 2^-126 the step is 2^-133 (subnormals). The rounding is
+    done once, straight from float64 (no double rounding through float32).
+    Magnitudes that round to 2^128 or beyond become infinite.
+    """
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)
+    r = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+    r = np.where(np.abs(v) < 2.0 ** -126, np.round(v * 2.0 ** 133) * 2.0 ** -133, r)
+    with np.errstate(invalid="ignore"):
+        return np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, v), r)
 
 
 def _mx_along_rows(V):
@@ -465,10 +484,11 @@ def _mx_backward_rows(X, dYr, wr, W, Q):
     expert's dWg, dWu, dWd (which need all of its rows)."""
     Wg, Wu, Wd = W
     out, a, b = _mx_ffn(X, *Q, with_ab=True)
-    h = swiglu(a, b)
-    dO = wr[:, None] * dYr
+    a, b = bf16_round(a), bf16_round(b)            # saved by the forward in bf16
+    h = bf16_round(swiglu(a, b))
+    dO = bf16_round(wr[:, None] * dYr)
     dh = _mx_along_rows(dO) @ _mx_along_cols(Wd)
-    dA, dB = _swiglu_backward(dh, a, b)
+    dA, dB = (bf16_round(g) for g in _swiglu_backward(dh, a, b))
     dAB = _mx_along_rows(np.concatenate([dA, dB], axis=1))
     dxr = dAB @ _mx_along_cols(np.concatenate([Wg, Wu], axis=0))
     Xt = _mx_along_tokens(X)
