@@ -3,19 +3,28 @@
 
 One step = one pass of the whole layer on one batch of synthetic input:
 routing schedule -> forward (saving the backward context) -> backward.
-Default workload: bf16, T=4096 tokens, H=2048, E=64 experts, top-8, I=768,
-near-uniform routing. Inputs are seeded and already resident in HBM when the
-timed region starts.
+Default workload (the fwd+bwd one): bf16, T=16384 tokens, H=7168, E=32
+experts, top-4, I=2048, expert loads skewed by a Zipf(0.8) routing bias.
+Inputs are seeded and already resident in HBM when the timed region starts.
 
 Prints ONE JSON line. `value` is layer TFLOP/s: algorithmic FLOPs
 (forward 6*R*H*I + backward 12*R*H*I, R = T*k routed rows, padding excluded)
-divided by the measured step time.
+divided by the measured step time. The timed steps run without the library's
+per-kernel tracer; per-kernel times come from a separate traced pass of the
+same step. Further legs on the same line: the bf16 forward alone, the MXFP8
+step on the same workload, the router front end, a 10-run bitwise
+determinism check, per-expert loads, measured matrix-core and copy peaks,
+the fp64 oracle timed on a sample of the workload on the host cores, and
+the other workloads (bf16 forward of the small, fine-grained and Zipf(1.2)
+ones; MXFP8 forward of the Zipf(1.2) one).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,17 +41,22 @@ GEMM_FLOPS_PER_ROW = {
     "gateup_gemm": 4, "down_gemm": 2, "bwd_dh_gemm": 2, "bwd_dwd_gemm": 2,
     "bwd_dwgu_gemm": 4, "bwd_dx_gemm": 4,
 }
-
-
-# HBM traffic of the GEMM kernels, from rocprofv3 counter runs of this bench
-# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a plain copy of known
-# size); valid only for the kernel sources and workload it was taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gemm_traffic_bf16_T4096_H2048_E64_k8_I768.txt")
+MOVE_KERNELS = ("schedule", "gather", "combine", "reverse_combine", "reverse_dispatch")
 KERNEL_SOURCES = ["gemm_core.h", "k_gemm.hip", "k_rows.hip", "mok_device.h", "mok_launch.h", "mok_host.hip"]
 
 
+def workload_tag(p):
+    return f"{p.dtype}_T{p.T}_H{p.H}_E{p.E}_k{p.k}_I{p.I}"
+
+
+def traffic_file(p):
+    """HBM traffic record of the GEMM and row-moving kernels for workload p
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this bench, scaled by a plain
+    copy of known size)."""
+    return os.path.join(ROOT, "profiles", f"moe_gemm_traffic_{workload_tag(p)}.txt")
+
+
 def kernel_sources_sha256():
-    import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_layer_30_amd", "csrc", name), "rb") as f:
@@ -52,11 +66,12 @@ def kernel_sources_sha256():
 
 def measured_traffic(kernel, p, minibatch_rows):
     """(bytes per launch, source) for `kernel`, or (None, reason)."""
+    path = traffic_file(p)
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.loads([ln for ln in f if ln.startswith("{")][-1])
     except (OSError, IndexError, ValueError):
-        return None, "no traffic record"
+        return None, "no traffic record for this workload"
     if rec.get("sources_sha256") != kernel_sources_sha256():
         return None, "kernel sources changed since the counters were taken"
     if rec.get("workload") != p.name or rec.get("minibatch_rows") != minibatch_rows:
@@ -64,7 +79,7 @@ def measured_traffic(kernel, p, minibatch_rows):
     k = rec.get("kernels", {}).get(kernel)
     if not k:
         return None, "no record for this kernel"
-    return k["bytes_per_launch"], os.path.relpath(TRAFFIC_FILE, ROOT)
+    return k["bytes_per_launch"], os.path.relpath(path, ROOT)
 
 
 def log(msg):
@@ -74,18 +89,18 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--config", type=int, default=1, help="reference workload id (0-4)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="workload id of the headline step (0-4)")
+    ap.add_argument("--extra-configs", default="0,1,2,3",
+                    help="workload ids whose forward is also timed ('' = none; 3 is the MXFP8 forward)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens in the oracle's CPU-baseline sample (0 = skip)")
-    ap.add_argument("--cpu-reps", type=int, default=4,
-                    help="repetitions of the CPU-baseline sample (best is reported)")
     ap.add_argument("--driver", type=int, default=0)
     ap.add_argument("--minibatch-rows", type=int, default=0)
     ap.add_argument("--ring-slots", type=int, default=0)
     ap.add_argument("--only-step", action="store_true",
-                    help="time the step only (no forward-only or MXFP8 legs); for counter runs")
+                    help="the headline step only (no other legs); for counter runs")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write the GEMM traffic record from four rocprofv3 counter_collection.csv "
                          "files (FETCH_SIZE and WRITE_SIZE of a --only-step run, then of a 1 GiB "
@@ -132,8 +147,8 @@ def _counter_per_dispatch(path, counter):
 
 def write_traffic_record(args):
     """Average FETCH_SIZE / WRITE_SIZE per launch of each GEMM kernel, each
-    scaled by what the same counter reads for a 1 GiB device copy, into
-    TRAFFIC_FILE (text summary plus one JSON line that the bench reads)."""
+    scaled by what the same counter reads for a 1 GiB device copy, into the
+    workload's traffic file (text summary plus one JSON line the bench reads)."""
     import mixture_experts_layer_30_amd as mok
     from synthetic import CONFIGS
     fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.traffic_record
@@ -166,7 +181,8 @@ def write_traffic_record(args):
                           "write_kib": round(wk, 1), "bytes_per_launch": int(round((fk * ff + wk * wf) * 1024))}
     rec = {"workload": p.name, "minibatch_rows": mb_rows, "fetch_factor": round(ff, 4),
            "write_factor": round(wf, 4), "sources_sha256": kernel_sources_sha256(), "kernels": kernels}
-    extra = f" --minibatch-rows {args.minibatch_rows}" if args.minibatch_rows else ""
+    extra = f" --config {args.config}" + (f" --minibatch-rows {args.minibatch_rows}" if args.minibatch_rows else "")
+    bench = f"python3 /root/repo/bench.py --steps 2 --warmup 1 --cpu-tokens 0 --only-step{extra}"
     lines = [
         f"# HBM traffic of the grouped-GEMM and row-moving kernels: MoE layer step, bf16, {p.name} "
         f"(minibatch {mb_rows} rows)",
@@ -175,8 +191,8 @@ def write_traffic_record(args):
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp",
-        f"rocprofv3 --pmc FETCH_SIZE -d <f> -o pmc -f csv -- python3 /root/repo/bench.py --steps 2 --warmup 1 --cpu-tokens 0 --only-step{extra}",
-        f"rocprofv3 --pmc WRITE_SIZE -d <w> -o pmc -f csv -- python3 /root/repo/bench.py --steps 2 --warmup 1 --cpu-tokens 0 --only-step{extra}",
+        f"rocprofv3 --pmc FETCH_SIZE -d <f> -o pmc -f csv -- {bench}",
+        f"rocprofv3 --pmc WRITE_SIZE -d <w> -o pmc -f csv -- {bench}",
         "# calibration: a plain 1 GiB device copy (hipMemcpy blit kernel __amd_rocclr_copyBuffer)",
         "rocprofv3 --pmc FETCH_SIZE -d <cf> -o pmc -f csv -- python3 -c \"import torch; a=torch.ones(2**28, "
         "device='cuda', dtype=torch.int32); b=torch.empty_like(a); b.copy_(a); torch.cuda.synchronize()\"",
@@ -200,14 +216,17 @@ def write_traffic_record(args):
                      f"{k['bytes_per_launch'] / 1e6:.1f} MB |")
     lines += ["", "Machine-readable record (bench.py reads the last line; it reports the traffic only while "
               "the kernel sources hash to `sources_sha256` and the workload matches):", "", json.dumps(rec)]
-    with open(TRAFFIC_FILE, "w") as f:
+    path = traffic_file(p)
+    with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    print(f"wrote {os.path.relpath(TRAFFIC_FILE, ROOT)}", file=sys.stderr)
+    print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
 
 
-def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok, reps=1):
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok):
     """The fp64 oracle (as it stands) on the first n_tok tokens of the same
-    workload: forward + backward, reported in the same unit."""
+    workload: the schedule of the whole batch, then forward and forward +
+    backward of the sample, each timed on its own."""
     import numpy as np
     import oracle
     from synthetic import bf16_to_f32
@@ -226,17 +245,180 @@ def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok, reps=1):
 
     xs = bf16_to_f32(x[:n_tok]).astype(np.float64)
     dys = bf16_to_f32(dy[:n_tok]).astype(np.float64)
-    times = []
-    for _ in range(max(1, reps)):
-        t0 = time.perf_counter()
-        oracle.backward(xs, ids[:n_tok], w[:n_tok].astype(np.float64), Ex(), dys)   # runs forward too
-        times.append(time.perf_counter() - t0)
-    dt = min(times)
+    ws = w[:n_tok].astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.schedule(ids, p.E)
+    t1 = time.perf_counter()
+    oracle.forward(xs, ids[:n_tok], ws, Ex())
+    t2 = time.perf_counter()
+    oracle.backward(xs, ids[:n_tok], ws, Ex(), dys)      # recomputes the forward itself
+    t3 = time.perf_counter()
     flops = 18.0 * n_tok * p.k * p.H * p.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n_tok} of {p.T} tokens, forward+backward in fp64 NumPy, best of "
-                      f"{len(times)} runs ({sum(times):.1f} s of CPU work in total)",
-            "seconds": dt}
+    return {"value": flops / (t3 - t2) / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tok} of {p.T} tokens of the same workload: forward + backward in fp64 NumPy "
+                      f"(oracle.backward, which also runs the forward), one run; "
+                      f"{t1 - t0 + t3 - t1:.1f} s of CPU work in total",
+            "seconds_schedule_full_batch": round(t1 - t0, 3), "seconds_forward": round(t2 - t1, 3),
+            "seconds_forward_backward": round(t3 - t2, 3),
+            "seconds_backward_only": round((t3 - t2) - (t2 - t1), 3), "tokens": n_tok}
+
+
+# ------------------------------------------------------------------ timing helpers
+def time_steps(fn, steps, stream):
+    """(mean, median, min) ms of `steps` calls of fn, each bracketed by events
+    on the launch stream; synchronized before and after."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, statistics.median(per), min(per)
+
+
+def traced(fn, steps):
+    """Per-kernel {name: (launches, total_ms, max_ms)} over `steps` calls, from
+    the library's per-launch HIP events (a separate pass from the timed one)."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    torch.cuda.synchronize()
+    mok.trace_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    mok.trace_enable(False)
+    return mok.trace_collect()
+
+
+def gemm_rates(stats, p, steps):
+    return {k: round(GEMM_FLOPS_PER_ROW[k] * p.R * p.H * p.I * steps / (v[1] * 1e-3) / 1e12, 2)
+            for k, v in stats.items() if k in GEMM_FLOPS_PER_ROW}
+
+
+def load_stats(ids, E):
+    import numpy as np
+    c = np.bincount(ids.reshape(-1)[(ids.reshape(-1) >= 0) & (ids.reshape(-1) < E)], minlength=E)
+    return {"experts": E, "rows": int(c.sum()), "mean": round(float(c.mean()), 1), "max": int(c.max()),
+            "min": int(c.min()), "empty": int((c == 0).sum()), "max_over_mean": round(float(c.max() / c.mean()), 3),
+            "cv": round(float(c.std() / c.mean()), 3)}
+
+
+def digest(tensors):
+    """Two integer checksums per tensor (sum, and position-weighted sum, of
+    its 32-bit words; exact integer arithmetic on the device) and their sha256."""
+    import torch
+    parts = []
+    for t in tensors:
+        v = t.contiguous().view(torch.int32).reshape(-1).to(torch.int64)
+        wgt = torch.arange(v.numel(), device=v.device, dtype=torch.int64) % 65521 + 1
+        parts += [int(v.sum().item()), int((v * wgt).sum().item())]
+    return parts, hashlib.sha256(json.dumps(parts).encode()).hexdigest()[:16]
+
+
+def measure_peaks(stream):
+    """Matrix-core rate of back-to-back MFMAs on register operands (bf16 and
+    MXFP8), and device copy bandwidth (read + write bytes of a 4 GiB copy)."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    out = {}
+    wgs = 256 * 8
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    for kind, name, iters in ((0, "bf16_tflops", 2000), (1, "fp8_tflops", 1000)):
+        fl = mok.probe_mfma(kind, wgs, 50, sink, stream)
+        fl = 0.0
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fl = mok.probe_mfma(kind, wgs, iters, sink, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name] = round(fl / (best * 1e-3) / 1e12, 1)
+    a = torch.empty(1 << 30, dtype=torch.int32, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    out["copy_gbs"] = round(2 * a.numel() * 4 / (best * 1e-3) / 1e9, 1)
+    out["how"] = ("mok_probe_mfma: 2048 workgroups x 4 wavefronts, 8 MFMA chains each, best of 3; "
+                  "copy: torch copy_ of a 4 GiB buffer (read + write bytes), best of 3")
+    return out
+
+
+# ------------------------------------------------------------------ workloads on the device
+class Dev:
+    """Device copies of a workload's inputs."""
+
+    def __init__(self, p, threads=16, with_dy=True):
+        import numpy as np
+        import torch
+        from synthetic import make_all_experts, make_dy, make_routing, make_x
+        self.p = p
+        t0 = time.time()
+        self.x_h = make_x(p)
+        self.ids_h, self.w_h = make_routing(p, self.x_h)
+        self.wg_h, self.wu_h, self.wd_h = make_all_experts(p, threads=threads)
+        self.dy_h = make_dy(p) if with_dy else None
+        log(f"[bench] {p.name}: inputs generated in {time.time() - t0:.1f} s")
+
+        def dev16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+        self.x = dev16(self.x_h)
+        self.ids = torch.from_numpy(self.ids_h.astype(np.int32)).cuda()
+        self.w = torch.from_numpy(self.w_h).cuda()
+        self.weights = (dev16(self.wg_h), dev16(self.wu_h), dev16(self.wd_h))
+        self.dy = dev16(self.dy_h) if with_dy else None
+
+
+def forward_leg(d, dtype, steps, warmup, stream, cfg):
+    """Schedule + forward (no context) of workload d; bf16 or MXFP8."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    p = d.p
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=dtype, training=False, **cfg)
+    wts = d.weights if dtype == mok.MOK_BF16 else F.quantize_weights(*d.weights)
+    y = torch.empty_like(d.x)
+
+    def fwd():
+        mok.build_schedule(ws.problem, d.ids, ws.schedule, ws.config, stream)
+        mok.forward(ws.problem, ws.schedule, d.x, d.w, wts, y, ws.workspace, None, ws.config, stream)
+
+    for _ in range(warmup):
+        fwd()
+    mean, med, mn = time_steps(fwd, steps, stream)
+    st = traced(fwd, steps)
+    fl = p.fwd_flops()
+    peak = PEAK_BF16_TFLOPS if dtype == mok.MOK_BF16 else PEAK_FP8_TFLOPS
+    move = sum(st[k][1] for k in MOVE_KERNELS if k in st) / steps
+    sched = st["schedule"][1] / steps if "schedule" in st else 0.0
+    traced_ms = sum(v[1] for v in st.values()) / steps
+    rec = {"workload": p.name, "dtype": "mxfp8" if dtype == mok.MOK_MXFP8 else "bf16",
+           "ms": round(mean, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+           "tflops": round(fl / (mean * 1e-3) / 1e12, 2),
+           "pct_peak": round(100 * fl / (mean * 1e-3) / 1e12 / peak, 2),
+           "tokens_per_s": round(p.T / (mean * 1e-3), 1),
+           "gemm_tflops": gemm_rates(st, p, steps),
+           "schedule_share": round(sched / traced_ms, 4) if traced_ms else None,
+           "sched_gather_combine_share": round(move / traced_ms, 4) if traced_ms else None,
+           "minibatch_rows": mok.schedule_layout(ws.problem, ws.config).minibatch_rows,
+           "loads": load_stats(d.ids_h, p.E)}
+    del ws, wts, y
+    return rec
 
 
 def main():
@@ -246,175 +428,81 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(this library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import mixture_experts_layer_30_amd as mok
     from mixture_experts_layer_30_amd import functional as F
-    from synthetic import CONFIGS, make_all_experts, make_dy, make_routing, make_x, router_weights
+    from synthetic import CONFIGS, router_weights
 
     assert torch.cuda.is_available(), "no GPU visible"
-    p = CONFIGS[args.config]
-    log(f"[bench] workload {p.name}: generating inputs")
-    x = make_x(p)
-    ids, w = make_routing(p, x)
-    wg, wu, wd = make_all_experts(p, threads=16)
-    dy = make_dy(p)
-
-    def dev16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
-    dx_ = dev16(x)
-    dids = torch.from_numpy(ids.astype(np.int32)).cuda()
-    dw_ = torch.from_numpy(w).cuda()
-    weights = (dev16(wg), dev16(wu), dev16(wd))
-    ddy = dev16(dy)
-    cfg = dict(driver=args.driver, minibatch_rows=args.minibatch_rows, ring_slots=args.ring_slots)
-    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True, **cfg)
-    y = torch.empty_like(dx_)
-    gx = torch.empty_like(dx_)
-    gwg, gwu, gwd = (torch.empty_like(t) for t in weights)
-    gtw = torch.empty_like(dw_)
+    mok.lib()
     stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    cfg = dict(driver=args.driver, minibatch_rows=args.minibatch_rows, ring_slots=args.ring_slots)
+
+    peaks = None
+    if not args.only_step:
+        log("[bench] measured peaks (matrix cores, copy)")
+        peaks = measure_peaks(stream)
+        log(f"[bench] {peaks}")
+
+    p = CONFIGS[args.config]
+    d = Dev(p)
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True, **cfg)
+    y = torch.empty_like(d.x)
+    gx = torch.empty_like(d.x)
+    gwg, gwu, gwd = (torch.empty_like(t) for t in d.weights)
+    gtw = torch.empty_like(d.w)
+    outs = (y, gx, gwg, gwu, gwd, gtw)
 
     def step():
-        mok.build_schedule(ws.problem, dids, ws.schedule, ws.config, stream)
-        mok.forward(ws.problem, ws.schedule, dx_, dw_, weights, y, ws.workspace, ws.fwd_ctx,
-                    ws.config, stream)
-        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, dx_, dw_, weights, ddy, gx, gwg, gwu,
-                     gwd, gtw, ws.workspace, ws.config, stream)
+        mok.build_schedule(ws.problem, d.ids, ws.schedule, ws.config, stream)
+        mok.forward(ws.problem, ws.schedule, d.x, d.w, d.weights, y, ws.workspace, ws.fwd_ctx, ws.config, stream)
+        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d.x, d.w, d.weights, d.dy, gx, gwg, gwu, gwd, gtw,
+                     ws.workspace, ws.config, stream)
 
-    def fwd_only():
-        mok.build_schedule(ws.problem, dids, ws.schedule, ws.config, stream)
-        mok.forward(ws.problem, ws.schedule, dx_, dw_, weights, y, ws.workspace, None, ws.config,
-                    stream)
-
-    def timed(fn, steps, trace):
-        torch.cuda.synchronize()
-        if trace:
-            mok.trace_enable(True)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if trace:
-            mok.trace_enable(False)
-        stats = mok.trace_collect() if trace else {}
-        return e0.elapsed_time(e1) / steps, stats
-
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    log(f"[bench] warmup {W} steps")
+    for _ in range(W):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    ms_step, stats = timed(step, args.steps, trace=True)
-    ms_fwd = ms_mx = ms_mxs = ms_wq = ms_rf = ms_rb = None
-    mxstats = mxsstats = {}
-    if not args.only_step:
-        log(f"[bench] {ms_step:.3f} ms/step; forward-only timing")
-        ms_fwd, _ = timed(fwd_only, args.steps, trace=True)
-
-        # MXFP8 forward on the same workload: weights pre-quantized once
-        # (outside the timed region), x quantized on the fly inside mok_forward.
-        log("[bench] MXFP8 forward timing")
-        wsm = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=False, **cfg)
-        qweights = F.quantize_weights(*weights)
-        ymx = torch.empty_like(dx_)
-
-        def fwd_mx():
-            mok.build_schedule(wsm.problem, dids, wsm.schedule, wsm.config, stream)
-            mok.forward(wsm.problem, wsm.schedule, dx_, dw_, qweights, ymx, wsm.workspace, None,
-                        wsm.config, stream)
-
-        for _ in range(2):
-            fwd_mx()
-        ms_mx, mxstats = timed(fwd_mx, args.steps, trace=True)
-        del wsm
-
-        # MXFP8 training step: schedule -> MXFP8 forward saving the context ->
-        # MXFP8 backward. The weights (and their transposed copies for the
-        # backward) are quantized before the timed region, as the pages'
-        # pre-quantized weights; that quantization is timed on its own.
-        log("[bench] MXFP8 step timing")
-        wst = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=True, **cfg)
-        qfull = qweights + F.quantize_weights_backward(*weights)
-
-        def step_mx():
-            mok.build_schedule(wst.problem, dids, wst.schedule, wst.config, stream)
-            mok.forward(wst.problem, wst.schedule, dx_, dw_, qfull, ymx, wst.workspace, wst.fwd_ctx,
-                        wst.config, stream)
-            mok.backward(wst.problem, wst.schedule, wst.fwd_ctx, dx_, dw_, qfull, ddy, gx, gwg, gwu, gwd,
-                         gtw, wst.workspace, wst.config, stream)
-
-        for _ in range(2):
-            step_mx()
-        ms_mxs, mxsstats = timed(step_mx, args.steps, trace=True)
-        ms_wq, _ = timed(lambda: (F.quantize_weights(*weights), F.quantize_weights_backward(*weights)), 3,
-                         trace=False)
-        del wst
-
-        # router front end on the same tokens (outside the layer step: the
-        # layer takes topk_ids / topk_w as inputs)
-        log("[bench] router timing")
-        wr, rbias = router_weights(p)
-        dwr = torch.from_numpy(np.ascontiguousarray(wr.T)).cuda()
-        drb = torch.from_numpy(np.where(np.isfinite(rbias), rbias, -1e30).astype(np.float32)).cuda()
-        rids, rw = torch.empty_like(dids), torch.empty_like(dw_)
-        rsel, rgw = torch.empty_like(dw_), torch.empty_like(dwr)
-        rg = torch.from_numpy(np.random.default_rng(p.seed + 11).standard_normal((p.T, p.k)).astype(np.float32)).cuda()
-
-        def router_fwd():
-            mok.router_forward(ws.problem, dx_, dwr, drb, rids, rw, stream)
-
-        def router_bwd():
-            mok.router_backward(ws.problem, ws.schedule, dx_, dwr, rids, rw, rg, rsel, gx, rgw, ws.config, stream)
-
-        router_fwd()
-        mok.build_schedule(ws.problem, rids, ws.schedule, ws.config, stream)
-        router_bwd()
-        # GPU time per call from the per-launch HIP events (back-to-back calls
-        # of a ~10 us kernel are bound by the host's enqueue rate otherwise)
-        _, rfstats = timed(router_fwd, args.steps, trace=True)
-        _, rstats = timed(router_bwd, args.steps, trace=True)
-        ms_rf = rfstats["router_forward"][1] / rfstats["router_forward"][0]
-        ms_rb = rstats["router_backward"][1] / rstats["router_backward"][0]
+    log(f"[bench] timing {K} steps (tracer off)")
+    ms_step, ms_med, ms_min = time_steps(step, K, stream)
+    log(f"[bench] {ms_step:.3f} ms/step (median {ms_med:.3f}, min {ms_min:.3f}); traced pass")
+    stats = traced(step, K)
 
     R, H, I = p.R, p.H, p.I
     flops_step = p.fwd_flops() + p.bwd_flops()
     value = flops_step / (ms_step * 1e-3) / 1e12
-
-    # per-kernel live timings (HIP events on the launch stream, timed region)
     kernels = {}
     for name, (n, tot, mx) in stats.items():
-        rec = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
-               "avg_launch_ms": tot / n}
+        rec = {"launches_per_step": n / K, "ms_per_step": round(tot / K, 4), "avg_launch_ms": round(tot / n, 4)}
         if name in GEMM_FLOPS_PER_ROW:
-            fl = GEMM_FLOPS_PER_ROW[name] * R * H * I * args.steps
-            rec["tflops"] = fl / (tot * 1e-3) / 1e12
+            rec["tflops"] = round(GEMM_FLOPS_PER_ROW[name] * R * H * I * K / (tot * 1e-3) / 1e12, 2)
         kernels[name] = rec
+    traced_ms = sum(v[1] for v in stats.values()) / K
     gemms = {k: v for k, v in kernels.items() if "tflops" in v}
     dom = max(gemms, key=lambda k: gemms[k]["ms_per_step"])
     dn = stats[dom][0]
-    dom_flops_per_launch = GEMM_FLOPS_PER_ROW[dom] * R * H * I * args.steps / dn
-    achieved = gemms[dom]["tflops"]
+    dom_flops_per_launch = GEMM_FLOPS_PER_ROW[dom] * R * H * I * K / dn
+    dom_avg_ms = stats[dom][1] / dn
+    achieved = dom_flops_per_launch / (dom_avg_ms * 1e-3) / 1e12
     mb_rows = mok.schedule_layout(ws.problem, ws.config).minibatch_rows
     traffic, traffic_src = measured_traffic(dom, p, mb_rows)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
-                "flops_per_launch": dom_flops_per_launch, "avg_launch_ms": stats[dom][1] / dn}
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
+                "flops_per_launch": dom_flops_per_launch, "avg_launch_ms": round(dom_avg_ms, 5),
+                "timing": "HIP events around each launch on the launch stream (library tracer), separate pass"}
+    if peaks:
+        roofline["frac_of_measured_mfma_peak"] = round(achieved / peaks["bf16_tflops"], 4)
     permute = {}
     for k, nbytes in permute_bytes(p).items():
         if k in kernels:
             kms, nl = kernels[k]["ms_per_step"], kernels[k]["launches_per_step"]
-            permute[k] = {"algorithmic_gbs": round(nbytes / (kms * 1e-3) / 1e9, 1),
-                          "bytes_per_step": nbytes, "ms_per_step": round(kms, 4),
-                          "launches_per_step": nl}
-            # counters of combine_kernel average its combine and reverse-dispatch launches
+            permute[k] = {"algorithmic_gbs": round(nbytes / (kms * 1e-3) / 1e9, 1), "bytes_per_step": nbytes,
+                          "ms_per_step": round(kms, 4), "launches_per_step": nl}
             key = "combine+reverse_dispatch" if k in ("combine", "reverse_dispatch") else k
             tb, _ = measured_traffic(key, p, mb_rows)
             if tb is not None:
@@ -422,73 +510,151 @@ def main():
     if permute:
         tot_b = sum(v["bytes_per_step"] for v in permute.values())
         tot_ms = sum(v["ms_per_step"] for v in permute.values())
-        permute["all"] = {"algorithmic_gbs": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-                          "bytes_per_step": tot_b, "ms_per_step": round(tot_ms, 4),
+        permute["all"] = {"algorithmic_gbs": round(tot_b / (tot_ms * 1e-3) / 1e9, 1), "bytes_per_step": tot_b,
+                          "ms_per_step": round(tot_ms, 4),
                           "frac_of_hbm_peak": round(tot_b / (tot_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    move = sum(kernels.get(k, {}).get("ms_per_step", 0.0)
-               for k in ("schedule", "gather", "combine", "reverse_combine", "reverse_dispatch"))
+        if peaks:
+            permute["all"]["frac_of_measured_copy"] = round(tot_b / (tot_ms * 1e-3) / 1e9 / peaks["copy_gbs"], 4)
+    move = sum(kernels.get(k, {}).get("ms_per_step", 0.0) for k in MOVE_KERNELS)
     gemm_ms = sum(v["ms_per_step"] for v in gemms.values())
-    fwd_flops = p.fwd_flops()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"MoE SwiGLU layer fwd+bwd: {p.name}", "T": p.T, "H": H, "I": I,
-                   "E": p.E, "topk": p.k, "routed_rows": R, "minibatch_rows": ws.config.minibatch_rows
-                   or mok.schedule_layout(ws.problem, ws.config).minibatch_rows,
+        "data": "synthetic (seeded; random-init expert weights)",
+        "config": {"workload": f"MoE SwiGLU layer fwd+bwd, bf16: {p.name}", "T": p.T, "H": H, "I": I,
+                   "E": p.E, "topk": p.k, "routed_rows": R, "minibatch_rows": mb_rows,
                    "ring_slots": mok.schedule_layout(ws.problem, ws.config).ring_slots,
-                   "driver": {0: "default (launch-per-minibatch)", 1: "launch-per-minibatch",
-                              2: "persistent (not provided)"}[args.driver]},
+                   "driver": {0: "default (launch per stage per ring group)", 1: "launch per stage per ring group",
+                              2: "persistent"}[args.driver]},
+        "ms_per_step_median": round(ms_med, 4), "ms_per_step_min": round(ms_min, 4),
         "tokens_per_s": round(p.T / (ms_step * 1e-3), 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 2) if gemm_ms else None,
-        "sched_gather_combine_share": round(move / ms_step, 4),
-        "schedule_share": round(kernels.get("schedule", {}).get("ms_per_step", 0.0) / ms_step, 4),
+        "sched_gather_combine_share": round(move / traced_ms, 4),
+        "schedule_share": round(kernels.get("schedule", {}).get("ms_per_step", 0.0) / traced_ms, 4),
         "kernels": kernels,
-        "permute_gbs": round(permute["all"]["algorithmic_gbs"], 1) if permute else None,
+        "permute_gbs": permute["all"]["algorithmic_gbs"] if permute else None,
         "permute": permute,
         "roofline": roofline,
+        "loads": load_stats(d.ids_h, p.E),
     }
-    if ms_fwd is not None:
-        out["forward"] = {"ms": round(ms_fwd, 4), "tflops": round(fwd_flops / (ms_fwd * 1e-3) / 1e12, 2),
-                          "tokens_per_s": round(p.T / (ms_fwd * 1e-3), 1)}
-    if ms_mx is not None:
-        out["mxfp8_forward"] = {
-            "ms": round(ms_mx, 4), "tflops": round(fwd_flops / (ms_mx * 1e-3) / 1e12, 2),
-            "pct_fp8_peak": round(100 * fwd_flops / (ms_mx * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
-            "tokens_per_s": round(p.T / (ms_mx * 1e-3), 1),
-            "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
-                            for k, v in mxstats.items() if k in GEMM_FLOPS_PER_ROW},
-        }
-    if ms_mxs is not None:
+    if peaks:
+        out["measured_peaks"] = peaks
+        out["pct_measured_bf16_peak"] = round(100 * value / peaks["bf16_tflops"], 2)
+
+    # 10 runs of the step on the same buffers: every output bitwise equal
+    log("[bench] determinism: 10 runs")
+    ref = None
+    same = True
+    dig = None
+    for run in range(10):
+        for o in outs:
+            o.fill_(7)
+        step()
+        torch.cuda.synchronize()
+        parts, h = digest(outs)
+        if ref is None:
+            ref, dig = parts, h
+        same = same and parts == ref
+    out["determinism"] = {"runs": 10, "bitwise_identical": same, "digest": dig,
+                          "outputs": "y, dx, dWg, dWu, dWd, d topk_w"}
+
+    if not args.only_step:
+        log("[bench] forward-only timing")
+        out["forward"] = forward_leg(d, mok.MOK_BF16, K, W, stream, cfg)
+        del ws
+        # MXFP8 step on the same workload: the weights (and their transposed
+        # copies for the backward) are quantized once before the timed region,
+        # as the pages' pre-quantized weights; that quantization is timed too.
+        log("[bench] MXFP8 step timing")
+        wst = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=mok.MOK_MXFP8, training=True, **cfg)
+        t_q = time_steps(lambda: F.quantize_weights(*d.weights) + F.quantize_weights_backward(*d.weights), 3,
+                         stream)[0]
+        qfull = F.quantize_weights(*d.weights) + F.quantize_weights_backward(*d.weights)
+        ymx = torch.empty_like(d.x)
+
+        def step_mx():
+            mok.build_schedule(wst.problem, d.ids, wst.schedule, wst.config, stream)
+            mok.forward(wst.problem, wst.schedule, d.x, d.w, qfull, ymx, wst.workspace, wst.fwd_ctx, wst.config,
+                        stream)
+            mok.backward(wst.problem, wst.schedule, wst.fwd_ctx, d.x, d.w, qfull, d.dy, gx, gwg, gwu, gwd, gtw,
+                         wst.workspace, wst.config, stream)
+
+        for _ in range(W):
+            step_mx()
+        mxm, mxmed, mxmin = time_steps(step_mx, K, stream)
+        mxst = traced(step_mx, K)
         out["mxfp8_step"] = {
-            "ms": round(ms_mxs, 4), "tflops": round(flops_step / (ms_mxs * 1e-3) / 1e12, 2),
-            "pct_fp8_peak": round(100 * flops_step / (ms_mxs * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
-            "tokens_per_s": round(p.T / (ms_mxs * 1e-3), 1),
-            "gemm_tflops": {k: round(GEMM_FLOPS_PER_ROW[k] * R * H * I * args.steps / (v[1] * 1e-3) / 1e12, 2)
-                            for k, v in mxsstats.items() if k in GEMM_FLOPS_PER_ROW},
-            "kernels_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in mxsstats.items()},
-            "weight_quantize_ms": round(ms_wq, 4),
-        }
-    if ms_rf is not None:
-        # algorithmic bytes: forward reads x and Wr once and writes ids, w;
-        # backward reads ids, w, d topk_w, Wr and x, writes d_sel, dx, dWr
-        # (d_sel read back once by the dWr pass)
+            "workload": p.name, "ms": round(mxm, 4), "ms_median": round(mxmed, 4), "ms_min": round(mxmin, 4),
+            "tflops": round(flops_step / (mxm * 1e-3) / 1e12, 2),
+            "pct_fp8_peak": round(100 * flops_step / (mxm * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+            "tokens_per_s": round(p.T / (mxm * 1e-3), 1), "gemm_tflops": gemm_rates(mxst, p, K),
+            "kernels_ms_per_step": {k: round(v[1] / K, 4) for k, v in mxst.items()},
+            "weight_quantize_ms": round(t_q, 4)}
+        if peaks:
+            out["mxfp8_step"]["pct_measured_fp8_peak"] = round(
+                100 * flops_step / (mxm * 1e-3) / 1e12 / peaks["fp8_tflops"], 2)
+        del wst, qfull, ymx
+
+        # router front end on the same tokens (outside the layer step: the
+        # layer takes topk_ids / topk_w as inputs)
+        log("[bench] router timing")
+        import numpy as np
+        wr, rbias = router_weights(p)
+        dwr = torch.from_numpy(np.ascontiguousarray(wr.T)).cuda()
+        drb = torch.from_numpy(np.where(np.isfinite(rbias), rbias, -1e30).astype(np.float32)).cuda()
+        rids, rw = torch.empty_like(d.ids), torch.empty_like(d.w)
+        rsel, rgw = torch.empty_like(d.w), torch.empty_like(dwr)
+        rg = torch.from_numpy(np.random.default_rng(p.seed + 11).standard_normal((p.T, p.k)).astype(np.float32)).cuda()
+        wsr = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=False, **cfg)
+        prob = mok.make_problem(p.T, p.H, p.I, p.E, p.k)
+
+        def router_fwd():
+            mok.router_forward(prob, d.x, dwr, drb, rids, rw, stream)
+
+        def router_bwd():
+            mok.router_backward(prob, wsr.schedule, d.x, dwr, rids, rw, rg, rsel, gx, rgw, wsr.config, stream)
+
+        router_fwd()
+        mok.build_schedule(wsr.problem, rids, wsr.schedule, wsr.config, stream)
+        router_bwd()
+        rfst, rbst = traced(router_fwd, K), traced(router_bwd, K)
+        ms_rf = rfst["router_forward"][1] / rfst["router_forward"][0]
+        ms_rb = rbst["router_backward"][1] / rbst["router_backward"][0]
         b_f = p.T * 2 * H + p.E * H * 4 + p.T * p.k * 8
         b_b = 2 * p.T * 2 * H + 2 * p.E * H * 4 + p.T * p.k * 20
         out["router"] = {
-            "forward_ms": round(ms_rf, 4), "backward_ms": round(ms_rb, 4),
-            "forward_gbs": round(b_f / (ms_rf * 1e-3) / 1e9, 1),
-            "backward_gbs": round(b_b / (ms_rb * 1e-3) / 1e9, 1),
+            "workload": p.name, "forward_ms": round(ms_rf, 4), "backward_ms": round(ms_rb, 4),
+            "forward_gbs": round(b_f / (ms_rf * 1e-3) / 1e9, 1), "backward_gbs": round(b_b / (ms_rb * 1e-3) / 1e9, 1),
             "forward_bytes": b_f, "backward_bytes": b_b,
             "logit_tflops": round(2 * p.T * p.E * H / (ms_rf * 1e-3) / 1e12, 3),
-            "timing": "HIP events around each call on the launch stream (mok_trace), averaged over the calls",
-        }
+            "timing": "HIP events around each call on the launch stream (mok_trace), averaged over the calls"}
+        del wsr
+
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(p, x, ids, w, wg, wu, wd, dy, min(args.cpu_tokens, p.T),
-                                           args.cpu_reps)
+        out["cpu_baseline"] = cpu_baseline(p, d.x_h, d.ids_h, d.w_h, d.wg_h, d.wu_h, d.wd_h, d.dy_h,
+                                           min(args.cpu_tokens, p.T))
+
+    extra = [int(c) for c in args.extra_configs.split(",") if c.strip()] if not args.only_step else []
+    if extra:
+        del d, outs, y, gx, gwg, gwu, gwd, gtw
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        cache = {}
+        for c in extra:
+            q = CONFIGS[c]
+            key = (q.T, q.H, q.E, q.k, q.I, q.seed, q.zipf_s, q.empty_den)
+            if key not in cache:
+                cache.clear()
+                torch.cuda.empty_cache()
+                cache[key] = Dev(q, with_dy=False)
+            dq = cache[key]
+            dq.p = q
+            log(f"[bench] workload {c}: {q.name}")
+            out["configs"][str(c)] = forward_leg(dq, mok.MOK_MXFP8 if q.dtype == "mxfp8" else mok.MOK_BF16,
+                                                 K, W, stream, cfg)
     print(json.dumps(out), flush=True)
 
 

@@ -67,8 +67,9 @@ typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
 #define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
 #define MOK_STATUS_WATCHDOG      0x2   /* reserved (persistent driver, not provided) */
 
-/* Problem shape. Supported: T >= 1, 1 <= topk <= E <= 512, T*topk < 2^31,
- * H and I multiples of 128. dtype MOK_MXFP8 is forward-only. */
+/* Problem shape. Supported: T >= 0, 1 <= topk <= E <= 512, T*topk < 2^31,
+ * H and I multiples of 128. dtype MOK_MXFP8 selects the MXFP8 forward and
+ * backward (weights pre-quantized, see mok_weights). */
 typedef struct {
   int64_t T, H, I;
   int32_t E, topk;
@@ -111,7 +112,8 @@ typedef struct {
    * w_down_t = Wd^T [E][I][H] E4M3 with s_down_t [E][I][H/32] (blocks along H);
    * w_gu_t = [Wg; Wu]^T [E][H][2I] E4M3 with s_gu_t [E][H][2I/32] (blocks
    * along 2I; I is a multiple of 32, so no block spans Wg and Wu). Both come
-   * from mok_mxfp8_quantize of the transposed bf16 weights. */
+   * from mok_mxfp8_quantize_transposed of the bf16 weights (Wd with ld = H;
+   * Wg at col0 = 0 and Wu at col0 = I with ld = 2I). */
   const void* w_down_t;
   const void* w_gu_t;
   const uint8_t* s_down_t;
@@ -218,6 +220,22 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
 mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K,
                               uint8_t* q, uint8_t* scales, void* stream);
 
+/* MXFP8 quantization along the other axis ([MoK card] "Core concepts" and
+ * "Limits": pre-quantized MXFP8 weights; the MXFP8 backward contracts the
+ * weights over their output axis, so it needs copies blocked along that axis).
+ * src [batch][rows][cols] bf16 -> q[b][c][col0 + r] = E4M3 code of src[b][r][c]
+ * and scales[b][c][(col0 + r)/32], blocked by 32 along r: exactly the codes and
+ * scale bytes mok_mxfp8_quantize gives for each transposed [cols][rows] matrix,
+ * written into columns [col0, col0 + rows) of a [cols][ld] output (other
+ * columns untouched), so that two calls can fill [Wg; Wu]^T.
+ * q is [batch][cols][ld] bytes, scales [batch][cols][ld/32] bytes.
+ * Requires rows, ld and col0 multiples of 32, cols a multiple of 8,
+ * col0 + rows <= ld, src and q 16-byte aligned (MOK_ERR_INVALID_ARG
+ * otherwise); batch <= 65535 (MOK_ERR_UNSUPPORTED). Empty inputs are a no-op. */
+mok_status mok_mxfp8_quantize_transposed(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                         uint8_t* q, uint8_t* scales, int64_t ld, int64_t col0,
+                                         void* stream);
+
 /* ---------------------------------------------------------------- router
  * Router front end ([MoK clip] key chart: "Router picks top-k", upstream of
  * the layer; the pages give no formula, this is the plainest reading):
@@ -273,6 +291,18 @@ mok_status mok_trace_enable(int32_t on);
 
 /* [host] Fill out[0 .. min(n, capacity)) and *n_out = n, the number of kernels. */
 mok_status mok_trace_collect(mok_trace_stat* out, int32_t capacity, int32_t* n_out);
+
+/* ---------------------------------------------------------------- peak probe
+ * Matrix-core rate the device sustains, for putting the grouped GEMMs' rates
+ * beside a measured peak ([MoK clip] How-to item 1: profile first). Enqueues
+ * `workgroups` workgroups of 4 wavefronts; each wavefront issues 8 * iters
+ * matrix instructions back to back on register operands (no memory traffic):
+ * kind 0 = bf16 (v_mfma_f32_32x32x16_bf16, 32768 FLOP each), kind 1 = MXFP8
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3, 131072 FLOP each). Total FLOP =
+ * workgroups * 4 * 8 * iters * (FLOP each). Writes one float per thread to
+ * sink [workgroups * 256] (device). The caller times it on `stream`. Kind not
+ * 0 or 1, negative counts, or a NULL sink with work to do: MOK_ERR_INVALID_ARG. */
+mok_status mok_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,7 +64,8 @@ _lib = None
 
 EXPORTS = ("mok_version", "mok_status_string", "mok_buffer_sizes", "mok_get_schedule_layout",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
-           "mok_router_forward", "mok_router_backward", "mok_trace_enable", "mok_trace_collect")
+           "mok_router_forward", "mok_router_backward", "mok_trace_enable", "mok_trace_collect",
+           "mok_mxfp8_quantize_transposed", "mok_probe_mfma")
 
 
 class TraceStat(ctypes.Structure):
@@ -99,6 +100,11 @@ def lib():
                                    vp, vp, vp, vp, vp, sz, vp]
         L.mok_mxfp8_quantize.restype = ctypes.c_int
         L.mok_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+        L.mok_mxfp8_quantize_transposed.restype = ctypes.c_int
+        L.mok_mxfp8_quantize_transposed.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp,
+                                                     ctypes.c_int64, ctypes.c_int64, vp]
+        L.mok_probe_mfma.restype = ctypes.c_int
+        L.mok_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
         L.mok_router_forward.restype = ctypes.c_int
         L.mok_router_forward.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp]
         L.mok_router_backward.restype = ctypes.c_int
@@ -203,6 +209,25 @@ def mxfp8_quantize(src, q, scales, stream=None):
     _check(lib().mok_mxfp8_quantize(_ptr(src), int(rows) if src.dim() == 2 else int(src.numel() // K),
                                     int(K), _ptr(q), _ptr(scales), _stream(stream)),
            "mok_mxfp8_quantize")
+
+
+def mxfp8_quantize_transposed(src, q, scales, col0=0, stream=None):
+    """src [batch][rows][cols] (or [rows][cols]) bf16 -> q[b][c][col0 + r] (E4M3) and
+    scales[b][c][(col0 + r) / 32] (E8M0), blocked by 32 along the source rows; q is
+    [batch][cols][ld] uint8 and scales [batch][cols][ld/32] uint8 (ld = q.shape[-1])."""
+    rows, cols, ld = src.shape[-2], src.shape[-1], q.shape[-1]
+    batch = int(src.numel() // (rows * cols)) if rows * cols else 0
+    _check(lib().mok_mxfp8_quantize_transposed(_ptr(src), batch, int(rows), int(cols), _ptr(q), _ptr(scales),
+                                               int(ld), int(col0), _stream(stream)),
+           "mok_mxfp8_quantize_transposed")
+
+
+def probe_mfma(kind, workgroups, iters, sink, stream=None):
+    """Enqueue the matrix-core peak probe (kind 0 bf16, 1 MXFP8); sink holds
+    workgroups * 256 float32. Returns the FLOPs it performs."""
+    _check(lib().mok_probe_mfma(int(kind), int(workgroups), int(iters), _ptr(sink), _stream(stream)),
+           "mok_probe_mfma")
+    return float(workgroups) * 4 * 8 * iters * (32768 if kind == 0 else 131072)
 
 
 def router_forward(problem, x, w_router, bias, topk_ids, topk_w, stream=None):

@@ -426,7 +426,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, i
 
 // dh = dO . Wd[e] (K = H) from dO rows and Wd^T rows, then the SwiGLU
 // backward; writes dA|dB rows quantized along 2I (for dX), dA|dB token-blocked
-// (for dWg/dWu) and h (bf16, token-blocked by token_quantize_kernel).
+// (for dWg/dWu) and h (bf16, token-blocked by token_quantize_kernel). dA and dB
+// are rounded to bf16 once and both of their quantizations take those values.
 __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, int ncol) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
@@ -496,10 +497,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
             da[u + v] = dh[v] * bv[v] * sg * (1.0f + av[v] * (1.0f - sg));
             db[u + v] = dh[v] * av[v] * sg;
             h[v] = av[v] * sg * bv[v];
+          }
+          *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
+          // dA and dB are bf16 values before either of their quantizations
+          unpack_bf16x8(pack_bf16x8(da + u), da + u);
+          unpack_bf16x8(pack_bf16x8(db + u), db + u);
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
             amaxa = fmaxf(amaxa, fabsf(da[u + v]));
             amaxb = fmaxf(amaxb, fabsf(db[u + v]));
           }
-          *reinterpret_cast<uint4*>(a.hb + p * I + n0 + c0 + u) = pack_bf16x8(h);
         }
         // the row's bf16 dA and dB values replace its fp32 dh block in the
         // staging area (this thread alone reads that block): 64 bytes of dA,

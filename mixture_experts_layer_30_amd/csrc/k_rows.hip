@@ -189,6 +189,56 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16_t* __res
   scales[idx] = (uint8_t)sc;
 }
 
+// ------------------------------------------------------------------ transposing MXFP8 quantize
+// q[b][c][col0 + r] = E4M3 code of src[b][r][c], blocked by 32 along r (the
+// source rows): the weight copies that the MXFP8 backward contracts over the
+// weights' other axis (Wd^T blocked along H, [Wg; Wu]^T along 2I). The codes
+// and scale bytes are those mxfp8_quantize_kernel gives for the transposed
+// matrix. One workgroup per 64 source rows x 128 source columns of matrix b:
+// the tile comes in as 256-byte row segments (16-byte loads) into LDS; each
+// thread then takes one source column and one 32-row block (a wavefront's 64
+// lanes read 64 adjacent bf16 of one tile row per step, conflict-free) and
+// writes its 32 codes as two 16-byte stores along the output row.
+__global__ __launch_bounds__(256) void mxfp8_quantize_t_kernel(const bf16_t* __restrict__ src, int64_t rows,
+                                                              int64_t cols, uint8_t* __restrict__ q,
+                                                              uint8_t* __restrict__ scales, int64_t ld,
+                                                              int64_t col0) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64 * 128];
+  const int64_t b = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 128;
+  const bf16_t* s = src + b * rows * cols;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = threadIdx.x + 256 * u, row = idx >> 4, ch = idx & 15;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r0 + row < rows && c0 + ch * 8 < cols)
+      v = *reinterpret_cast<const uint4*>(s + (r0 + row) * cols + c0 + ch * 8);
+    *reinterpret_cast<uint4*>(tile + row * 128 + ch * 8) = v;
+  }
+  __syncthreads();
+  const int c = threadIdx.x & 127, rb = threadIdx.x >> 7;
+  if (c0 + c >= cols || r0 + 32 * rb >= rows) return;
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    v[r] = bf16_to_f32(tile[(32 * rb + r) * 128 + c]);
+    amax = fmaxf(amax, fabsf(v[r]));
+  }
+  const int sc = mx_scale_byte(amax);
+  const float inv = mx_inv_scale(sc);
+  uint32_t wds[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    wds[u] = e4m3_pack4(v[4 * u] * inv, v[4 * u + 1] * inv, v[4 * u + 2] * inv, v[4 * u + 3] * inv);
+  const int64_t orow = b * cols + c0 + c;
+  const int64_t ocol = col0 + r0 + 32 * rb;
+  uint4* d = reinterpret_cast<uint4*>(q + orow * ld + ocol);
+  d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+  scales[orow * (ld / 32) + ocol / 32] = (uint8_t)sc;
+}
+
 // ------------------------------------------------------------------ token-blocked MXFP8
 // For the weight-gradient GEMMs of the MXFP8 backward (contraction over an
 // expert's rows): expert e's rows [o_e, o_e + c_e) of the source, transposed
@@ -368,6 +418,16 @@ hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K,
   if (nblocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3(grid_for(nblocks, 256)), dim3(256), 0, st, src,
                      nblocks, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_mxfp8_quantize_t(const bf16_t* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* q,
+                                       uint8_t* scales, int64_t ld, int64_t col0, hipStream_t st) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  if (batch > 65535 || (rows + 63) / 64 > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mxfp8_quantize_t_kernel, dim3((unsigned)((cols + 127) / 128), (unsigned)((rows + 63) / 64),
+                                                   (unsigned)batch),
+                     dim3(256), 0, st, src, rows, cols, q, scales, ld, col0);
   return hipGetLastError();
 }
 

@@ -547,6 +547,38 @@ mok_status mok_mxfp8_quantize(const void* src, int64_t rows, int64_t K, uint8_t*
   return MOK_OK;
 }
 
+mok_status mok_mxfp8_quantize_transposed(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                         uint8_t* q, uint8_t* scales, int64_t ld, int64_t col0,
+                                         void* stream) {
+  TraceCall tc;
+  if (batch < 0 || rows < 0 || cols < 0 || ld < 0 || col0 < 0) return MOK_ERR_INVALID_ARG;
+  if (rows % 32 != 0 || cols % 8 != 0 || ld % 32 != 0 || col0 % 32 != 0 || col0 + rows > ld)
+    return MOK_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0 || cols == 0) return MOK_OK;
+  if (!src || !q || !scales) return MOK_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+    return MOK_ERR_INVALID_ARG;
+  if (batch > 65535 || (rows + 63) / 64 > 65535) return MOK_ERR_UNSUPPORTED;
+  mok_status s = check_device();
+  if (s != MOK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN("mxfp8_quantize_t", mok_launch_mxfp8_quantize_t(static_cast<const bf16_t*>(src), batch, rows, cols,
+                                                          q, scales, ld, col0, st));
+  return MOK_OK;
+}
+
+mok_status mok_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  TraceCall tc;
+  if ((kind != 0 && kind != 1) || workgroups < 0 || iters < 0) return MOK_ERR_INVALID_ARG;
+  if (workgroups > 0 && iters > 0 && !sink) return MOK_ERR_INVALID_ARG;
+  mok_status s = check_device();
+  if (s != MOK_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  MOK_RUN(kind == 0 ? "probe_mfma_bf16" : "probe_mfma_fp8",
+          mok_launch_probe_mfma(kind, workgroups, iters, sink, st));
+  return MOK_OK;
+}
+
 // [MoK clip] key chart "Router picks top-k" (reading stated in include/mok.h)
 mok_status mok_router_forward(const mok_problem* problem, const void* x, const float* w_router,
                               const float* bias, int32_t* topk_ids, float* topk_w, void* stream) {

@@ -54,6 +54,17 @@ hipError_t mok_launch_reverse_dispatch(const bf16_t* dxrows, const int32_t* dest
 hipError_t mok_launch_mxfp8_quantize(const bf16_t* src, int64_t rows, int64_t K, uint8_t* q,
                                      uint8_t* scales, hipStream_t st);
 
+// q[b][c][col0 + r] = E4M3(src[b][r][c]) blocked by 32 along r; scales
+// [b][c][ld/32] at (col0 + r)/32. rows % 32 == 0, cols % 8 == 0, ld and col0
+// multiples of 32, src and q 16-byte aligned (checked by the caller).
+hipError_t mok_launch_mxfp8_quantize_t(const bf16_t* src, int64_t batch, int64_t rows, int64_t cols, uint8_t* q,
+                                       uint8_t* scales, int64_t ld, int64_t col0, hipStream_t st);
+
+// Matrix-core peak probe: `workgroups` workgroups of 4 wavefronts, each
+// issuing 8 * iters MFMAs back to back on register operands (kind 0: bf16
+// 32x32x16, kind 1: scaled fp8 32x32x64), one float per thread to sink.
+hipError_t mok_launch_probe_mfma(int kind, int workgroups, int iters, float* sink, hipStream_t st);
+
 hipError_t mok_launch_zero(void* p, int64_t bytes, hipStream_t st);
 
 // ---------------------------------------------------------------- grouped GEMMs

@@ -10,7 +10,7 @@ import dataclasses
 import torch
 
 from . import (MOK_BF16, backward, buffer_sizes, build_schedule, forward, make_config,
-               make_problem, mxfp8_quantize, schedule_layout)
+               make_problem, mxfp8_quantize, mxfp8_quantize_transposed, schedule_layout)
 
 
 @dataclasses.dataclass
@@ -53,18 +53,20 @@ def run_backward(w: Workspace, x, topk_w, weights, dy):
 
 
 def quantize_weights_backward(wg, wu, wd):
-    """The transposed MXFP8 weight copies the MXFP8 backward needs: Wd^T
-    [E][I][H] blocked along H, and [Wg; Wu]^T [E][H][2I] blocked along 2I.
+    """The MXFP8 weight copies the MXFP8 backward needs, quantized along the
+    weights' other axis by the library's transposing quantizer: Wd^T
+    [E][I][H] blocked along H, and [Wg; Wu]^T [E][H][2I] blocked along 2I
+    (Wg into columns [0, I), Wu into [I, 2I)).
     Returns (w_down_t, w_gu_t, s_down_t, s_gu_t)."""
-    wdt = wd.transpose(1, 2).contiguous()
-    wgut = torch.cat([wg, wu], dim=1).transpose(1, 2).contiguous()
-    out = []
-    for m in (wdt, wgut):
-        q = torch.empty(m.shape, dtype=torch.uint8, device=m.device)
-        s = torch.empty(m.shape[:-1] + (m.shape[-1] // 32,), dtype=torch.uint8, device=m.device)
-        mxfp8_quantize(m.reshape(-1, m.shape[-1]), q, s)
-        out.append((q, s))
-    (qd, sd), (qgu, sgu) = out
+    E, I, H = wg.shape
+    dev = wg.device
+    qd = torch.empty((E, I, H), dtype=torch.uint8, device=dev)
+    sd = torch.empty((E, I, H // 32), dtype=torch.uint8, device=dev)
+    qgu = torch.empty((E, H, 2 * I), dtype=torch.uint8, device=dev)
+    sgu = torch.empty((E, H, 2 * I // 32), dtype=torch.uint8, device=dev)
+    mxfp8_quantize_transposed(wd, qd, sd)
+    mxfp8_quantize_transposed(wg, qgu, sgu, col0=0)
+    mxfp8_quantize_transposed(wu, qgu, sgu, col0=I)
     return qd, qgu, sd, sgu
 
 

@@ -148,3 +148,27 @@ def test_router_calls_reject_bad_arguments():
         a = list(args)
         a[i] = None
         assert L.mok_router_backward(ctypes.byref(prob), None, *a, None) == mok.MOK_ERR_INVALID_ARG, i
+
+
+def test_transposed_quantize_and_probe_reject_bad_arguments():
+    L = mok.lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1008)                 # not 16-byte aligned
+    Q = L.mok_mxfp8_quantize_transposed
+    E = mok.MOK_ERR_INVALID_ARG
+    assert Q(fake, 2, 48, 64, fake, fake, 64, 0, None) == E          # rows not a multiple of 32
+    assert Q(fake, 2, 64, 60, fake, fake, 64, 0, None) == E          # cols not a multiple of 8
+    assert Q(fake, 2, 64, 64, fake, fake, 96, 16, None) == E         # col0 not a multiple of 32
+    assert Q(fake, 2, 64, 64, fake, fake, 80, 0, None) == E          # ld not a multiple of 32
+    assert Q(fake, 2, 64, 64, fake, fake, 64, 32, None) == E         # col0 + rows > ld
+    assert Q(fake, -1, 64, 64, fake, fake, 64, 0, None) == E
+    assert Q(None, 2, 64, 64, fake, fake, 64, 0, None) == E
+    assert Q(fake, 2, 64, 64, fake, None, 64, 0, None) == E
+    assert Q(odd, 2, 64, 64, fake, fake, 64, 0, None) == E
+    assert Q(fake, 2, 64, 64, odd, fake, 64, 0, None) == E
+    assert Q(fake, 70000, 64, 64, fake, fake, 64, 0, None) == mok.MOK_ERR_UNSUPPORTED
+    assert Q(None, 0, 64, 64, None, None, 64, 0, None) == mok.MOK_OK  # empty: nothing to do
+    P_ = L.mok_probe_mfma
+    assert P_(2, 4, 4, fake, None) == E
+    assert P_(0, -1, 4, fake, None) == E
+    assert P_(1, 4, 4, None, None) == E

@@ -110,12 +110,49 @@ def test_large_hidden_fwd_bwd_sampled():
                                       f64(dy[toks]))
     assert_close_bf16(from_dev_bf16(dx)[toks], dxr, "dx[sampled]")
     assert_close_bf16(dtw.cpu().numpy()[toks].astype(np.float64), dwr, "d topk_w[sampled]")
+    # the least, a middle and the most loaded expert: the weight-gradient
+    # GEMMs run K = the expert's rows (about 270 to 12000 here), so the
+    # hottest expert takes the longest K loop the kernels ever run
     counts = np.bincount(ids.reshape(-1), minlength=p.E)
-    for e in (int(np.argmin(counts)),):
+    order = np.argsort(counts, kind="stable")
+    for e in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+        print(f"expert {e}: {counts[e]} rows", flush=True)
         dg, du, dd = oracle.backward_expert_weights(e, f64(x), ids, w.astype(np.float64), ex, f64(dy))
         assert_close_bf16(from_dev_bf16(dwg[e]), dg, f"dWg[{e}]")
         assert_close_bf16(from_dev_bf16(dwu[e]), du, f"dWu[{e}]")
         assert_close_bf16(from_dev_bf16(dwd[e]), dd, f"dWd[{e}]")
+
+
+@pytest.mark.timeout(900)
+def test_large_hidden_step_bitwise_deterministic_10_runs():
+    """The whole bf16 step (schedule, forward with context, backward) on
+    T=16384, H=7168, E=32, top-4, I=2048 with Zipf(0.8) loads, run 10 times
+    on the same buffers: every output bitwise equal to the first run's."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    p = CONFIGS[4]
+    d = device_inputs(p)
+    ddy = to_dev_bf16(make_dy(p))
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True)
+    wg, wu, wd = d["weights"]
+    outs = [torch.empty_like(d["x"]), torch.empty_like(d["x"]), torch.empty_like(wg), torch.empty_like(wu),
+            torch.empty_like(wd), torch.empty_like(d["w"])]
+    ref = None
+    for run in range(10):
+        for o in outs:
+            o.fill_(7)
+        y, dx, dwg, dwu, dwd, dtw = outs
+        F.run_schedule(ws, d["ids"])
+        mok.forward(ws.problem, ws.schedule, d["x"], d["w"], d["weights"], y, ws.workspace, ws.fwd_ctx, ws.config)
+        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d["x"], d["w"], d["weights"], ddy, dx, dwg, dwu, dwd,
+                     dtw, ws.workspace, ws.config)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = [o.clone() for o in outs]
+        else:
+            for o, r in zip(outs, ref):
+                assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"run {run} differs"
 
 
 def test_backward_bitwise_deterministic():
