@@ -139,6 +139,9 @@ typedef struct {
   int32_t ring_slots;            /* resolved N_s */
   int32_t n_minibatches;         /* ceil(R / M)  */
   int32_t max_fwd_tiles, max_bwd_tiles, fwd_tile_rows, bwd_tile_rows;
+  size_t arrays;                 /* bytes of the schedule arrays alone, without the
+                                    build's scratch tail: the size
+                                    mok_build_schedule_noalloc needs              */
 } mok_schedule_layout;
 
 /* [host] Library version, major*10000 + minor*100 + patch. */
@@ -173,6 +176,23 @@ mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config*
 mok_status mok_build_schedule(const mok_problem* problem, const mok_config* config,
                               const int32_t* topk_ids,
                               void* schedule, size_t schedule_bytes, void* stream);
+
+/* The same schedule for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): identical results to mok_build_schedule, but the build's
+ * scratch (the per-chunk count table) lives in a static device array of the
+ * library instead of the tail of `schedule`, so schedule_bytes need only be
+ * mok_schedule_layout's `arrays` (passing the full size is fine too).
+ * The array holds 2048 x 513 x 4 bytes (about 4 MiB), one copy per GPU,
+ * kept until the process ends; it covers every supported problem, and a
+ * problem needing more returns MOK_ERR_UNSUPPORTED. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must not run concurrently. Allocates nothing:
+ * no hipMalloc, no library allocation. Errors as mok_build_schedule, plus
+ * MOK_ERR_DEVICE if the array's device address cannot be obtained. */
+mok_status mok_build_schedule_noalloc(const mok_problem* problem, const mok_config* config,
+                                      const int32_t* topk_ids, void* schedule, size_t schedule_bytes,
+                                      void* stream);
 
 /* Forward ([MoK clip] Conclusion and key chart: dispatch -> expert SwiGLU
  * FFN -> combine -> weighted sum). Per minibatch, in order: gate/up grouped

@@ -57,7 +57,7 @@ class ScheduleLayout(ctypes.Structure):
         "mb_tile_start", "n_bwd_tiles", "bwd_tiles", "total")] + [
         (n, ctypes.c_int32) for n in (
             "minibatch_rows", "ring_slots", "n_minibatches", "max_fwd_tiles", "max_bwd_tiles",
-            "fwd_tile_rows", "bwd_tile_rows")]
+            "fwd_tile_rows", "bwd_tile_rows")] + [("arrays", ctypes.c_size_t)]
 
 
 _lib = None
@@ -65,7 +65,7 @@ _lib = None
 EXPORTS = ("mok_version", "mok_status_string", "mok_buffer_sizes", "mok_get_schedule_layout",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
            "mok_router_forward", "mok_router_backward", "mok_trace_enable", "mok_trace_collect",
-           "mok_mxfp8_quantize_transposed", "mok_probe_mfma")
+           "mok_mxfp8_quantize_transposed", "mok_probe_mfma", "mok_build_schedule_noalloc")
 
 
 class TraceStat(ctypes.Structure):
@@ -93,6 +93,8 @@ def lib():
         L.mok_get_schedule_layout.argtypes = [P(Problem), P(Config), P(ScheduleLayout)]
         L.mok_build_schedule.restype = ctypes.c_int
         L.mok_build_schedule.argtypes = [P(Problem), P(Config), vp, vp, sz, vp]
+        L.mok_build_schedule_noalloc.restype = ctypes.c_int
+        L.mok_build_schedule_noalloc.argtypes = [P(Problem), P(Config), vp, vp, sz, vp]
         L.mok_forward.restype = ctypes.c_int
         L.mok_forward.argtypes = [P(Problem), P(Config), vp, vp, vp, P(Weights), vp, vp, vp, sz, vp]
         L.mok_backward.restype = ctypes.c_int
@@ -173,6 +175,14 @@ def build_schedule(problem, topk_ids, schedule, config=None, stream=None):
     _check(lib().mok_build_schedule(ctypes.byref(problem), _cfg(config), _ptr(topk_ids),
                                     _ptr(schedule), schedule.numel() * schedule.element_size(),
                                     _stream(stream)), "mok_build_schedule")
+
+
+def build_schedule_noalloc(problem, topk_ids, schedule, config=None, stream=None):
+    """mok_build_schedule with the build's scratch in the library's static
+    device array (schedule needs only schedule_layout(...).arrays bytes)."""
+    _check(lib().mok_build_schedule_noalloc(ctypes.byref(problem), _cfg(config), _ptr(topk_ids),
+                                            _ptr(schedule), schedule.numel() * schedule.element_size(),
+                                            _stream(stream)), "mok_build_schedule_noalloc")
 
 
 def _weights(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None, w_down_t=None, w_gu_t=None,

@@ -307,6 +307,32 @@ struct TraceScope {
 
 }  // namespace
 
+// ---------------------------------------------------------------- schedule build without a caller scratch
+// The per-chunk count table of the schedule build (hist -> scan -> scatter),
+// for mok_build_schedule_noalloc: a static device array, one copy on every GPU
+// the library runs on, held until the process ends. Its size covers every
+// supported problem (at most 2048 chunks x (512 + 1) buckets of 4 bytes).
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, once per device, and kernels get that pointer.
+constexpr size_t kNoAllocScratchBytes = (size_t)2048 * (kMaxE + 1) * 4;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static mok_status noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOK_ERR_DEVICE;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOK_ERR_DEVICE;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return MOK_OK;
+}
+
 extern "C" {
 
 int32_t mok_version(void) { return kVersion; }
@@ -334,6 +360,31 @@ mok_status mok_buffer_sizes(const mok_problem* problem, const mok_config* config
   return MOK_OK;
 }
 
+mok_status mok_build_schedule_noalloc(const mok_problem* problem, const mok_config* config,
+                                      const int32_t* topk_ids, void* schedule, size_t schedule_bytes,
+                                      void* stream) {
+  TraceCall tc;
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || (r.R > 0 && !topk_ids)) return MOK_ERR_INVALID_ARG;
+  const SchedLayout L = sched_layout(r);
+  if (schedule_bytes < L.chunk_counts) return MOK_ERR_BUFFER_TOO_SMALL;
+  const int64_t chunk = mok_schedule_chunk_rows(r.R);
+  const size_t need = 4 * (size_t)((r.R + chunk - 1) / chunk) * (size_t)(r.E + 1);
+  if (need > kNoAllocScratchBytes) return MOK_ERR_UNSUPPORTED;
+  if ((s = check_device()) != MOK_OK) return s;
+  void* ptr = nullptr;
+  if ((s = noalloc_scratch(&ptr)) != MOK_OK) return s;
+  const mok_sched_ptrs p = sched_ptrs(r, schedule);
+  hipStream_t st = (hipStream_t)stream;
+  // the count table is written in full by the first launch (no clearing needed)
+  MOK_RUN("schedule", mok_launch_schedule(topk_ids, p, (int)r.R, r.E, r.k, r.M, kTileRowsFwd,
+                                          kTileRowsBwd, r.n_mb, r.max_fwd_tiles,
+                                          r.max_bwd_tiles, static_cast<int32_t*>(ptr), st));
+  return MOK_OK;
+}
+
 mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config* config,
                                    mok_schedule_layout* out) {
   if (!out) return MOK_ERR_INVALID_ARG;
@@ -344,7 +395,7 @@ mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config*
   out->status = L.status; out->counts = L.counts; out->offsets = L.offsets;
   out->perm = L.perm; out->dest = L.dest; out->n_fwd_tiles = L.n_fwd;
   out->fwd_tiles = L.fwd_tiles; out->mb_tile_start = L.mb_start; out->n_bwd_tiles = L.n_bwd;
-  out->bwd_tiles = L.bwd_tiles; out->total = L.total;
+  out->bwd_tiles = L.bwd_tiles; out->total = L.total; out->arrays = L.chunk_counts;
   out->minibatch_rows = r.M; out->ring_slots = r.n_slots; out->n_minibatches = r.n_mb;
   out->max_fwd_tiles = r.max_fwd_tiles; out->max_bwd_tiles = r.max_bwd_tiles;
   out->fwd_tile_rows = kTileRowsFwd; out->bwd_tile_rows = kTileRowsBwd;
