@@ -217,34 +217,33 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) 
 }
 
 // One launch covers the tiles of minibatches [m0, m1). Launch grids are 1-D
-// upper bounds; the tile count is read on the device and the logical tile
-// order is XCD-aware (xcd_tile), row-major over (row tile, column tile).
+// upper bounds; the tile count is read on the device and the tile order is
+// XCD-aware (xcd_swizzle: 4 x 8 blocks of row x column tiles per XCD).
 template <bool F8>
 __global__ __launch_bounds__(kThreads, 1) void gateup_kernel(mok_fwd_args a, int m0, int m1, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
   const int t0 = a.mb_tile_start[m0];
-  const int L = xcd_tile((a.mb_tile_start[m1] - t0) * ncol);
-  if (L < 0) return;
-  gateup_tile<F8>(a, lds_raw, t0 + L / ncol, L % ncol);
+  int row, col;
+  if (!xcd_swizzle(a.mb_tile_start[m1] - t0, ncol, row, col)) return;
+  gateup_tile<F8>(a, lds_raw, t0 + row, col);
 }
 
 template <bool F8>
 __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m0, int m1, int ncol) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
   const int t0 = a.mb_tile_start[m0];
-  const int L = xcd_tile((a.mb_tile_start[m1] - t0) * ncol);
-  if (L < 0) return;
-  down_tile<F8>(a, lds_raw, t0 + L / ncol, L % ncol);
+  int row, col;
+  if (!xcd_swizzle(a.mb_tile_start[m1] - t0, ncol, row, col)) return;
+  down_tile<F8>(a, lds_raw, t0 + row, col);
 }
 
 // ================================================================== backward
-// Backward row-tile kernels: 1-D grid, logical tile L = (row tile, column
-// tile) row-major in XCD-aware order; ny receives the column tile.
+// Backward row-tile kernels: 1-D grid over (row tile, column tile) in the
+// XCD-aware order of xcd_swizzle; ny receives the column tile.
 MOK_DEV bool bwd_tile(const mok_bwd_args& a, int ncol, mok_tile& t, int& ny) {
-  const int L = xcd_tile(*a.n_tiles * ncol);
-  if (L < 0) return false;
-  t = a.tiles[L / ncol];
-  ny = L % ncol;
+  int row;
+  if (!xcd_swizzle(*a.n_tiles, ncol, row, ny)) return false;
+  t = a.tiles[row];
   return true;
 }
 
@@ -374,12 +373,12 @@ MOK_DEV void dw_tile(uint8_t* lds_raw, const LA& la, int mlimit, const LB& lb, i
 }
 
 // dWd[e] = sum_p dO[p]^T h[p] = sum_p dy[tok[p]]^T (w_p h[p]) (hb holds w_p h)
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int tiles_per_e) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, int ntm, int ry) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
-  const int L = xcd_tile(a.E * tiles_per_e);
-  if (L < 0) return;
-  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  int e, mt_, nt_;
+  if (!dw_tile_of(a.E, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  const int tl = mt_ * (int)((a.I + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((I + G::BN - 1) / G::BN);
   const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
@@ -392,12 +391,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, in
 }
 
 // [dWg; dWu][e] = sum_p [dA dB][p]^T x[tok[p]]
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, int tiles_per_e) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, int ntm, int ry) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
-  const int L = xcd_tile(a.E * tiles_per_e);
-  if (L < 0) return;
-  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  int e, mt_, nt_;
+  if (!dw_tile_of(a.E, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  const int tl = mt_ * (int)((a.H + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((H + G::BN - 1) / G::BN);
   const int mt = tl / ntn;
@@ -625,12 +624,12 @@ MOK_DEV void dw8_tile(uint8_t* lds_raw, const uint8_t* A, const uint8_t* As, int
   store_bf16_x<kTrDw, G>(lds_raw, acc, mlim, nlim, [&](int r) { return out + (int64_t)r * ldo; });
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, int tiles_per_e) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, int ntm, int ry) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
-  const int L = xcd_tile(a.E * tiles_per_e);
-  if (L < 0) return;
-  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  int e, mt_, nt_;
+  if (!dw_tile_of(a.E, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  const int tl = mt_ * (int)((a.I + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((I + G::BN - 1) / G::BN);
   const int m0 = (tl / ntn) * G::BM, n0 = (tl % ntn) * G::BN;
@@ -643,12 +642,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, i
            a.dwd + (int64_t)e * H * I + (int64_t)m0 * I + n0, I);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu8_kernel(mok_bwd_args a, int tiles_per_e) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dwgu8_kernel(mok_bwd_args a, int ntm, int ry) {
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
-  const int L = xcd_tile(a.E * tiles_per_e);
-  if (L < 0) return;
-  const int e = L / tiles_per_e, tl = L % tiles_per_e;
+  int e, mt_, nt_;
+  if (!dw_tile_of(a.E, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  const int tl = mt_ * (int)((a.H + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((H + G::BN - 1) / G::BN);
   const int mt = tl / ntn;
@@ -671,12 +670,37 @@ unsigned cdivu(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
 }  // namespace
 
-unsigned grid8(int64_t n) { return (unsigned)((n + kXcds - 1) / kXcds * kXcds); }
+// grid of the row-tile kernels (see xcd_swizzle)
+unsigned rt_grid(int64_t max_tiles, int ncol) {
+  return (unsigned)((int64_t)kXcds * ((max_tiles + kXcds - 1) / kXcds) * ncol);
+}
+// blocks of the weight-gradient grids (see dw_tile_of): kXcds = ry x (kXcds/ry)
+// blocks per expert, ry chosen so that the blocks are closest to square
+// without an empty block (an empty block would idle an XCD)
+int dw_ry(int ntm, int ntn) {
+  int best = 1;
+  double bs = 1e30;
+  for (int ry = 1; ry <= kXcds; ry *= 2) {
+    const int cx = kXcds / ry;
+    if (ry > ntm || cx > ntn) continue;
+    const double h = (double)ntm / ry, w = (double)ntn / cx;
+    const double sq = h > w ? h / w : w / h;
+    if (sq < bs) {
+      bs = sq;
+      best = ry;
+    }
+  }
+  return best;
+}
+unsigned dw_grid(int E, int ntm, int ntn, int ry) {
+  const int cx = kXcds / ry;
+  return (unsigned)((int64_t)kXcds * E * ((ntm + ry - 1) / ry) * ((ntn + cx - 1) / cx));
+}
 
 hipError_t mok_launch_gateup(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                              hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN / 2);
-  const dim3 grid(grid8((int64_t)max_tiles * ncol));
+  const dim3 grid(rt_grid(max_tiles, ncol));
   if (mxfp8) hipLaunchKernelGGL(gateup_kernel<true>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   else hipLaunchKernelGGL(gateup_kernel<false>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   return hipGetLastError();
@@ -685,7 +709,7 @@ hipError_t mok_launch_gateup(const mok_fwd_args& a, int m0, int m1, int max_tile
 hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles, bool mxfp8,
                            hipStream_t st) {
   const int ncol = (int)cdivu(a.H, G256::BN);
-  const dim3 grid(grid8((int64_t)max_tiles * ncol));
+  const dim3 grid(rt_grid(max_tiles, ncol));
   if (mxfp8) hipLaunchKernelGGL(down_kernel<true>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   else hipLaunchKernelGGL(down_kernel<false>, grid, dim3(kThreads), 0, st, a, m0, m1, ncol);
   return hipGetLastError();
@@ -694,48 +718,52 @@ hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles,
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN);
-  hipLaunchKernelGGL(bwd_dh_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  hipLaunchKernelGGL(bwd_dh_kernel, dim3(rt_grid(a.max_tiles, ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dh8(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN);
-  hipLaunchKernelGGL(bwd_dh8_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  hipLaunchKernelGGL(bwd_dh8_kernel, dim3(rt_grid(a.max_tiles, ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dx8(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.H, G256::BN);
-  hipLaunchKernelGGL(bwd_dx8_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  hipLaunchKernelGGL(bwd_dx8_kernel, dim3(rt_grid(a.max_tiles, ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwd8(const mok_bwd_args& a, hipStream_t st) {
-  const int tpe = (int)(cdivu(a.H, G256::BM) * cdivu(a.I, G256::BN));
-  hipLaunchKernelGGL(bwd_dwd8_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
+  const int ntm = (int)(cdivu(a.H, G256::BM)), ntn = (int)cdivu(a.I, G256::BN);
+  hipLaunchKernelGGL(bwd_dwd8_kernel, dim3(dw_grid(a.E, ntm, ntn, dw_ry(ntm, ntn))), dim3(kThreads), 0, st, a, ntm,
+                     dw_ry(ntm, ntn));
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwgu8(const mok_bwd_args& a, hipStream_t st) {
-  const int tpe = (int)(2 * cdivu(a.I, G256::BM) * cdivu(a.H, G256::BN));
-  hipLaunchKernelGGL(bwd_dwgu8_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
+  const int ntm = (int)(2 * cdivu(a.I, G256::BM)), ntn = (int)cdivu(a.H, G256::BN);
+  hipLaunchKernelGGL(bwd_dwgu8_kernel, dim3(dw_grid(a.E, ntm, ntn, dw_ry(ntm, ntn))), dim3(kThreads), 0, st, a, ntm,
+                     dw_ry(ntm, ntn));
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dx(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.H, G256::BN);
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3(grid8((int64_t)a.max_tiles * ncol)), dim3(kThreads), 0, st, a, ncol);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(rt_grid(a.max_tiles, ncol)), dim3(kThreads), 0, st, a, ncol);
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwd(const mok_bwd_args& a, hipStream_t st) {
-  const int tpe = (int)(cdivu(a.H, G256::BM) * cdivu(a.I, G256::BN));
-  hipLaunchKernelGGL(bwd_dwd_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
+  const int ntm = (int)(cdivu(a.H, G256::BM)), ntn = (int)cdivu(a.I, G256::BN);
+  hipLaunchKernelGGL(bwd_dwd_kernel, dim3(dw_grid(a.E, ntm, ntn, dw_ry(ntm, ntn))), dim3(kThreads), 0, st, a, ntm,
+                     dw_ry(ntm, ntn));
   return hipGetLastError();
 }
 
 hipError_t mok_launch_bwd_dwgu(const mok_bwd_args& a, hipStream_t st) {
-  const int tpe = (int)(2 * cdivu(a.I, G256::BM) * cdivu(a.H, G256::BN));
-  hipLaunchKernelGGL(bwd_dwgu_kernel, dim3(grid8((int64_t)a.E * tpe)), dim3(kThreads), 0, st, a, tpe);
+  const int ntm = (int)(2 * cdivu(a.I, G256::BM)), ntn = (int)cdivu(a.H, G256::BN);
+  hipLaunchKernelGGL(bwd_dwgu_kernel, dim3(dw_grid(a.E, ntm, ntn, dw_ry(ntm, ntn))), dim3(kThreads), 0, st, a, ntm,
+                     dw_ry(ntm, ntn));
   return hipGetLastError();
 }
