@@ -101,6 +101,14 @@ def parse():
     ap.add_argument("--ring-slots", type=int, default=0)
     ap.add_argument("--only-step", action="store_true",
                     help="the headline step only (no other legs); for counter runs")
+    ap.add_argument("--step-dtype", choices=("bf16", "mxfp8"), default="bf16",
+                    help="with --only-step: run the step in MXFP8 (for counter runs of the MXFP8 kernels)")
+    ap.add_argument("--kernel-stats-record", metavar="STATS_CSV",
+                    help="write the kernel-duration summary from a rocprofv3 --kernel-trace --stats "
+                         "run of --only-step (its *_kernel_stats.csv) and exit; needs no GPU")
+    ap.add_argument("--mfma-record", metavar="PMC_CSV",
+                    help="write the MFMA-utilisation summary from a rocprofv3 --pmc run of --only-step "
+                         "(counter_collection.csv with the counters named in the summary) and exit")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write the GEMM traffic record from four rocprofv3 counter_collection.csv "
                          "files (FETCH_SIZE and WRITE_SIZE of a --only-step run, then of a 1 GiB "
@@ -217,6 +225,120 @@ def write_traffic_record(args):
     lines += ["", "Machine-readable record (bench.py reads the last line; it reports the traffic only while "
               "the kernel sources hash to `sources_sha256` and the workload matches):", "", json.dumps(rec)]
     path = traffic_file(p)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
+
+
+def _profile_cmd(args, extra_pmc=None, trace=False):
+    tail = (f"--only-step --config {args.config}" + (" --step-dtype mxfp8" if args.step_dtype == "mxfp8" else "")
+            + (f" --minibatch-rows {args.minibatch_rows}" if args.minibatch_rows else ""))
+    what = "--kernel-trace --stats" if trace else f"--pmc {extra_pmc}"
+    steps = "--steps 5 --warmup 2" if trace else "--steps 2 --warmup 1"
+    return (f"rocprofv3 {what} -d <d> -o run -f csv -- python3 /root/repo/bench.py {steps} --cpu-tokens 0 {tail}")
+
+
+def _short(name):
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def write_kernel_stats_record(args):
+    """Kernel durations of the step from a rocprofv3 --kernel-trace --stats
+    run, as a markdown summary under profiles/."""
+    import csv
+    from synthetic import CONFIGS
+    p = CONFIGS[args.config]
+    rows = list(csv.DictReader(open(args.kernel_stats_record)))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    tag = workload_tag(p) + ("_mxfp8step" if args.step_dtype == "mxfp8" else "")
+    flops = {"gateup_kernel": 4, "down_kernel": 2, "bwd_dh_kernel": 2, "bwd_dwd_kernel": 2, "bwd_dwgu_kernel": 4,
+             "bwd_dx_kernel": 4, "bwd_dh8_kernel": 2, "bwd_dwd8_kernel": 2, "bwd_dwgu8_kernel": 4,
+             "bwd_dx8_kernel": 4}
+    lines = [f"# Kernel durations: MoE layer step ({args.step_dtype}), {p.name}", "",
+             "Command (repository root on an MI355X, ROCm 7.2):", "", "```", "cd /tmp && export TMPDIR=/tmp",
+             _profile_cmd(args, trace=True),
+             f"python3 bench.py --config {args.config}" + (" --step-dtype mxfp8" if args.step_dtype == "mxfp8" else "")
+             + " --kernel-stats-record <d>/run_kernel_stats.csv", "```", "",
+             "2 warm-up + 5 timed + 5 traced steps under the profiler (every launch of the run). TFLOP/s = "
+             "algorithmic FLOPs per launch (routed rows only) / average duration; launches per step: "
+             "gate/up and down once per ring group of minibatches, the others once.", "",
+             "| kernel | calls | average ms | total ms | share | TFLOP/s per launch |", "|---|---:|---:|---:|---:|---:|"]
+    rec = {}
+    steps = sum(int(r["Calls"]) for r in rows if "sched_scan_kernel" in r["Name"])   # one per step
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        n = _short(r["Name"])
+        avg = float(r["AverageNs"]) / 1e6
+        key = n.split("<")[0]
+        tf = ""
+        if key in flops:
+            nl = int(r["Calls"]) / steps               # launches per step
+            tf = f"{flops[key] * p.R * p.H * p.I / nl / (avg * 1e-3) / 1e12:.1f}"
+        lines.append(f"| `{n}` | {r['Calls']} | {avg:.4f} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f}% | {tf} |")
+        rec[n] = {"calls": int(r["Calls"]), "avg_ms": round(avg, 5)}
+    lines += ["", json.dumps({"workload": p.name, "step_dtype": args.step_dtype,
+                              "sources_sha256": kernel_sources_sha256(), "kernels": rec})]
+    path = os.path.join(ROOT, "profiles", f"moe_kernel_stats_{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_VALU_MFMA_BUSY_CYCLES "
+                 "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def write_mfma_record(args):
+    """MFMA busy share, executed vs algorithmic FLOPs and clock of each GEMM
+    kernel from one rocprofv3 counter pass."""
+    import csv
+    from synthetic import CONFIGS
+    p = CONFIGS[args.config]
+    per = {}
+    for r in csv.DictReader(open(args.mfma_record)):
+        d = int(r["Dispatch_Id"])
+        e = per.setdefault(d, {"name": r["Kernel_Name"], "dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    flops = {"gateup_kernel": 4, "down_kernel": 2, "bwd_dh_kernel": 2, "bwd_dwd_kernel": 2, "bwd_dwgu_kernel": 4,
+             "bwd_dx_kernel": 4, "bwd_dh8_kernel": 2, "bwd_dwd8_kernel": 2, "bwd_dwgu8_kernel": 4,
+             "bwd_dx8_kernel": 4}
+    agg = {}
+    steps = sum(1 for e in per.values() if "sched_scan_kernel" in e["name"])          # one per step
+    for e in per.values():
+        n = _short(e["name"])
+        if n.split("<")[0] not in flops:
+            continue
+        a = agg.setdefault(n, {"n": 0, "busy": 0.0, "gui": 0.0, "mops": 0.0, "dur": 0.0})
+        a["n"] += 1
+        a["busy"] += e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a["gui"] += e.get("GRBM_GUI_ACTIVE", 0.0) / 8.0            # summed over the 8 XCDs
+        a["mops"] += e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        a["dur"] += e["dur"]
+    tag = workload_tag(p) + ("_mxfp8step" if args.step_dtype == "mxfp8" else "")
+    launches = {n: a["n"] for n, a in agg.items()}
+    lines = [f"# MFMA utilisation of the grouped GEMMs: MoE layer step ({args.step_dtype}), {p.name}", "",
+             "Command (repository root on an MI355X, ROCm 7.2; one counter pass):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp", _profile_cmd(args, extra_pmc=MFMA_COUNTERS),
+             f"python3 bench.py --config {args.config}" + (" --step-dtype mxfp8" if args.step_dtype == "mxfp8" else "")
+             + " --mfma-record <d>/run_counter_collection.csv", "```", "",
+             "Per kernel, summed over its dispatches (rocprofv3 sums each counter over its hardware "
+             "instances; GRBM_GUI_ACTIVE over the 8 XCDs, so it is divided by 8):", "",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs): the share of "
+             "SIMD-cycles the matrix cores were busy at the clock the kernel ran;",
+             "- executed GFLOP = MOPS x 512 per dispatch; algorithmic GFLOP = routed rows only; useful = "
+             "algorithmic / executed;",
+             "- clock = GRBM_GUI_ACTIVE per XCD / dispatch duration (timestamps of the counter run).", "",
+             "| kernel | dispatches | MFMA busy | executed GFLOP | algorithmic GFLOP | useful | clock GHz |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for n, a in agg.items():
+        nl = a["n"]
+        ex = a["mops"] * 512 / nl / 1e9
+        al = flops[n.split("<")[0]] * p.R * p.H * p.I / (launches[n] / steps) / 1e9
+        busy = a["busy"] / (a["gui"] * 1024) if a["gui"] else 0.0
+        clk = a["gui"] / a["dur"] if a["dur"] else 0.0
+        lines.append(f"| `{n}` | {nl} | {100 * busy:.1f}% | {ex:.1f} | {al:.1f} | {100 * al / ex if ex else 0:.1f}% | "
+                     f"{clk:.2f} |")
+    path = os.path.join(ROOT, "profiles", f"moe_gemm_mfma_util_{tag}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
@@ -426,6 +548,14 @@ def main():
     if args.traffic_record:
         write_traffic_record(args)
         return
+    if args.kernel_stats_record:
+        write_kernel_stats_record(args)
+        return
+    if args.mfma_record:
+        write_mfma_record(args)
+        return
+    if args.step_dtype == "mxfp8" and not args.only_step:
+        raise SystemExit("--step-dtype mxfp8 is for counter runs: use it with --only-step")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path)", file=sys.stderr)
@@ -450,7 +580,10 @@ def main():
 
     p = CONFIGS[args.config]
     d = Dev(p)
-    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True, **cfg)
+    mx_step = args.step_dtype == "mxfp8"
+    ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True,
+                         dtype=mok.MOK_MXFP8 if mx_step else mok.MOK_BF16, **cfg)
+    step_w = (F.quantize_weights(*d.weights) + F.quantize_weights_backward(*d.weights)) if mx_step else d.weights
     y = torch.empty_like(d.x)
     gx = torch.empty_like(d.x)
     gwg, gwu, gwd = (torch.empty_like(t) for t in d.weights)
@@ -459,8 +592,8 @@ def main():
 
     def step():
         mok.build_schedule(ws.problem, d.ids, ws.schedule, ws.config, stream)
-        mok.forward(ws.problem, ws.schedule, d.x, d.w, d.weights, y, ws.workspace, ws.fwd_ctx, ws.config, stream)
-        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d.x, d.w, d.weights, d.dy, gx, gwg, gwu, gwd, gtw,
+        mok.forward(ws.problem, ws.schedule, d.x, d.w, step_w, y, ws.workspace, ws.fwd_ctx, ws.config, stream)
+        mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d.x, d.w, step_w, d.dy, gx, gwg, gwu, gwd, gtw,
                      ws.workspace, ws.config, stream)
 
     log(f"[bench] warmup {W} steps")
@@ -490,8 +623,9 @@ def main():
     achieved = dom_flops_per_launch / (dom_avg_ms * 1e-3) / 1e12
     mb_rows = mok.schedule_layout(ws.problem, ws.config).minibatch_rows
     traffic, traffic_src = measured_traffic(dom, p, mb_rows)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+    peak = PEAK_FP8_TFLOPS if mx_step else PEAK_BF16_TFLOPS
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch", "traffic_source": traffic_src,
                 "flops_per_launch": dom_flops_per_launch, "avg_launch_ms": round(dom_avg_ms, 5),
                 "timing": "HIP events around each launch on the launch stream (library tracer), separate pass"}
@@ -520,7 +654,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8" if mx_step else "bf16",
         "data": "synthetic (seeded; random-init expert weights)",
         "config": {"workload": f"MoE SwiGLU layer fwd+bwd, bf16: {p.name}", "T": p.T, "H": H, "I": I,
                    "E": p.E, "topk": p.k, "routed_rows": R, "minibatch_rows": mb_rows,
