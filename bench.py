@@ -109,6 +109,9 @@ def parse():
     ap.add_argument("--mfma-record", metavar="PMC_CSV",
                     help="write the MFMA-utilisation summary from a rocprofv3 --pmc run of --only-step "
                          "(counter_collection.csv with the counters named in the summary) and exit")
+    ap.add_argument("--stall-record", nargs=2, metavar=("PMC_A_CSV", "PMC_B_CSV"),
+                    help="write the stall breakdown of the GEMMs from two rocprofv3 --pmc runs of "
+                         "--only-step (the counter sets named in the summary) and exit; needs no GPU")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="write the GEMM traffic record from four rocprofv3 counter_collection.csv "
                          "files (FETCH_SIZE and WRITE_SIZE of a --only-step run, then of a 1 GiB "
@@ -344,6 +347,88 @@ def write_mfma_record(args):
     print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
 
 
+STALL_COUNTERS_A = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+                    "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE")
+STALL_COUNTERS_B = ("SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_INST_LEVEL_VMEM SQ_INSTS_VMEM_RD "
+                    "SQ_LDS_DATA_FIFO_FULL SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU TA_TA_BUSY "
+                    "TA_DATA_STALLED_BY_TC_CYCLES TCP_TCC_READ_REQ_LATENCY TCP_TCC_READ_REQ "
+                    "TCP_PENDING_STALL_CYCLES TCP_READ_TAGCONFLICT_STALL_CYCLES GRBM_GUI_ACTIVE")
+GEMM_PREFIXES = ("gateup_kernel", "down_kernel", "bwd_dh", "bwd_dwd", "bwd_dwgu", "bwd_dx")
+
+
+def _pmc_per_kernel(path):
+    """Counters of one rocprofv3 --pmc csv, summed per kernel over its
+    dispatches (each counter summed over its hardware instances)."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        e = per.setdefault(d, {"name": _short(r["Kernel_Name"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for e in per.values():
+        if not e["name"].startswith(GEMM_PREFIXES):
+            continue
+        a = agg.setdefault(e["name"], {"n": 0})
+        a["n"] += 1
+        for k, v in e.items():
+            if k != "name":
+                a[k] = a.get(k, 0.0) + v
+    return agg
+
+
+def write_stall_record(args):
+    """Where the GEMM wavefronts and their memory path spend their cycles,
+    from two rocprofv3 counter passes of the step."""
+    from synthetic import CONFIGS
+    p = CONFIGS[args.config]
+    A, B = (_pmc_per_kernel(f) for f in args.stall_record)
+    tag = workload_tag(p) + ("_mxfp8step" if args.step_dtype == "mxfp8" else "")
+    dt = " --step-dtype mxfp8" if args.step_dtype == "mxfp8" else ""
+    lines = [f"# Stall breakdown of the grouped GEMMs: MoE layer step ({args.step_dtype}), {p.name}", "",
+             "Commands (repository root on an MI355X, ROCm 7.2; two counter passes, each a run of its own):",
+             "", "```", "cd /tmp && export TMPDIR=/tmp",
+             _profile_cmd(args, extra_pmc=STALL_COUNTERS_A).replace("<d>", "<a>"),
+             _profile_cmd(args, extra_pmc=STALL_COUNTERS_B).replace("<d>", "<b>"),
+             f"python3 bench.py --config {args.config}{dt} --stall-record <a>/run_counter_collection.csv "
+             "<b>/run_counter_collection.csv", "```", "",
+             f"Kernel sources sha256: `{kernel_sources_sha256()}`", "",
+             "Per kernel, summed over its dispatches; GRBM_GUI_ACTIVE is summed over the 8 XCDs and divided "
+             "by 8. Wave shares are of SQ_WAVE_CYCLES (cycles summed over resident waves); unit shares are of "
+             "the kernel's busy cycles times 256 units (one texture address unit and one L1 per CU):", "",
+             "- MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x 1024 SIMDs);",
+             "- wait any / wait inst / wait LDS: SQ_WAIT_ANY, SQ_WAIT_INST_ANY (waiting on an instruction's "
+             "inputs), SQ_WAIT_INST_LDS;",
+             "- VMEM active / LDS active: SQ_ACTIVE_INST_VMEM, SQ_ACTIVE_INST_LDS;",
+             "- bank conflicts per LDS instruction: SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS;",
+             "- TA busy, TA stalled by L1: TA_TA_BUSY, TA_DATA_STALLED_BY_TC_CYCLES;",
+             "- L2 read latency (cycles): TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ; L1 pending stall: "
+             "TCP_PENDING_STALL_CYCLES;",
+             "- VMEM loads in flight per wave: SQ_INST_LEVEL_VMEM / SQ_INSTS_VMEM_RD.", "",
+             "| kernel | dispatches | MFMA busy | wait any | wait inst | wait LDS | VMEM active | LDS active "
+             "| conflicts / LDS inst | TA busy | TA stalled | L2 latency | L1 pending | VMEM in flight |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for n, a in A.items():
+        b = B.get(n)
+        if b is None:
+            continue
+        gui_a, gui_b, wc = a["GRBM_GUI_ACTIVE"] / 8, b["GRBM_GUI_ACTIVE"] / 8, a["SQ_WAVE_CYCLES"]
+        pct = lambda v, d: f"{100 * v / d:.1f}%" if d else "-"   # noqa: E731
+        lines.append(
+            f"| `{n}` | {a['n']:.0f} | {pct(a['SQ_VALU_MFMA_BUSY_CYCLES'], gui_a * 1024)} "
+            f"| {pct(a['SQ_WAIT_ANY'], wc)} | {pct(a['SQ_WAIT_INST_ANY'], wc)} | {pct(a['SQ_WAIT_INST_LDS'], wc)} "
+            f"| {pct(a['SQ_ACTIVE_INST_VMEM'], wc)} | {pct(a['SQ_ACTIVE_INST_LDS'], wc)} "
+            f"| {b['SQ_LDS_BANK_CONFLICT'] / max(b['SQ_INSTS_LDS'], 1):.2f} "
+            f"| {pct(b['TA_TA_BUSY'], gui_b * 256)} | {pct(b['TA_DATA_STALLED_BY_TC_CYCLES'], gui_b * 256)} "
+            f"| {b['TCP_TCC_READ_REQ_LATENCY'] / max(b['TCP_TCC_READ_REQ'], 1):.0f} "
+            f"| {pct(b['TCP_PENDING_STALL_CYCLES'], gui_b * 256)} "
+            f"| {b['SQ_INST_LEVEL_VMEM'] / max(b['SQ_INSTS_VMEM_RD'], 1):.1f} |")
+    path = os.path.join(ROOT, "profiles", f"moe_gemm_stalls_{tag}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(p, x, ids, w, wg, wu, wd, dy, n_tok):
     """The fp64 oracle (as it stands) on the first n_tok tokens of the same
@@ -547,6 +632,9 @@ def main():
     args = parse()
     if args.traffic_record:
         write_traffic_record(args)
+        return
+    if args.stall_record:
+        write_stall_record(args)
         return
     if args.kernel_stats_record:
         write_kernel_stats_record(args)
