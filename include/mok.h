@@ -63,9 +63,15 @@ typedef enum {
 
 typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
 
-/* Status word bits written by mok_build_schedule (read it whenever you like). */
+/* Status word bits, written by mok_build_schedule (and the second by
+ * mok_forward with driver 2); read the word after the stream has passed the
+ * call. */
 #define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
-#define MOK_STATUS_WATCHDOG      0x2   /* reserved (persistent driver, not provided) */
+#define MOK_STATUS_WATCHDOG      0x2   /* driver 2 gave up: a wait between its
+                                          tiles passed its time limit (2 s), or
+                                          the schedule's tile table failed its
+                                          checks; y and fwd_ctx are incomplete.
+                                          Set by mok_forward (driver 2).        */
 
 /* Problem shape. Supported: T >= 0, 1 <= topk <= E <= 512, T*topk < 2^31,
  * H and I multiples of 128. dtype MOK_MXFP8 selects the MXFP8 forward and
@@ -96,8 +102,17 @@ typedef struct {
   int32_t driver;                /* 0 = default (= 1), 1 = one launch per
                                     stage (gate/up, down) per ring group of
                                     N_s minibatches,
-                                    2 = one persistent launch for all minibatches
-                                    (not provided: MOK_ERR_UNSUPPORTED).          */
+                                    2 = one persistent launch for all minibatches:
+                                    a resident grid takes the gate/up and down
+                                    tiles from per-XCD queues, minibatch after
+                                    minibatch, the tiles waking each other
+                                    through device counters and a ring slot
+                                    reused once the down tiles that read it
+                                    are done ([MoK clip] Key points 3-5).
+                                    Results are bitwise those of driver 1.
+                                    Runs alone on the device: kernels of other
+                                    streams that hold CUs for long can make its
+                                    waits give up (MOK_STATUS_WATCHDOG).       */
 } mok_config;
 
 typedef struct {
@@ -205,7 +220,9 @@ mok_status mok_build_schedule_noalloc(const mok_problem* problem, const mok_conf
  * expert outputs and the gate/up pre-activations (bf16). MXFP8 ([MoK card]
  * "Core concepts": weights pre-quantized with mok_mxfp8_quantize): x rows are
  * quantized along H (once per token) and h along I the same way on the fly;
- * accumulation is fp32, y is bf16. */
+ * accumulation is fp32, y is bf16. With config->driver == 2 the call may set
+ * MOK_STATUS_WATCHDOG in the schedule's status word (the only write to the
+ * schedule). */
 mok_status mok_forward(const mok_problem* problem, const mok_config* config,
                        const void* schedule, const void* x, const float* topk_w,
                        const mok_weights* weights, void* y, void* fwd_ctx,

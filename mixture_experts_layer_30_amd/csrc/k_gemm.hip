@@ -12,6 +12,7 @@
 // Tile machinery (LDS layout, loaders, MFMA stage) lives in gemm_core.h.
 #include "gemm_core.h"
 #include "mok_launch.h"
+#include "persist_plan.h"
 
 using namespace mok;
 
@@ -235,6 +236,154 @@ __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m
   int row, col;
   if (!xcd_swizzle(a.mb_tile_start[m1] - t0, ncol, row, col)) return;
   down_tile<F8>(a, lds_raw, t0 + row, col);
+}
+
+// ================================================================== persistent driver
+// One launch runs the forward's gate/up and down tiles (gateup_tile and
+// down_tile, unchanged) as items taken from per-XCD queues in the order of
+// persist_plan.h, which also states why every wait ends. Completion travels
+// through counters: a U item adds one to its row tile's counter, a D item to
+// its minibatch's; a D item waits for all U items of its row tile, a U item
+// of minibatch m >= N_s for all D items of minibatch m - N_s, the previous
+// user of its ring slot.
+//
+// Bounded by construction: each workgroup's loop ends when its queue is
+// exhausted (tickets only grow), a wait gives up after ps.spin_limit ticks
+// of the real-time counter, and a give-up (or a tile table that fails the
+// checks below) sets ps.give_up_bit in the status word and a stop flag that
+// ends every workgroup's loop at its next item. The outputs are then
+// incomplete; the status word says so.
+//
+// Visibility: a finishing item writes its results back to memory visible to
+// every CU (agent-scope release) before its counter moves; a waiting item
+// invalidates its caches (agent-scope acquire) after its counter is reached.
+// The U and D items of one row tile share a queue, so h stays within one
+// XCD's L2; only the slot-reuse waits cross XCDs, and they guard writes.
+
+MOK_DEV bool persist_wait(const int* c, int target, int* stop, const mok_persist_args& ps, int* s_ok) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          ok = 0;
+          break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > ps.spin_limit) {
+          __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    *s_ok = ok;
+  }
+  __syncthreads();
+  const bool ok = *s_ok != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return ok;
+}
+
+MOK_DEV void persist_signal(int* c) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's stores, written back
+  __builtin_amdgcn_s_waitcnt(0);                       // ... and the write-back finished
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tiles run as calls: inlined into the item loop, the lane-dependent
+// address arithmetic of both tile kinds is hoisted out of the loop and kept
+// live across it, and the registers spill inside the main loops. A call keeps
+// each tile's code as in its one-stage kernel. The kernel passes its kernarg
+// segment pointer (valid only in the kernel itself: the call convention does
+// not hand it to callees, where the builtin yields a null pointer) and the
+// callee reads the forward arguments there (they come first) with scalar
+// loads; the LDS goes in as an LDS pointer. Neither goes through private
+// memory.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef const __attribute__((address_space(4))) mok_fwd_args* fwd_args_cptr;
+
+MOK_DEV const mok_fwd_args& persist_fwd_args(fwd_args_cptr ap) {
+  // the pointer arrives in vector registers; it is the same in every lane
+  const uint64_t v = (uint64_t)ap;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return *(const mok_fwd_args*)(fwd_args_cptr)(((uint64_t)hi << 32) | lo);
+}
+
+template <bool F8>
+__device__ __noinline__ void persist_gateup(fwd_args_cptr ap, lds_u8* lds, int ti, int col) {
+  gateup_tile<F8>(persist_fwd_args(ap), (uint8_t*)lds, ti, col);
+}
+
+template <bool F8>
+__device__ __noinline__ void persist_down(fwd_args_cptr ap, lds_u8* lds, int ti, int col) {
+  down_tile<F8>(persist_fwd_args(ap), (uint8_t*)lds, ti, col);
+}
+
+template <bool F8>
+__global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_args a, mok_persist_args ps) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
+  __shared__ int s_ticket, s_ok;
+  const int q = (int)blockIdx.x % kPlanQueues;
+  PersistPlan P;
+  P.mbs = a.mb_tile_start;
+  P.n_mb = a.n_mb;
+  P.n_slots = a.n_slots;
+  P.ntu = (int)((a.I + G256::BN / 2 - 1) / (G256::BN / 2));
+  P.ntd = (int)((a.H + G256::BN - 1) / G256::BN);
+  // the kernel's own arguments, for the tile calls: `a` is the first one
+  const fwd_args_cptr ap = (fwd_args_cptr)__builtin_amdgcn_kernarg_segment_ptr();
+  int* stop = ps.ctr + kPlanQueues;
+  int* ddone = ps.ctr + kPlanQueues + 1;
+  int* udone = ddone + a.n_mb;
+
+  // the tile table (written by the schedule) must fit the bounds the counters
+  // and the host's item count were sized for; every workgroup reads the same
+  // table and reaches the same verdict
+  bool valid = P.mbs[0] == 0 && P.mbs[a.n_mb] <= ps.max_tiles;
+  for (int m = 0; m < a.n_mb && valid; ++m) {
+    const int n = P.nr(m);
+    valid = n >= 0 && n <= ps.max_mb_tiles;
+  }
+  if (!valid) {
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  PlanCursor cur;
+  plan_cursor_init(cur);
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int t = -1;
+      if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        t = __hip_atomic_fetch_add(ps.ctr + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ticket = t;
+    }
+    __syncthreads();
+    const int t = s_ticket;
+    __syncthreads();                                   // s_ticket is free for the next item
+    PlanItem it;
+    if (t < 0 || !plan_item(P, cur, q, t, it)) break;
+    if (it.down) {
+      if (!persist_wait(udone + it.ti, P.ntu, stop, ps, &s_ok)) break;
+      persist_down<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
+      persist_signal(ddone + it.m);
+    } else {
+      if (it.m >= a.n_slots) {
+        const int mp = it.m - a.n_slots;
+        if (!persist_wait(ddone + mp, (int)P.down_items(mp), stop, ps, &s_ok)) break;
+      }
+      persist_gateup<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
+      persist_signal(udone + it.ti);
+    }
+  }
 }
 
 // ================================================================== backward
@@ -715,6 +864,14 @@ hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles,
   return hipGetLastError();
 }
 
+
+hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, const mok_persist_args& ps, int grid,
+                                     bool mxfp8, hipStream_t st) {
+  if (grid <= 0 || grid % kPlanQueues != 0) return hipErrorInvalidValue;
+  if (mxfp8) hipLaunchKernelGGL(fwd_persistent_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, ps);
+  else hipLaunchKernelGGL(fwd_persistent_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a, ps);
+  return hipGetLastError();
+}
 
 hipError_t mok_launch_bwd_dh(const mok_bwd_args& a, hipStream_t st) {
   const int ncol = (int)cdivu(a.I, G256::BN);

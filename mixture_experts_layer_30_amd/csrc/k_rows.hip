@@ -359,9 +359,16 @@ __global__ __launch_bounds__(256) void token_offsets_kernel(const int32_t* __res
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t n16) {
+// clears bytes [0, bytes) of a 16-byte aligned buffer: 16-byte stores, the
+// last partial unit byte by byte
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, int64_t bytes) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n16) p[i] = make_uint4(0, 0, 0, 0);
+  if (16 * i + 16 <= bytes) {
+    p[i] = make_uint4(0, 0, 0, 0);
+  } else if (16 * i < bytes) {
+    uint8_t* b = reinterpret_cast<uint8_t*>(p + i);
+    for (int64_t j = 0; j < bytes - 16 * i; ++j) b[j] = 0;
+  }
 }
 
 inline unsigned grid_for(int64_t n, int64_t per_block) {
@@ -451,8 +458,8 @@ hipError_t mok_launch_token_offsets(const int32_t* offsets, int E, int64_t R, in
 }
 
 hipError_t mok_launch_zero(void* p, int64_t bytes, hipStream_t st) {
-  const int64_t n16 = bytes / 16;
-  if (n16 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(n16, 256)), dim3(256), 0, st, (uint4*)p, n16);
+  if (bytes <= 0) return hipSuccess;
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for((bytes + 15) / 16, 256)), dim3(256), 0, st, (uint4*)p, bytes);
   return hipGetLastError();
 }

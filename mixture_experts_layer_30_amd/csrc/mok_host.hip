@@ -17,6 +17,7 @@ namespace {
 constexpr int32_t kVersion = 100;   // 0.1.0
 constexpr int kMaxE = kMaxExperts;
 constexpr size_t kAlign = 256;
+constexpr uint64_t kPersistWaitSeconds = 2;   // a persistent-driver wait gives up after this long
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -123,7 +124,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
 // Workspace carve-up. Forward and backward never run inside one call, so
 // they share the same bytes.
 struct FwdWs {
-  size_t ring_h, ring_hs, obuf, xq, xqs, total;
+  size_t ring_h, ring_hs, obuf, xq, xqs, ctr, total;
 };
 struct BwdWs {
   size_t dab, hb, dxrows;
@@ -141,6 +142,8 @@ FwdWs fwd_ws(const Resolved& r) {
   w.obuf = o;    o = align_up(o + (size_t)r.R * 2 * r.H);
   w.xq = o;      o = align_up(o + (r.mx ? (size_t)r.T * r.H : 0));
   w.xqs = o;     o = align_up(o + (r.mx ? (size_t)r.T * (r.H / 32) : 0));
+  // completion counters of the persistent driver (driver 2)
+  w.ctr = o;     o = align_up(o + 4 * (size_t)mok_persist_counters(r.n_mb, r.max_fwd_tiles));
   w.total = o;
   return w;
 }
@@ -196,8 +199,9 @@ size_t ctx_bytes(const Resolved& r) { return ctx_layout(r).total; }
 // gfx950 check and compute-unit count, once per device (device properties
 // only; no device memory is touched).
 int g_cus[64] = {0};
+int g_wclk_khz[64] = {0};   // rate of the device's 64-bit real-time counter
 
-mok_status check_device(int* cus = nullptr) {
+mok_status check_device(int* cus = nullptr, int* wclk_khz = nullptr) {
   static std::mutex mu;
   static int state[64] = {0};   // 0 unknown, 1 ok, 2 bad
   int dev = 0;
@@ -208,8 +212,13 @@ mok_status check_device(int* cus = nullptr) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOK_ERR_DEVICE;
     state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_cus[dev] = prop.multiProcessorCount;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      khz = 100000;
+    g_wclk_khz[dev] = khz;
   }
   if (cus) *cus = g_cus[dev];
+  if (wclk_khz) *wclk_khz = g_wclk_khz[dev];
   return state[dev] == 1 ? MOK_OK : MOK_ERR_DEVICE;
 }
 
@@ -432,13 +441,16 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
-  // The persistent minibatch kernel (driver 2) is not provided: its first
-  // version did not complete on the device and the cause was not established.
-  if (r.driver == 2) return MOK_ERR_UNSUPPORTED;
   const FwdWs W = fwd_ws(r);
   if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
-  int cus = 0;
-  if ((s = check_device(&cus)) != MOK_OK) return s;
+  int cus = 0, wclk_khz = 0;
+  if ((s = check_device(&cus, &wclk_khz)) != MOK_OK) return s;
+  // persistent driver: tickets (int32) per queue stay below 2^31
+  const int64_t ntu = cdiv(r.I, 128), ntd = cdiv(r.H, 256);
+  const int max_mb_tiles = (int)std::min<int64_t>(cdiv(r.M, kTileRowsFwd) + r.E + 1, r.max_fwd_tiles);
+  if (r.driver == 2 && ((int64_t)r.max_fwd_tiles * (ntu + ntd) + cus >= ((int64_t)1 << 31) ||
+                        (int64_t)max_mb_tiles * ntd >= ((int64_t)1 << 31)))
+    return MOK_ERR_UNSUPPORTED;
   if (r.T == 0) return MOK_OK;
   hipStream_t st = (hipStream_t)stream;
   const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
@@ -470,6 +482,25 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
                                                           ws + W.xq, ws + W.xqs, st));
     a.x = ws + W.xq;
     a.xs = ws + W.xqs;
+  }
+  if (r.driver == 2) {
+    // [MoK clip] Key points bullets 3-5: one resident grid consumes the
+    // minibatches in order through the ring, the stages waking each other
+    // through counters (fwd_persistent_kernel; the plan in persist_plan.h).
+    // The counters are cleared by a fill kernel on the same stream.
+    mok_persist_args ps;
+    ps.ctr = reinterpret_cast<int*>(ws + W.ctr);
+    ps.status = sp.status;
+    ps.give_up_bit = MOK_STATUS_WATCHDOG;
+    ps.max_tiles = r.max_fwd_tiles;
+    ps.max_mb_tiles = max_mb_tiles;
+    ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
+    const int grid = std::max(1, cus / 8) * 8;
+    MOK_RUN("persist_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.n_mb, r.max_fwd_tiles), st));
+    MOK_RUN("persistent_fwd", mok_launch_fwd_persistent(a, ps, grid, r.mx, st));
+    MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
+                               static_cast<bf16_t*>(y), st));
+    return MOK_OK;
   }
   // Minibatches go through the ring N_s at a time: the group [m0, m1) with
   // m0 a multiple of N_s occupies slots 0 .. m1-m0-1, i.e. one contiguous

@@ -123,9 +123,6 @@ def test_calls_reject_bad_arguments_before_any_launch():
     wm = mok.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
     assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(wm), fake,
                           fake, fake, fake, fake, fake, fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
-    # the persistent minibatch driver is switched off
-    assert L.mok_forward(ctypes.byref(prob), ctypes.byref(mok.make_config(driver=2)), fake, fake,
-                         fake, ctypes.byref(w), fake, None, fake, ws, None) == mok.MOK_ERR_UNSUPPORTED
     # quantize: K must be a multiple of 32
     assert L.mok_mxfp8_quantize(fake, 4, 48, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_mxfp8_quantize(fake, -1, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG

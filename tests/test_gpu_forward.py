@@ -112,18 +112,6 @@ def test_full_size_forward_sampled(cfg_id):
     assert_close_bf16(got, ref, f"y[sampled] cfg{cfg_id}")
 
 
-@pytest.mark.skip(reason="persistent minibatch kernel (driver=2) is not provided: its first version "
-                         "did not complete on the device, the cause was not established, and the "
-                         "kernel was removed; mok_forward returns MOK_ERR_UNSUPPORTED for driver=2")
-def test_persistent_driver_matches_launch_per_minibatch():
-    import torch
-    p = problem(37, 256, 256, 5, 2, seed=11)
-    d = device_inputs(p)
-    y1, _ = gpu_forward(p, d, driver=1)
-    y2, _ = gpu_forward(p, d, driver=2)
-    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-
-
 def test_forward_bitwise_deterministic_10_runs():
     import torch
     p = CONFIGS[1]
