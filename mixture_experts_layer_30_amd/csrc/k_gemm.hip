@@ -242,10 +242,11 @@ __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m
 // One launch runs the forward's gate/up and down tiles (gateup_tile and
 // down_tile, unchanged) as items taken from per-XCD queues in the order of
 // persist_plan.h, which also states why every wait ends. Completion travels
-// through counters: a U item adds one to its row tile's counter, a D item to
-// its minibatch's; a D item waits for all U items of its row tile, a U item
-// of minibatch m >= N_s for all D items of minibatch m - N_s, the previous
-// user of its ring slot.
+// through counters per row tile: a U item adds one to udone[tile], a D item
+// to dcnt[tile], and the last D item of a tile marks it retired. A D item
+// waits for all U items of its row tile; a U item of minibatch m >= N_s
+// waits until every row tile of minibatch m - N_s whose ring rows overlap
+// its own is retired (the previous users of those slot rows).
 //
 // Bounded by construction: each workgroup's loop ends when its queue is
 // exhausted (tickets only grow), a wait gives up after ps.spin_limit ticks
@@ -254,44 +255,62 @@ __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m
 // ends every workgroup's loop at its next item. The outputs are then
 // incomplete; the status word says so.
 //
-// Visibility: a finishing item writes its results back to memory visible to
-// every CU (agent-scope release) before its counter moves; a waiting item
-// invalidates its caches (agent-scope acquire) after its counter is reached.
-// The U and D items of one row tile share a queue, so h stays within one
-// XCD's L2; only the slot-reuse waits cross XCDs, and they guard writes.
+// Visibility. Each XCD has its own L2; the L2s are not coherent with each
+// other. The U and D items of a row tile share a queue, and queue q is
+// served by the workgroups that run on XCD q, so h goes from its writer to
+// its readers through one L2: the writer waits until its stores are in the
+// L2 before its counter moves, and the reader invalidates its CU's L1 after
+// the wait. The hazard across XCDs is the reuse of ring rows: dirty h lines
+// of minibatch m left in one XCD's L2 must reach memory before another XCD
+// writes the same rows for minibatch m + N_s, so the last D item of a row
+// tile writes its XCD's L2 back (agent-scope release) before it marks the
+// tile retired, and the reuse waits on retired tiles. At the start every
+// workgroup checks the XCD it runs on (HW_REG_XCC_ID) against its queue and
+// the grid agrees on the result (one arrival counter); if any workgroup is
+// elsewhere, every signal releases and every wait acquires at agent scope.
 
-MOK_DEV bool persist_wait(const int* c, int target, int* stop, const mok_persist_args& ps, int* s_ok) {
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-          ok = 0;
-          break;
-        }
-        if (__builtin_amdgcn_s_memrealtime() - t0 > ps.spin_limit) {
-          __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    *s_ok = ok;
-  }
-  __syncthreads();
-  const bool ok = *s_ok != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return ok;
+MOK_DEV uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xf;
 }
 
-MOK_DEV void persist_signal(int* c) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's stores, written back
-  __builtin_amdgcn_s_waitcnt(0);                       // ... and the write-back finished
+// thread 0 spins until *c >= target (false: stopped or gave up)
+MOK_DEV bool persist_spin(const int* c, int target, int* stop, const mok_persist_args& ps) {
+  if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > ps.spin_limit) {
+      __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// the workgroup learns thread 0's verdict
+MOK_DEV bool wg_agree(bool ok, int* s_ok) {
+  if (threadIdx.x == 0) *s_ok = ok ? 1 : 0;
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *s_ok != 0;
+}
+
+// this thread's stores are in its XCD's L2 (all of them, with `agent`: in
+// memory) once the workgroup passes the barrier
+MOK_DEV void persist_release(bool agent) {
+  if (agent) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// after a wait: the CU's L1 holds no line older than the wait (`agent`: nor
+// the L2)
+MOK_DEV void persist_acquire(bool agent) {
+  if (agent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  else asm volatile("buffer_inv sc0" ::: "memory");
 }
 
 // The tiles run as calls: inlined into the item loop, the lane-dependent
@@ -327,7 +346,7 @@ __device__ __noinline__ void persist_down(fwd_args_cptr ap, lds_u8* lds, int ti,
 template <bool F8>
 __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_args a, mok_persist_args ps) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
-  __shared__ int s_ticket, s_ok;
+  __shared__ int s_ticket, s_ok, s_agent;
   const int q = (int)blockIdx.x % kPlanQueues;
   PersistPlan P;
   P.mbs = a.mb_tile_start;
@@ -337,9 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
   P.ntd = (int)((a.H + G256::BN - 1) / G256::BN);
   // the kernel's own arguments, for the tile calls: `a` is the first one
   const fwd_args_cptr ap = (fwd_args_cptr)__builtin_amdgcn_kernarg_segment_ptr();
-  int* stop = ps.ctr + kPlanQueues;
-  int* ddone = ps.ctr + kPlanQueues + 1;
-  int* udone = ddone + a.n_mb;
+  PersistCounters C = persist_counters(ps.ctr, ps.max_tiles);
 
   // the tile table (written by the schedule) must fit the bounds the counters
   // and the host's item count were sized for; every workgroup reads the same
@@ -352,18 +369,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
   if (!valid) {
     if (threadIdx.x == 0) {
       __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(C.stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
+
+  // placement: every workgroup on the XCD of its queue, or agent-scope sync
+  if (threadIdx.x == 0) {
+    if (xcc_id() != (uint32_t)q)
+      __hip_atomic_fetch_or(C.misplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(C.arrived, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int agent_sync = -1;   // -1: the grid did not gather (stop)
+    if (persist_spin(C.arrived, (int)gridDim.x, C.stop, ps)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      agent_sync = __hip_atomic_load(C.misplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    }
+    s_agent = agent_sync;
+  }
+  __syncthreads();
+  if (s_agent < 0) return;
+  const bool agent = s_agent != 0;
 
   PlanCursor cur;
   plan_cursor_init(cur);
   for (;;) {
     if (threadIdx.x == 0) {
       int t = -1;
-      if (__hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
-        t = __hip_atomic_fetch_add(ps.ctr + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_load(C.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        t = __hip_atomic_fetch_add(C.ticket + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_ticket = t;
     }
     __syncthreads();
@@ -372,16 +405,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
     PlanItem it;
     if (t < 0 || !plan_item(P, cur, q, t, it)) break;
     if (it.down) {
-      if (!persist_wait(udone + it.ti, P.ntu, stop, ps, &s_ok)) break;
+      bool w = true;
+      if (threadIdx.x == 0) w = persist_spin(C.udone + it.ti, P.ntu, C.stop, ps);
+      if (!wg_agree(w, &s_ok)) break;
+      persist_acquire(agent);
       persist_down<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
-      persist_signal(ddone + it.m);
-    } else {
-      if (it.m >= a.n_slots) {
-        const int mp = it.m - a.n_slots;
-        if (!persist_wait(ddone + mp, (int)P.down_items(mp), stop, ps, &s_ok)) break;
+      persist_release(agent);
+      if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(C.dcnt + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == P.ntd - 1) {
+          // the tile's last reader: its XCD's dirty h lines go to memory
+          // before another XCD may write these ring rows
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __builtin_amdgcn_s_waitcnt(0);               // the write-back finished
+          __hip_atomic_store(C.retired + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
+    } else {
+      bool w = true;
+      if (it.m >= a.n_slots && threadIdx.x == 0) {
+        const mok_tile cur_t = a.tiles[it.ti];
+        const int mp = it.m - a.n_slots;
+        const int64_t o0 = cur_t.p0 - (int64_t)it.m * a.M, o1 = cur_t.p1 - (int64_t)it.m * a.M;
+        int u = plan_first_overlap(P, a.tiles, a.M, mp, o0);
+        for (; w && plan_overlaps(P, a.tiles, a.M, mp, u, o1); ++u)
+          w = persist_spin(C.retired + u, 1, C.stop, ps);
+      }
+      if (!wg_agree(w, &s_ok)) break;
       persist_gateup<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
-      persist_signal(udone + it.ti);
+      persist_release(agent);
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(C.udone + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

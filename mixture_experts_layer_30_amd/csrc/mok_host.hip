@@ -143,7 +143,7 @@ FwdWs fwd_ws(const Resolved& r) {
   w.xq = o;      o = align_up(o + (r.mx ? (size_t)r.T * r.H : 0));
   w.xqs = o;     o = align_up(o + (r.mx ? (size_t)r.T * (r.H / 32) : 0));
   // completion counters of the persistent driver (driver 2)
-  w.ctr = o;     o = align_up(o + 4 * (size_t)mok_persist_counters(r.n_mb, r.max_fwd_tiles));
+  w.ctr = o;     o = align_up(o + 4 * (size_t)mok_persist_counters(r.max_fwd_tiles));
   w.total = o;
   return w;
 }
@@ -496,7 +496,7 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
     ps.max_mb_tiles = max_mb_tiles;
     ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
     const int grid = std::max(1, cus / 8) * 8;
-    MOK_RUN("persist_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.n_mb, r.max_fwd_tiles), st));
+    MOK_RUN("persist_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.max_fwd_tiles), st));
     MOK_RUN("persistent_fwd", mok_launch_fwd_persistent(a, ps, grid, r.mx, st));
     MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
                                static_cast<bf16_t*>(y), st));

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "mok_device.h"
+#include "persist_plan.h"
 
 struct mok_sched_ptrs {
   int32_t* status;
@@ -110,16 +111,15 @@ hipError_t mok_launch_down(const mok_fwd_args& a, int m0, int m1, int max_tiles,
 // Persistent forward: one launch runs every gate/up and down tile of the
 // layer, minibatch after minibatch through the ring (plan: persist_plan.h).
 struct mok_persist_args {
-  int* ctr;              // mok_persist_counters ints, zero at the launch: [0, 8) ticket
-                         // of each XCD queue, [8] stop flag, [9, 9 + n_mb) down tiles
-                         // done per minibatch, then gate/up tiles done per row tile
+  int* ctr;              // mok_persist_counters ints, zero at the launch (layout:
+                         // persist_counters in persist_plan.h)
   int32_t* status;       // schedule status word
   int32_t give_up_bit;   // set in *status when a wait gives up or the tile table is inconsistent
   int max_tiles;         // bound on mb_tile_start[n_mb]
   int max_mb_tiles;      // bound on the row tiles of one minibatch
   uint64_t spin_limit;   // ticks of the 64-bit real-time counter one wait may last
 };
-inline int64_t mok_persist_counters(int n_mb, int max_tiles) { return 9 + (int64_t)n_mb + max_tiles; }
+inline int64_t mok_persist_counters(int max_tiles) { return mok::persist_counter_count(max_tiles); }
 // grid: a multiple of 8, at most the workgroups resident at once (one per CU)
 hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, const mok_persist_args& ps, int grid,
                                      bool mxfp8, hipStream_t st);

@@ -11,24 +11,16 @@
 //                writing the tile's h rows into slot m mod N_s;
 //   D(m, ti, c)  down GEMM of row tile ti, output column tile c < ntd,
 //                reading those h rows.
-// D(m, ti, *) needs every U(m, ti, *); U(m, *, *) needs every D(m - N_s, *, *)
-// (the previous user of its slot) when m >= N_s.
-//
-// Queues. There is one queue per XCD (workgroup wg serves queue wg mod 8).
-// Each minibatch's row tiles are cut into groups of 4 consecutive tiles, and
-// the groups of all minibatches, in order, are dealt to the queues round-robin
-// (group g of minibatch m to queue (groups before m + g) mod 8), so the queues
-// get equal work over the layer whatever the tile count of one minibatch. Both
-// the U and the D items of a row tile are in the queue of its group: h never
-// crosses an XCD. Within a group the items run column by column, so the 32 or
-// so tiles in flight on an XCD share 4 row panels and 8 column panels in its
-// L2 (the row-tile order of the one-launch-per-stage kernels).
+// D(m, ti, *) needs every U(m, ti, *). A row tile is retired once all its D
+// items are done. U(m, ti, *) with m >= N_s needs the row tiles of minibatch
+// m - N_s (the previous users of slot m mod N_s) whose slot rows overlap
+// ti's to be retired: a few tiles, found by plan_first_overlap.
 //
 // Order. Queue q lists stage s = 0 .. n_mb as [U(s) items, D(s-1) items]
 // (its own groups only), or [D(s-1), U(s)] with a single ring slot. Every item
 // then depends only on items earlier in this stage order: D(s-1) on U(s-1),
-// one stage back; U(s) on D(s - N_s), which sits in stage s - N_s + 1 < s for
-// N_s >= 2, and in stage s before the U block for N_s = 1. Workgroups take
+// one stage back; U(s) on D(s - N_s) items, which sit in stage s - N_s + 1 < s
+// for N_s >= 2, and in stage s before the U block for N_s = 1. Workgroups take
 // tickets from their queue in increasing order, so the earliest unfinished
 // item in the stage order has finished dependencies, and it is either held by
 // a running workgroup or is the next ticket of its queue, whose workgroups are
@@ -146,6 +138,52 @@ MOK_HD bool plan_item(const PersistPlan& P, PlanCursor& c, int q, int64_t t, Pla
   it.col = jj / hg;
   it.ti = P.mbs[m] + kPlanGroup * g + jj % hg;
   return true;
+}
+
+// Completion counters in device memory (ints, zero at the launch).
+constexpr int kPlanHeader = 16;   // [0, 8) ticket per queue, 8 stop flag,
+                                  // 9 arrivals, 10 misplaced workgroups
+struct PersistCounters {
+  int* ticket;      // [kPlanQueues]
+  int* stop;
+  int* arrived;
+  int* misplaced;
+  int* udone;       // [max_tiles] U items done per row tile
+  int* dcnt;        // [max_tiles] D items done per row tile
+  int* retired;     // [max_tiles] 1 once the row tile's slot rows may be rewritten
+};
+MOK_HD int64_t persist_counter_count(int max_tiles) { return kPlanHeader + 3 * (int64_t)max_tiles; }
+MOK_HD PersistCounters persist_counters(int* c, int max_tiles) {
+  PersistCounters k;
+  k.ticket = c;
+  k.stop = c + kPlanQueues;
+  k.arrived = c + kPlanQueues + 1;
+  k.misplaced = c + kPlanQueues + 2;
+  k.udone = c + kPlanHeader;
+  k.dcnt = k.udone + max_tiles;
+  k.retired = k.dcnt + max_tiles;
+  return k;
+}
+
+// Slot-reuse dependencies. The row tiles of one minibatch are consecutive in
+// the table and ascending and contiguous in the permuted row p; minibatch mp
+// holds rows [mp*M, ...) at slot offsets p - mp*M. The tiles of minibatch mp
+// whose slot rows overlap slot offsets [o0, o1) are u = plan_first_overlap(..,
+// o0) onwards while plan_overlaps(.., u, o1).
+template <class Tile>
+MOK_HD int plan_first_overlap(const PersistPlan& P, const Tile* tiles, int64_t M, int mp, int64_t o0) {
+  int l = P.mbs[mp], r = P.mbs[mp + 1];
+  const int64_t lo = (int64_t)mp * M + o0;
+  while (l < r) {                      // first tile with p1 > lo
+    const int h = (l + r) >> 1;
+    if (tiles[h].p1 > lo) r = h;
+    else l = h + 1;
+  }
+  return l;
+}
+template <class Tile>
+MOK_HD bool plan_overlaps(const PersistPlan& P, const Tile* tiles, int64_t M, int mp, int u, int64_t o1) {
+  return u < P.mbs[mp + 1] && tiles[u].p0 < (int64_t)mp * M + o1;
 }
 
 }  // namespace mok

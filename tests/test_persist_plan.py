@@ -32,4 +32,4 @@ def sim(tmp_path_factory):
 def test_plan_runs_every_item_once_without_deadlock(sim):
     out = subprocess.run([sim, "400"], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.strip() == "ok 404"
+    assert out.stdout.strip() == "ok 405"
