@@ -260,7 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m
 // served by the workgroups that run on XCD q, so h goes from its writer to
 // its readers through one L2: the writer waits until its stores are in the
 // L2 before its counter moves, and the reader invalidates its CU's L1 after
-// the wait. The hazard across XCDs is the reuse of ring rows: dirty h lines
+// the wait. A D item's obuf rows are read only after the launch, so it
+// signals without waiting for its stores. The hazard across XCDs is the reuse of ring rows: dirty h lines
 // of minibatch m left in one XCD's L2 must reach memory before another XCD
 // writes the same rows for minibatch m + N_s, so the last D item of a row
 // tile writes its XCD's L2 back (agent-scope release) before it marks the
@@ -410,7 +411,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
       if (!wg_agree(w, &s_ok)) break;
       persist_acquire(agent);
       persist_down<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
-      persist_release(agent);
+      // no wait for the obuf stores (read after the launch only); the tile's
+      // h reads are complete (its main loop consumed every copy)
+      __syncthreads();
       if (threadIdx.x == 0) {
         const int done = __hip_atomic_fetch_add(C.dcnt + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == P.ntd - 1) {

@@ -16,8 +16,21 @@
 // m - N_s (the previous users of slot m mod N_s) whose slot rows overlap
 // ti's to be retired: a few tiles, found by plan_first_overlap.
 //
+// Queues. There is one queue per XCD (workgroup wg serves queue wg mod 8).
+// Minibatch m's nr row tiles are cut into 8 contiguous chunks, one per
+// queue, of nr / 8 tiles, the nr mod 8 extra tiles going one each to the
+// queues that follow the previous minibatch's extras (the chunks of queue
+// rank j = (q - mb_tile_start[m]) mod 8; mb_tile_start[m] is the count of
+// all tiles before m, so the extras are dealt round-robin over the whole
+// layer and any two queues' tile counts differ by at most one). Both the U
+// and the D items of a row tile are in the queue of its chunk: h never
+// crosses an XCD. A chunk runs in groups of 4 tiles, each group column by
+// column, so the 32 or so tiles in flight on an XCD share 4 row panels and 8
+// column panels in its L2 (the row-tile order of the one-launch-per-stage
+// kernels).
+//
 // Order. Queue q lists stage s = 0 .. n_mb as [U(s) items, D(s-1) items]
-// (its own groups only), or [D(s-1), U(s)] with a single ring slot. Every item
+// (its own chunks only), or [D(s-1), U(s)] with a single ring slot. Every item
 // then depends only on items earlier in this stage order: D(s-1) on U(s-1),
 // one stage back; U(s) on D(s - N_s) items, which sit in stage s - N_s + 1 < s
 // for N_s >= 2, and in stage s before the U block for N_s = 1. Workgroups take
@@ -57,22 +70,21 @@ struct PersistPlan {
   int n_mb, n_slots, ntu, ntd;
 
   MOK_HD int nr(int m) const { return (m < 0 || m >= n_mb) ? 0 : mbs[m + 1] - mbs[m]; }
-  MOK_HD static int ngroups(int nr) { return (nr + kPlanGroup - 1) / kPlanGroup; }
-  // first group of a minibatch (gb groups before it) that queue q takes
-  MOK_HD static int first_group(int gb, int q) {
-    return ((q - gb) % kPlanQueues + kPlanQueues) % kPlanQueues;
+  // queue q's chunk of minibatch m: tiles [mbs[m] + first, + count)
+  MOK_HD void chunk(int m, int q, int& first, int& count) const {
+    const int n = nr(m);
+    if (n == 0) { first = 0; count = 0; return; }
+    const int j = ((q - mbs[m]) % kPlanQueues + kPlanQueues) % kPlanQueues;
+    const int base = n / kPlanQueues, extra = n % kPlanQueues;
+    first = j * base + (j < extra ? j : extra);
+    count = base + (j < extra ? 1 : 0);
   }
-  // row tiles of a minibatch (nr tiles, gb groups before it) in queue q
-  MOK_HD static int rows_q(int nr, int gb, int q) {
-    const int ng = ngroups(nr), g0 = first_group(gb, q);
-    if (g0 >= ng) return 0;
-    const int cnt = (ng - 1 - g0) / kPlanQueues + 1;
-    const int last = g0 + kPlanQueues * (cnt - 1);
-    return kPlanGroup * cnt - (last == ng - 1 ? kPlanGroup * ng - nr : 0);
+  MOK_HD int chunk_size(int m, int q) const {
+    int f, c;
+    chunk(m, q, f, c);
+    return c;
   }
   MOK_HD bool down_first() const { return n_slots == 1; }
-  // completed D items of minibatch m that free its slot
-  MOK_HD int64_t down_items(int m) const { return (int64_t)ntd * nr(m); }
 };
 
 // A workgroup's position in its queue. Its tickets increase, so the stage
@@ -81,20 +93,15 @@ struct PersistPlan {
 struct PlanCursor {
   int s;          // stage
   int64_t base;   // items of the queue before stage s
-  int gbu;        // groups of the minibatches before s (U block: minibatch s)
-  int gbd;        // groups of the minibatches before s - 1 (D block: minibatch s - 1)
 };
 
 MOK_HD void plan_cursor_init(PlanCursor& c) {
   c.s = 0;
   c.base = 0;
-  c.gbu = 0;
-  c.gbd = 0;
 }
 
 MOK_HD int64_t plan_stage_items(const PersistPlan& P, const PlanCursor& c, int q) {
-  return (int64_t)P.ntd * PersistPlan::rows_q(P.nr(c.s - 1), c.gbd, q) +
-         (int64_t)P.ntu * PersistPlan::rows_q(P.nr(c.s), c.gbu, q);
+  return (int64_t)P.ntd * P.chunk_size(c.s - 1, q) + (int64_t)P.ntu * P.chunk_size(c.s, q);
 }
 
 // Item of ticket t of queue q (t not below any earlier ticket of this
@@ -106,13 +113,11 @@ MOK_HD bool plan_item(const PersistPlan& P, PlanCursor& c, int q, int64_t t, Pla
     const int64_t n = plan_stage_items(P, c, q);
     if (t < c.base + n) break;
     c.base += n;
-    c.gbd = c.gbu;
-    c.gbu += PersistPlan::ngroups(P.nr(c.s));
     ++c.s;
   }
   int64_t o = t - c.base;
-  const int64_t nd = (int64_t)P.ntd * PersistPlan::rows_q(P.nr(c.s - 1), c.gbd, q);
-  const int64_t nu = (int64_t)P.ntu * PersistPlan::rows_q(P.nr(c.s), c.gbu, q);
+  const int64_t nd = (int64_t)P.ntd * P.chunk_size(c.s - 1, q);
+  const int64_t nu = (int64_t)P.ntu * P.chunk_size(c.s, q);
   int down;
   if (P.down_first()) {
     down = o < nd;
@@ -123,20 +128,18 @@ MOK_HD bool plan_item(const PersistPlan& P, PlanCursor& c, int q, int64_t t, Pla
   }
   const int m = down ? c.s - 1 : c.s;
   const int nc = down ? P.ntd : P.ntu;
-  const int gb = down ? c.gbd : c.gbu;
-  const int nr = P.nr(m);
-  // the queue's groups of minibatch m in ascending order, kPlanGroup * nc
-  // items per group (only the minibatch's last group may be shorter, and it
-  // comes last)
-  const int j = (int)(o / ((int64_t)kPlanGroup * nc));
-  const int g = PersistPlan::first_group(gb, q) + kPlanQueues * j;
-  const int rem = nr - kPlanGroup * g;
+  int first, count;
+  P.chunk(m, q, first, count);
+  // groups of kPlanGroup tiles of the chunk in ascending order, kPlanGroup *
+  // nc items per group (only the last group may be shorter)
+  const int g = (int)(o / ((int64_t)kPlanGroup * nc));
+  const int rem = count - kPlanGroup * g;
   const int hg = rem < kPlanGroup ? rem : kPlanGroup;
-  const int jj = (int)(o - (int64_t)j * kPlanGroup * nc);
+  const int jj = (int)(o - (int64_t)g * kPlanGroup * nc);
   it.down = down;
   it.m = m;
   it.col = jj / hg;
-  it.ti = P.mbs[m] + kPlanGroup * g + jj % hg;
+  it.ti = P.mbs[m] + first + kPlanGroup * g + jj % hg;
   return true;
 }
 

@@ -16,8 +16,8 @@
 //    brute force here) is done, and plan_first_overlap / plan_overlaps name
 //    exactly those tiles;
 //  - the U and D items of one row tile run in the same queue;
-//  - groups of 4 row tiles stay in one queue, and the queues' group counts
-//    differ by at most one.
+//  - a queue's row tiles of one minibatch are contiguous, and the queues'
+//    tile counts over the layer differ by at most one.
 // Prints "ok <cases>" on success, a diagnosis and exit status 1 otherwise.
 #define MOK_HD inline
 #include "../mixture_experts_layer_30_amd/csrc/persist_plan.h"
@@ -184,19 +184,24 @@ bool run_case(const Case& k, uint64_t seed) {
     for (int c = 0; c < k.ntd; ++c)
       if (ran_d[(size_t)ti * k.ntd + c].load() != 1) { fail("D item not run exactly once", ti, c, ran_d[(size_t)ti * k.ntd + c].load()); return false; }
   }
-  // balance: the groups (4 consecutive row tiles of a minibatch) of the
-  // whole layer are dealt round-robin, so the queues' group counts differ by
-  // at most one
-  std::vector<int> groups(kPlanQueues, 0);
-  for (int m = 0; m < n_mb; ++m)
-    for (int ti = k.mbs[m]; ti < k.mbs[m + 1]; ti += kPlanGroup) {
+  // balance: each queue's tiles of a minibatch are one contiguous chunk, and
+  // the queues' tile counts over the layer differ by at most one
+  std::vector<int> tiles_q(kPlanQueues, 0);
+  for (int m = 0; m < n_mb; ++m) {
+    std::vector<int> seen(kPlanQueues, 0);
+    int prev = -1;
+    for (int ti = k.mbs[m]; ti < k.mbs[m + 1]; ++ti) {
       const int q = queue_u[ti].load();
-      for (int u = ti; u < std::min(ti + kPlanGroup, k.mbs[m + 1]); ++u)
-        if (queue_u[u].load() != q) { fail("group split over queues", m, ti, u); return false; }
-      groups[q] += 1;
+      if (q != prev) {
+        if (seen[q]) { fail("chunk of a queue not contiguous", m, ti, q); return false; }
+        seen[q] = 1;
+        prev = q;
+      }
+      tiles_q[q] += 1;
     }
-  const auto mm = std::minmax_element(groups.begin(), groups.end());
-  if (*mm.second - *mm.first > 1) { fail("queues unbalanced (groups)", *mm.first, *mm.second, 0); return false; }
+  }
+  const auto mm = std::minmax_element(tiles_q.begin(), tiles_q.end());
+  if (*mm.second - *mm.first > 1) { fail("queues unbalanced (tiles)", *mm.first, *mm.second, 0); return false; }
   return true;
 }
 
