@@ -64,14 +64,15 @@ typedef enum {
 typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
 
 /* Status word bits, written by mok_build_schedule (and the second by
- * mok_forward with driver 2); read the word after the stream has passed the
- * call. */
+ * mok_forward with driver 2 and by mok_forward_fused); read the word after
+ * the stream has passed the call. */
 #define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
 #define MOK_STATUS_WATCHDOG      0x2   /* driver 2 gave up: a wait between its
                                           tiles passed its time limit (2 s), or
                                           the schedule's tile table failed its
                                           checks; y and fwd_ctx are incomplete.
-                                          Set by mok_forward (driver 2).        */
+                                          Set by mok_forward (driver 2) and
+                                          mok_forward_fused.                    */
 
 /* Problem shape. Supported: T >= 0, 1 <= topk <= E <= 512, T*topk < 2^31,
  * H and I multiples of 128. dtype MOK_MXFP8 selects the MXFP8 forward and
@@ -227,6 +228,30 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config,
                        const void* schedule, const void* x, const float* topk_w,
                        const mok_weights* weights, void* y, void* fwd_ctx,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Single-launch forward ([MoK card] "What it is": the layer in one kernel;
+ * [MoK clip] Key points 4-5 and key chart: schedule generation on the GPU,
+ * then dispatch -> expert FFN -> combine, stages waking each other through
+ * device counters). One persistent grid (a workgroup per compute unit) builds
+ * the schedule from topk_ids (the steps of mok_build_schedule), runs the
+ * minibatch forward of driver 2 (the dispatch fused into the gate/up operand
+ * copies, the down rows pushed to their flat slots) and the weighted combine;
+ * a small fill kernel clears its counters first, on the same stream.
+ * Arguments: those of mok_build_schedule (topk_ids, schedule, schedule_bytes:
+ * the schedule written is the one mok_build_schedule writes, so mok_backward
+ * can use it) and of mok_forward (x, topk_w, weights, y, fwd_ctx, workspace);
+ * config->driver is ignored. Results: schedule, y and fwd_ctx bitwise those of
+ * mok_build_schedule followed by mok_forward. The grid waits for itself
+ * between steps, so it must have the device to itself: kernels of other
+ * streams that hold compute units can make a wait give up after 2 s, which
+ * sets MOK_STATUS_WATCHDOG in the schedule's status word and leaves y and
+ * fwd_ctx incomplete. Errors as mok_build_schedule and mok_forward, plus
+ * MOK_ERR_UNSUPPORTED where the item counts would overflow 32-bit tickets. */
+mok_status mok_forward_fused(const mok_problem* problem, const mok_config* config,
+                             const int32_t* topk_ids, void* schedule, size_t schedule_bytes,
+                             const void* x, const float* topk_w, const mok_weights* weights,
+                             void* y, void* fwd_ctx, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Backward. [MoK clip] How-to item 2: reverse-combine then reverse-dispatch
  * with the same schedule; [MoK card] "What it is": forward and backward in

@@ -65,7 +65,8 @@ _lib = None
 EXPORTS = ("mok_version", "mok_status_string", "mok_buffer_sizes", "mok_get_schedule_layout",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
            "mok_router_forward", "mok_router_backward", "mok_trace_enable", "mok_trace_collect",
-           "mok_mxfp8_quantize_transposed", "mok_probe_mfma", "mok_build_schedule_noalloc")
+           "mok_mxfp8_quantize_transposed", "mok_probe_mfma", "mok_build_schedule_noalloc",
+           "mok_forward_fused")
 
 
 class TraceStat(ctypes.Structure):
@@ -97,6 +98,9 @@ def lib():
         L.mok_build_schedule_noalloc.argtypes = [P(Problem), P(Config), vp, vp, sz, vp]
         L.mok_forward.restype = ctypes.c_int
         L.mok_forward.argtypes = [P(Problem), P(Config), vp, vp, vp, P(Weights), vp, vp, vp, sz, vp]
+        L.mok_forward_fused.restype = ctypes.c_int
+        L.mok_forward_fused.argtypes = [P(Problem), P(Config), vp, vp, sz, vp, vp, P(Weights), vp, vp,
+                                        vp, sz, vp]
         L.mok_backward.restype = ctypes.c_int
         L.mok_backward.argtypes = [P(Problem), P(Config), vp, vp, vp, vp, P(Weights), vp, vp,
                                    vp, vp, vp, vp, vp, sz, vp]
@@ -201,6 +205,18 @@ def forward(problem, schedule, x, topk_w, weights, y, workspace, fwd_ctx=None, c
                              _ptr(topk_w), ctypes.byref(w), _ptr(y), _ptr(fwd_ctx),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream)), "mok_forward")
+
+
+def forward_fused(problem, topk_ids, schedule, x, topk_w, weights, y, workspace, fwd_ctx=None,
+                  config=None, stream=None):
+    """mok_forward_fused: the schedule from topk_ids and the forward, in one
+    persistent launch (weights as for forward)."""
+    w = _weights(*weights)
+    _check(lib().mok_forward_fused(ctypes.byref(problem), _cfg(config), _ptr(topk_ids), _ptr(schedule),
+                                   schedule.numel() * schedule.element_size(), _ptr(x), _ptr(topk_w),
+                                   ctypes.byref(w), _ptr(y), _ptr(fwd_ctx), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "mok_forward_fused")
 
 
 def backward(problem, schedule, fwd_ctx, x, topk_w, weights, dy, dx, dw_gate, dw_up, dw_down,

@@ -13,6 +13,8 @@
 #include "gemm_core.h"
 #include "mok_launch.h"
 #include "persist_plan.h"
+#include "rows_core.h"
+#include "sched_core.h"
 
 using namespace mok;
 
@@ -344,53 +346,47 @@ __device__ __noinline__ void persist_down(fwd_args_cptr ap, lds_u8* lds, int ti,
   down_tile<F8>(persist_fwd_args(ap), (uint8_t*)lds, ti, col);
 }
 
-template <bool F8>
-__global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_args a, mok_persist_args ps) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
-  __shared__ int s_ticket, s_ok, s_agent;
-  const int q = (int)blockIdx.x % kPlanQueues;
+// The tile table (written by the schedule) must fit the bounds the counters
+// and the host's item count were sized for; every workgroup reads the same
+// table and reaches the same verdict. On failure the give-up bit and the
+// stop flag are set.
+MOK_DEV bool persist_table_valid(const mok_fwd_args& a, const PersistPlan& P, const mok_persist_args& ps,
+                                 const PersistCounters& C) {
+  bool valid = P.mbs[0] == 0 && P.mbs[a.n_mb] <= ps.max_tiles;
+  for (int m = 0; m < a.n_mb && valid; ++m) {
+    const int n = P.nr(m);
+    valid = n >= 0 && n <= ps.max_mb_tiles;
+  }
+  if (!valid && threadIdx.x == 0) {
+    __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(C.stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return valid;
+}
+
+MOK_DEV PersistPlan persist_plan(const mok_fwd_args& a) {
   PersistPlan P;
   P.mbs = a.mb_tile_start;
   P.n_mb = a.n_mb;
   P.n_slots = a.n_slots;
   P.ntu = (int)((a.I + G256::BN / 2 - 1) / (G256::BN / 2));
   P.ntd = (int)((a.H + G256::BN - 1) / G256::BN);
-  // the kernel's own arguments, for the tile calls: `a` is the first one
-  const fwd_args_cptr ap = (fwd_args_cptr)__builtin_amdgcn_kernarg_segment_ptr();
-  PersistCounters C = persist_counters(ps.ctr, ps.max_tiles);
+  return P;
+}
 
-  // the tile table (written by the schedule) must fit the bounds the counters
-  // and the host's item count were sized for; every workgroup reads the same
-  // table and reaches the same verdict
-  bool valid = P.mbs[0] == 0 && P.mbs[a.n_mb] <= ps.max_tiles;
-  for (int m = 0; m < a.n_mb && valid; ++m) {
-    const int n = P.nr(m);
-    valid = n >= 0 && n <= ps.max_mb_tiles;
-  }
-  if (!valid) {
-    if (threadIdx.x == 0) {
-      __hip_atomic_fetch_or(ps.status, ps.give_up_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(C.stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return;
-  }
+// Thread 0 of every workgroup: records whether it runs on the XCD of its
+// queue q (misplaced flag) and arrives at counter `arrived`.
+MOK_DEV void persist_arrive(const PersistCounters& C, int* arrived, int q) {
+  if (xcc_id() != (uint32_t)q) __hip_atomic_fetch_or(C.misplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(arrived, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-  // placement: every workgroup on the XCD of its queue, or agent-scope sync
-  if (threadIdx.x == 0) {
-    if (xcc_id() != (uint32_t)q)
-      __hip_atomic_fetch_or(C.misplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(C.arrived, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    int agent_sync = -1;   // -1: the grid did not gather (stop)
-    if (persist_spin(C.arrived, (int)gridDim.x, C.stop, ps)) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      agent_sync = __hip_atomic_load(C.misplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-    }
-    s_agent = agent_sync;
-  }
-  __syncthreads();
-  if (s_agent < 0) return;
-  const bool agent = s_agent != 0;
-
+// The item loop of the persistent forward (queue q; s_ticket, s_ok: LDS
+// words of the workgroup). False if a wait gave up or the launch stopped.
+template <bool F8>
+MOK_DEV bool persist_item_loop(const mok_fwd_args& a, fwd_args_cptr ap, const mok_persist_args& ps,
+                               const PersistCounters& C, const PersistPlan& P, int q, bool agent,
+                               uint8_t* lds_raw, int* s_ticket, int* s_ok) {
   PlanCursor cur;
   plan_cursor_init(cur);
   for (;;) {
@@ -398,21 +394,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
       int t = -1;
       if (__hip_atomic_load(C.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
         t = __hip_atomic_fetch_add(C.ticket + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ticket = t;
+      *s_ticket = t;
     }
     __syncthreads();
-    const int t = s_ticket;
+    const int t = *s_ticket;
     __syncthreads();                                   // s_ticket is free for the next item
+    if (t < 0) return false;
     PlanItem it;
-    if (t < 0 || !plan_item(P, cur, q, t, it)) break;
+    if (!plan_item(P, cur, q, t, it)) return true;
     if (it.down) {
       bool w = true;
       if (threadIdx.x == 0) w = persist_spin(C.udone + it.ti, P.ntu, C.stop, ps);
-      if (!wg_agree(w, &s_ok)) break;
+      if (!wg_agree(w, s_ok)) return false;
       persist_acquire(agent);
       persist_down<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
-      // no wait for the obuf stores (read after the launch only); the tile's
-      // h reads are complete (its main loop consumed every copy)
+      // no wait for the obuf stores (read after the item loop only); the
+      // tile's h reads are complete (its main loop consumed every copy)
       __syncthreads();
       if (threadIdx.x == 0) {
         const int done = __hip_atomic_fetch_add(C.dcnt + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -434,12 +431,140 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
         for (; w && plan_overlaps(P, a.tiles, a.M, mp, u, o1); ++u)
           w = persist_spin(C.retired + u, 1, C.stop, ps);
       }
-      if (!wg_agree(w, &s_ok)) break;
+      if (!wg_agree(w, s_ok)) return false;
       persist_gateup<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
       persist_release(agent);
       if (threadIdx.x == 0)
         __hip_atomic_fetch_add(C.udone + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+}
+
+template <bool F8>
+__global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_args a, mok_persist_args ps) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
+  __shared__ int s_ticket, s_ok, s_agent;
+  const int q = (int)blockIdx.x % kPlanQueues;
+  const PersistPlan P = persist_plan(a);
+  // the kernel's own arguments, for the tile calls: `a` is the first one
+  const fwd_args_cptr ap = (fwd_args_cptr)__builtin_amdgcn_kernarg_segment_ptr();
+  const PersistCounters C = persist_counters(ps.ctr, ps.max_tiles);
+  if (!persist_table_valid(a, P, ps, C)) return;
+
+  // placement: every workgroup on the XCD of its queue, or agent-scope sync
+  if (threadIdx.x == 0) {
+    persist_arrive(C, C.arrived, q);
+    int agent_sync = -1;   // -1: the grid did not gather (stop)
+    if (persist_spin(C.arrived, (int)gridDim.x, C.stop, ps)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      agent_sync = __hip_atomic_load(C.misplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    }
+    s_agent = agent_sync;
+  }
+  __syncthreads();
+  if (s_agent < 0) return;
+  persist_item_loop<F8>(a, ap, ps, C, P, q, s_agent != 0, lds_raw, &s_ticket, &s_ok);
+}
+
+// ================================================================== single-launch layer
+// [MoK card] "What it is": the whole forward in one kernel; [MoK clip] Key
+// points 4-5 and the key chart: schedule generation on the GPU, then the
+// dispatch -> expert FFN -> combine pipeline, stages waking each other through
+// counters. One resident grid (a workgroup per CU) runs, separated by grid-
+// wide counter waits:
+//   1. (MXFP8) x quantized along H, and the schedule's chunk histograms;
+//   2. workgroup 0: the schedule scan (totals, offsets, chunk bases, tiles);
+//   3. the schedule scatter (perm, dest, tok);
+//   4. the gate/up and down items of the persistent forward (the gather is
+//      the gate/up tiles' operand copies through tok);
+//   5. the weighted combine of the obuf rows into y.
+// Each step's results are published at agent scope (every workgroup writes
+// its XCD's L2 back before it arrives, every waiter invalidates after the
+// wait). The schedule written here is the one mok_build_schedule writes (the
+// same steps, sched_core.h), so the backward can use it; y and fwd_ctx are
+// bitwise those of mok_build_schedule + mok_forward.
+template <bool F8>
+__global__ __launch_bounds__(kThreads, 1) void layer_fwd_kernel(mok_fwd_args a, mok_persist_args ps, mok_layer_args L) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G256, F8>>()];
+  __shared__ int s_ticket, s_ok, s_agent;
+  static_assert(sizeof(mok_sched::ChunkLds) <= sizeof(lds_raw), "chunk LDS");
+  static_assert(sizeof(mok_sched::ScanLds<kThreads>) <= sizeof(lds_raw), "scan LDS");
+  const int q = (int)blockIdx.x % kPlanQueues;
+  const int G = (int)gridDim.x, g = (int)blockIdx.x;
+  const fwd_args_cptr ap = (fwd_args_cptr)__builtin_amdgcn_kernarg_segment_ptr();
+  const PersistCounters C = persist_counters(ps.ctr, ps.max_tiles);
+  int* const step = C.misplaced + 1;                 // [0] hist done, [1] scan done, [2] scatter done, [3] GEMMs done
+
+  // 1. MXFP8 x, chunk histograms
+  if constexpr (F8) {
+    const int64_t nblk = a.T * (a.H / 32);
+    for (int64_t i = (int64_t)g * kThreads + threadIdx.x; i < nblk; i += (int64_t)G * kThreads)
+      mx_quantize_block(L.x, a.H, i, const_cast<uint8_t*>(a.x), const_cast<uint8_t*>(a.xs));
+  }
+  for (int c = g; c < L.nchunks; c += G) {
+    mok_sched::sched_hist_chunk(L.ids, L.R, a.E, L.chunk, c, L.bh, *reinterpret_cast<mok_sched::ChunkLds*>(lds_raw));
+    __syncthreads();
+  }
+  persist_release(true);
+  if (threadIdx.x == 0) persist_arrive(C, step + 0, q);
+
+  // 2. the scan
+  if (g == 0) {
+    bool ok = true;
+    if (threadIdx.x == 0) ok = persist_spin(step + 0, G, C.stop, ps);
+    if (!wg_agree(ok, &s_ok)) return;
+    persist_acquire(true);
+    mok_sched::sched_scan<kThreads>(L.s, L.R, a.E, L.nchunks, L.bh, a.M, L.bm_f, L.bm_b, a.n_mb, L.max_f,
+                                    L.max_b, *reinterpret_cast<mok_sched::ScanLds<kThreads>*>(lds_raw));
+    persist_release(true);
+    if (threadIdx.x == 0) __hip_atomic_store(step + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 3. the scatter
+  {
+    bool ok = true;
+    if (threadIdx.x == 0) ok = persist_spin(step + 1, 1, C.stop, ps);
+    if (!wg_agree(ok, &s_ok)) return;
+    persist_acquire(true);
+  }
+  for (int c = g; c < L.nchunks; c += G) {
+    mok_sched::sched_scatter_chunk(L.ids, L.s, L.R, a.E, a.topk, L.chunk, c, L.bh,
+                                   *reinterpret_cast<mok_sched::ChunkLds*>(lds_raw));
+    __syncthreads();
+  }
+  persist_release(true);
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(step + 2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    int agent_sync = -1;
+    if (persist_spin(step + 2, G, C.stop, ps)) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      agent_sync = __hip_atomic_load(C.misplaced, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    }
+    s_agent = agent_sync;
+  }
+  __syncthreads();
+  if (s_agent < 0) return;
+  persist_acquire(true);
+
+  // 4. the expert FFN
+  const PersistPlan P = persist_plan(a);
+  if (!persist_table_valid(a, P, ps, C)) return;
+  if (!persist_item_loop<F8>(a, ap, ps, C, P, q, s_agent != 0, lds_raw, &s_ticket, &s_ok)) return;
+  persist_release(true);                               // this XCD's obuf rows, in memory
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(step + 3, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 5. the combine
+  {
+    bool ok = true;
+    if (threadIdx.x == 0) ok = persist_spin(step + 3, G, C.stop, ps);
+    if (!wg_agree(ok, &s_ok)) return;
+    persist_acquire(true);
+  }
+  const int nvalid = L.s.offsets[a.E];
+  const int64_t nch = a.H >> 3;
+  for (int64_t i = (int64_t)g * kThreads + threadIdx.x; i < a.T * nch; i += (int64_t)G * kThreads) {
+    const int64_t t = i / nch;
+    combine_elem(a.obuf, L.topk_w, L.s.dest, nvalid, t, i - t * nch, a.topk, a.H, L.y);
   }
 }
 
@@ -927,6 +1052,14 @@ hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, const mok_persist_ar
   if (grid <= 0 || grid % kPlanQueues != 0) return hipErrorInvalidValue;
   if (mxfp8) hipLaunchKernelGGL(fwd_persistent_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, ps);
   else hipLaunchKernelGGL(fwd_persistent_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a, ps);
+  return hipGetLastError();
+}
+
+hipError_t mok_launch_layer_fwd(const mok_fwd_args& a, const mok_persist_args& ps, const mok_layer_args& L,
+                                int grid, bool mxfp8, hipStream_t st) {
+  if (grid <= 0 || grid % kPlanQueues != 0) return hipErrorInvalidValue;
+  if (mxfp8) hipLaunchKernelGGL(layer_fwd_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, ps, L);
+  else hipLaunchKernelGGL(layer_fwd_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a, ps, L);
   return hipGetLastError();
 }
 

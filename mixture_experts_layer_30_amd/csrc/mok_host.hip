@@ -431,31 +431,13 @@ mok_status mok_build_schedule(const mok_problem* problem, const mok_config* conf
   return MOK_OK;
 }
 
-mok_status mok_forward(const mok_problem* problem, const mok_config* config, const void* schedule,
-                       const void* x, const float* topk_w, const mok_weights* weights, void* y,
-                       void* fwd_ctx, void* workspace, size_t workspace_bytes, void* stream) {
-  TraceCall tc;
-  Resolved r;
-  mok_status s = resolve(problem, config, &r);
-  if (s != MOK_OK) return s;
-  if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
-  if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
-  if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
-  const FwdWs W = fwd_ws(r);
-  if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
-  int cus = 0, wclk_khz = 0;
-  if ((s = check_device(&cus, &wclk_khz)) != MOK_OK) return s;
-  // persistent driver: tickets (int32) per queue stay below 2^31
-  const int64_t ntu = cdiv(r.I, 128), ntd = cdiv(r.H, 256);
-  const int max_mb_tiles = (int)std::min<int64_t>(cdiv(r.M, kTileRowsFwd) + r.E + 1, r.max_fwd_tiles);
-  if (r.driver == 2 && ((int64_t)r.max_fwd_tiles * (ntu + ntd) + cus >= ((int64_t)1 << 31) ||
-                        (int64_t)max_mb_tiles * ntd >= ((int64_t)1 << 31)))
-    return MOK_ERR_UNSUPPORTED;
-  if (r.T == 0) return MOK_OK;
-  hipStream_t st = (hipStream_t)stream;
-  const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
+namespace {
 
+// The forward's kernel arguments (the schedule at sp, buffers carved from the
+// workspace and fwd_ctx); x is the bf16 input (for MXFP8 the caller points
+// a.x / a.xs at the quantized copy).
+mok_fwd_args fwd_args(const Resolved& r, const mok_sched_ptrs& sp, uint8_t* ws, const FwdWs& W, void* fwd_ctx,
+                      const mok_weights* weights, const void* x) {
   mok_fwd_args a;
   memset(&a, 0, sizeof a);
   a.T = r.T; a.H = r.H; a.I = r.I; a.E = r.E; a.topk = r.k;
@@ -470,13 +452,59 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   const CtxLayout C = ctx_layout(r);
   a.obuf = reinterpret_cast<bf16_t*>(ctx ? ctx + C.obuf : ws + W.obuf);
   a.ab = ctx ? reinterpret_cast<bf16_t*>(ctx + C.ab) : nullptr;
+  a.x = static_cast<const uint8_t*>(x);
+  a.xs = nullptr;
+  return a;
+}
+
+// Persistent-driver checks: tickets (int32) per queue stay below 2^31.
+bool persist_fits(const Resolved& r, int cus, int* max_mb_tiles) {
+  const int64_t ntu = cdiv(r.I, 128), ntd = cdiv(r.H, 256);
+  *max_mb_tiles = (int)std::min<int64_t>(cdiv(r.M, kTileRowsFwd) + r.E + 1, r.max_fwd_tiles);
+  return (int64_t)r.max_fwd_tiles * (ntu + ntd) + cus < ((int64_t)1 << 31) &&
+         (int64_t)*max_mb_tiles * ntd < ((int64_t)1 << 31);
+}
+
+mok_persist_args persist_args(const Resolved& r, const mok_sched_ptrs& sp, uint8_t* ws, const FwdWs& W,
+                              int max_mb_tiles, int wclk_khz) {
+  mok_persist_args ps;
+  ps.ctr = reinterpret_cast<int*>(ws + W.ctr);
+  ps.status = sp.status;
+  ps.give_up_bit = MOK_STATUS_WATCHDOG;
+  ps.max_tiles = r.max_fwd_tiles;
+  ps.max_mb_tiles = max_mb_tiles;
+  ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
+  return ps;
+}
+
+}  // namespace
+
+mok_status mok_forward(const mok_problem* problem, const mok_config* config, const void* schedule,
+                       const void* x, const float* topk_w, const mok_weights* weights, void* y,
+                       void* fwd_ctx, void* workspace, size_t workspace_bytes, void* stream) {
+  TraceCall tc;
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
+  if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
+  if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
+  const FwdWs W = fwd_ws(r);
+  if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
+  int cus = 0, wclk_khz = 0;
+  if ((s = check_device(&cus, &wclk_khz)) != MOK_OK) return s;
+  int max_mb_tiles = 0;
+  if (r.driver == 2 && !persist_fits(r, cus, &max_mb_tiles)) return MOK_ERR_UNSUPPORTED;
+  if (r.T == 0) return MOK_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const mok_sched_ptrs sp = sched_ptrs(r, const_cast<void*>(schedule));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  mok_fwd_args a = fwd_args(r, sp, ws, W, fwd_ctx, weights, x);
 
   // Dispatch: the gate/up GEMM reads each routed row's x row in place through
   // the token table. MXFP8: x is quantized once per token (blocks lie inside a
   // row, so this is bitwise the same as quantizing each gathered row) and the
   // GEMM reads the fp8 rows and their scale rows the same way.
-  a.x = static_cast<const uint8_t*>(x);
-  a.xs = nullptr;
   if (r.mx) {
     MOK_RUN("mxfp8_quantize_x", mok_launch_mxfp8_quantize(static_cast<const bf16_t*>(x), r.T, r.H,
                                                           ws + W.xq, ws + W.xqs, st));
@@ -488,13 +516,7 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
     // minibatches in order through the ring, the stages waking each other
     // through counters (fwd_persistent_kernel; the plan in persist_plan.h).
     // The counters are cleared by a fill kernel on the same stream.
-    mok_persist_args ps;
-    ps.ctr = reinterpret_cast<int*>(ws + W.ctr);
-    ps.status = sp.status;
-    ps.give_up_bit = MOK_STATUS_WATCHDOG;
-    ps.max_tiles = r.max_fwd_tiles;
-    ps.max_mb_tiles = max_mb_tiles;
-    ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
+    const mok_persist_args ps = persist_args(r, sp, ws, W, max_mb_tiles, wclk_khz);
     const int grid = std::max(1, cus / 8) * 8;
     MOK_RUN("persist_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.max_fwd_tiles), st));
     MOK_RUN("persistent_fwd", mok_launch_fwd_persistent(a, ps, grid, r.mx, st));
@@ -517,6 +539,63 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   }
   MOK_RUN("combine", mok_launch_combine(a.obuf, topk_w, sp.dest, sp.offsets + r.E, r.T, r.k, r.H,
                              static_cast<bf16_t*>(y), st));
+  return MOK_OK;
+}
+
+mok_status mok_forward_fused(const mok_problem* problem, const mok_config* config, const int32_t* topk_ids,
+                             void* schedule, size_t schedule_bytes, const void* x, const float* topk_w,
+                             const mok_weights* weights, void* y, void* fwd_ctx, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  TraceCall tc;
+  Resolved r;
+  mok_status s = resolve(problem, config, &r);
+  if (s != MOK_OK) return s;
+  if (!schedule || !weights || !y || (r.R > 0 && !topk_ids) || (r.T > 0 && (!x || !topk_w)))
+    return MOK_ERR_INVALID_ARG;
+  if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
+  if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
+  const SchedLayout SL = sched_layout(r);
+  if (schedule_bytes < SL.total) return MOK_ERR_BUFFER_TOO_SMALL;
+  const FwdWs W = fwd_ws(r);
+  if (!workspace || workspace_bytes < ws_bytes(r)) return MOK_ERR_BUFFER_TOO_SMALL;
+  int cus = 0, wclk_khz = 0;
+  if ((s = check_device(&cus, &wclk_khz)) != MOK_OK) return s;
+  int max_mb_tiles = 0;
+  if (!persist_fits(r, cus, &max_mb_tiles)) return MOK_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  const mok_sched_ptrs sp = sched_ptrs(r, schedule);
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(schedule) + SL.chunk_counts);
+  if (r.T == 0) {
+    // nothing to run but the (empty) schedule
+    MOK_RUN("schedule", mok_launch_schedule(topk_ids, sp, 0, r.E, r.k, r.M, kTileRowsFwd, kTileRowsBwd,
+                                            r.n_mb, r.max_fwd_tiles, r.max_bwd_tiles, chunk_counts, st));
+    return MOK_OK;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  mok_fwd_args a = fwd_args(r, sp, ws, W, fwd_ctx, weights, x);
+  if (r.mx) {
+    a.x = ws + W.xq;
+    a.xs = ws + W.xqs;
+  }
+  const mok_persist_args ps = persist_args(r, sp, ws, W, max_mb_tiles, wclk_khz);
+  mok_layer_args L;
+  L.ids = topk_ids;
+  L.s = sp;
+  L.R = (int)r.R;
+  L.chunk = mok_schedule_chunk_rows(r.R);
+  L.nchunks = (int)cdiv(r.R, L.chunk);
+  L.bh = chunk_counts;
+  L.bm_f = kTileRowsFwd; L.bm_b = kTileRowsBwd;
+  L.max_f = r.max_fwd_tiles; L.max_b = r.max_bwd_tiles;
+  L.x = static_cast<const bf16_t*>(x);
+  L.topk_w = topk_w;
+  L.y = static_cast<bf16_t*>(y);
+  const int grid = std::max(1, cus / 8) * 8;
+  // [MoK card] "What it is", [MoK clip] Key points 4-5: schedule, dispatch,
+  // expert FFN and combine in one persistent launch (layer_fwd_kernel); its
+  // counters are cleared by a fill kernel on the same stream first.
+  MOK_RUN("layer_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.max_fwd_tiles), st));
+  MOK_RUN("layer_fwd", mok_launch_layer_fwd(a, ps, L, grid, r.mx, st));
   return MOK_OK;
 }
 

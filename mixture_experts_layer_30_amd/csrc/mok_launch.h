@@ -124,6 +124,21 @@ inline int64_t mok_persist_counters(int max_tiles) { return mok::persist_counter
 hipError_t mok_launch_fwd_persistent(const mok_fwd_args& a, const mok_persist_args& ps, int grid,
                                      bool mxfp8, hipStream_t st);
 
+// Single-launch layer: the schedule steps and the combine around the
+// persistent forward, in one grid (layer_fwd_kernel).
+struct mok_layer_args {
+  const int32_t* ids;    // topk_ids [R]
+  mok_sched_ptrs s;      // the schedule being built
+  int R, chunk, nchunks; // routed rows; schedule chunk rows and count
+  int32_t* bh;           // chunk count table [nchunks][E + 1]
+  int bm_f, bm_b, max_f, max_b;
+  const bf16_t* x;       // bf16 x [T][H] (quantized into mok_fwd_args.x / xs for MXFP8)
+  const float* topk_w;
+  bf16_t* y;
+};
+hipError_t mok_launch_layer_fwd(const mok_fwd_args& a, const mok_persist_args& ps, const mok_layer_args& L,
+                                int grid, bool mxfp8, hipStream_t st);
+
 struct mok_bwd_args {
   int64_t T, H, I;
   int E, topk;

@@ -9,7 +9,7 @@ import dataclasses
 
 import torch
 
-from . import (MOK_BF16, backward, buffer_sizes, build_schedule, forward, make_config,
+from . import (MOK_BF16, backward, buffer_sizes, build_schedule, forward, forward_fused, make_config,
                make_problem, mxfp8_quantize, mxfp8_quantize_transposed, schedule_layout)
 
 
@@ -39,6 +39,14 @@ def run_forward(w: Workspace, x, topk_w, weights, y=None):
     if y is None:
         y = torch.empty_like(x)
     forward(w.problem, w.schedule, x, topk_w, weights, y, w.workspace, w.fwd_ctx, w.config)
+    return y
+
+
+def run_forward_fused(w: Workspace, topk_ids, x, topk_w, weights, y=None):
+    """Schedule + forward in one persistent launch (mok_forward_fused)."""
+    if y is None:
+        y = torch.empty_like(x)
+    forward_fused(w.problem, topk_ids, w.schedule, x, topk_w, weights, y, w.workspace, w.fwd_ctx, w.config)
     return y
 
 
