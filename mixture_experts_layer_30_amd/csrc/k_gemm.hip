@@ -497,9 +497,10 @@ __global__ __launch_bounds__(kThreads, 1) void layer_fwd_kernel(mok_fwd_args a, 
 
   // 1. MXFP8 x, chunk histograms
   if constexpr (F8) {
-    const int64_t nblk = a.T * (a.H / 32);
-    for (int64_t i = (int64_t)g * kThreads + threadIdx.x; i < nblk; i += (int64_t)G * kThreads)
-      mx_quantize_block(L.x, a.H, i, const_cast<uint8_t*>(a.x), const_cast<uint8_t*>(a.xs));
+    constexpr int NB = 4;
+    const int64_t nblk = a.T * (a.H / 32), S = (int64_t)G * kThreads;
+    for (int64_t i = (int64_t)g * kThreads + threadIdx.x; i < nblk; i += NB * S)
+      mx_quantize_batch<NB>(L.x, a.H, i, S, nblk, const_cast<uint8_t*>(a.x), const_cast<uint8_t*>(a.xs));
   }
   for (int c = g; c < L.nchunks; c += G) {
     mok_sched::sched_hist_chunk(L.ids, L.R, a.E, L.chunk, c, L.bh, *reinterpret_cast<mok_sched::ChunkLds*>(lds_raw));
@@ -560,12 +561,11 @@ __global__ __launch_bounds__(kThreads, 1) void layer_fwd_kernel(mok_fwd_args a, 
     if (!wg_agree(ok, &s_ok)) return;
     persist_acquire(true);
   }
+  // one token per wavefront at a time
   const int nvalid = L.s.offsets[a.E];
-  const int64_t nch = a.H >> 3;
-  for (int64_t i = (int64_t)g * kThreads + threadIdx.x; i < a.T * nch; i += (int64_t)G * kThreads) {
-    const int64_t t = i / nch;
-    combine_elem(a.obuf, L.topk_w, L.s.dest, nvalid, t, i - t * nch, a.topk, a.H, L.y);
-  }
+  const int nw = kThreads / 64;
+  for (int64_t t = (int64_t)g * nw + wave_id(); t < a.T; t += (int64_t)G * nw)
+    combine_token_wave<4>(a.obuf, L.topk_w, L.s.dest, nvalid, t, a.topk, a.H, L.y);
 }
 
 // ================================================================== backward

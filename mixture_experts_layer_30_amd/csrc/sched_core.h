@@ -173,19 +173,23 @@ MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int3
   const int tid = threadIdx.x, nb = E + 1;
   if (tid == 0) L.s_flag = 0;
   constexpr int kBatch = 16;                     // chunk counts loaded per round trip
+  // the loads of a round cover all BPT buckets of the thread
   int run[BPT];
 #pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    const int v = tid * BPT + b;
-    run[b] = 0;
-    if (v < nb) {
-      for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-        int n[kBatch];
+  for (int b = 0; b < BPT; ++b) run[b] = 0;
+  if (tid * BPT < nb) {
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int n[BPT][kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) n[u] = c0 + u < nchunks ? bh[(int64_t)(c0 + u) * nb + v] : 0;
+      for (int b = 0; b < BPT; ++b) {
+        const int v = tid * BPT + b;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) run[b] += n[u];
+        for (int u = 0; u < kBatch; ++u) n[b][u] = (v < nb && c0 + u < nchunks) ? bh[(int64_t)(c0 + u) * nb + v] : 0;
       }
+#pragma unroll
+      for (int b = 0; b < BPT; ++b)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) run[b] += n[b][u];
     }
   }
   __syncthreads();
@@ -193,28 +197,42 @@ MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int3
 #pragma unroll
   for (int b = 0; b < BPT; ++b) own += run[b];
   int nvalid_total = 0;
-  int excl = block_exclusive_scan<NT>(own, L.sums, &nvalid_total);
+  const int excl0 = block_exclusive_scan<NT>(own, L.sums, &nvalid_total);
+  int base[BPT];
+  {
+    int excl = excl0;
 #pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    const int v = tid * BPT + b;
-    if (v < nb) {
-      L.s_off[v] = excl;
-      if (v < E) s.counts[v] = run[b];
-      s.offsets[v] = excl;                       // offsets[E] = valid rows
-      if (v == E && run[b] > 0) L.s_flag = 1;
-      int base = excl;
-      for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
-        int n[kBatch];
+    for (int b = 0; b < BPT; ++b) {
+      const int v = tid * BPT + b;
+      base[b] = excl;
+      if (v < nb) {
+        L.s_off[v] = excl;
+        if (v < E) s.counts[v] = run[b];
+        s.offsets[v] = excl;                     // offsets[E] = valid rows
+        if (v == E && run[b] > 0) L.s_flag = 1;
+      }
+      excl += run[b];
+    }
+  }
+  if (tid * BPT < nb) {
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      int n[BPT][kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) n[u] = c0 + u < nchunks ? bh[(int64_t)(c0 + u) * nb + v] : 0;
+      for (int b = 0; b < BPT; ++b) {
+        const int v = tid * BPT + b;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) n[b][u] = (v < nb && c0 + u < nchunks) ? bh[(int64_t)(c0 + u) * nb + v] : 0;
+      }
+#pragma unroll
+      for (int b = 0; b < BPT; ++b) {
+        const int v = tid * BPT + b;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          if (c0 + u < nchunks) bh[(int64_t)(c0 + u) * nb + v] = base;
-          base += n[u];
+          if (v < nb && c0 + u < nchunks) bh[(int64_t)(c0 + u) * nb + v] = base[b];
+          base[b] += n[b][u];
         }
       }
     }
-    excl += run[b];
   }
   __syncthreads();
 
