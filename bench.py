@@ -628,6 +628,38 @@ def forward_leg(d, dtype, steps, warmup, stream, cfg):
     return rec
 
 
+def forward_drivers(d, steps, warmup, stream):
+    """Schedule + forward (bf16, no context) of workload d under the three
+    drivers: one launch per stage per ring group (driver 1), the persistent
+    minibatch kernel (driver 2, two calls), and the single launch
+    (mok_forward_fused). Results are bitwise the same (GPU tests)."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    p = d.p
+    y = torch.empty_like(d.x)
+    rec = {"workload": p.name}
+    for name, drv in (("launch_per_stage", 1), ("persistent", 2), ("single_launch", None)):
+        ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=False, driver=drv or 0)
+
+        def fwd():
+            if drv is None:
+                mok.forward_fused(ws.problem, d.ids, ws.schedule, d.x, d.w, d.weights, y, ws.workspace, None,
+                                  ws.config, stream)
+            else:
+                mok.build_schedule(ws.problem, d.ids, ws.schedule, ws.config, stream)
+                mok.forward(ws.problem, ws.schedule, d.x, d.w, d.weights, y, ws.workspace, None, ws.config,
+                            stream)
+
+        for _ in range(warmup):
+            fwd()
+        mean, med, mn = time_steps(fwd, steps, stream)
+        rec[name] = {"ms": round(mean, 4), "ms_median": round(med, 4), "ms_min": round(mn, 4),
+                     "tflops": round(p.fwd_flops() / (mean * 1e-3) / 1e12, 2)}
+        del ws
+    return rec
+
+
 def main():
     args = parse()
     if args.traffic_record:
@@ -789,6 +821,8 @@ def main():
         log("[bench] forward-only timing")
         out["forward"] = forward_leg(d, mok.MOK_BF16, K, W, stream, cfg)
         del ws
+        log("[bench] forward drivers (schedule + forward)")
+        out["forward_drivers"] = forward_drivers(d, K, W, stream)
         # MXFP8 step on the same workload: the weights (and their transposed
         # copies for the backward) are quantized once before the timed region,
         # as the pages' pre-quantized weights; that quantization is timed too.
