@@ -158,6 +158,9 @@ typedef struct {
   size_t arrays;                 /* bytes of the schedule arrays alone, without the
                                     build's scratch tail: the size
                                     mok_build_schedule_noalloc needs              */
+  size_t expert_order;           /* int32 [E]   experts by descending count, ties
+                                    to the lower id (the order in which the
+                                    weight-gradient GEMMs take the experts)       */
 } mok_schedule_layout;
 
 /* [host] Library version, major*10000 + minor*100 + patch. */

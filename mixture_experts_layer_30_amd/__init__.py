@@ -57,7 +57,7 @@ class ScheduleLayout(ctypes.Structure):
         "mb_tile_start", "n_bwd_tiles", "bwd_tiles", "total")] + [
         (n, ctypes.c_int32) for n in (
             "minibatch_rows", "ring_slots", "n_minibatches", "max_fwd_tiles", "max_bwd_tiles",
-            "fwd_tile_rows", "bwd_tile_rows")] + [("arrays", ctypes.c_size_t)]
+            "fwd_tile_rows", "bwd_tile_rows")] + [("arrays", ctypes.c_size_t), ("expert_order", ctypes.c_size_t)]
 
 
 _lib = None

@@ -897,13 +897,15 @@ MOK_DEV bool xcd_swizzle(int nr, int nc, int& row, int& col) {
 // whose K loop runs over the expert's routed rows, so a tile's cost follows
 // its expert's load. Every expert's grid is cut into kXcds near-square blocks
 // (ry rows of blocks x kXcds/ry columns; ry chosen on the host) and XCD k
-// runs block k of every expert, expert by expert, in groups of 4 tile rows
-// taken column by column. Each XCD thereby does 1/8 of every expert's work
+// runs block k of every expert, expert by expert in the order eorder (the
+// schedule's experts by descending count: the longest tiles first, so the
+// launch ends on short ones), in groups of 4 tile rows taken column by
+// column. Each XCD thereby does 1/8 of every expert's work
 // whatever the loads (a contiguous tile range per XCD gave the XCD holding
 // the busiest expert 1.7x the mean work on a Zipf(0.8) routing), and the
 // tiles in flight on an XCD share their operand panels as in xcd_swizzle.
 // Grid: kXcds * E * ceil(ntm / ry) * ceil(ntn / (kXcds / ry)). False past the end.
-MOK_DEV bool dw_tile_of(int E, int ntm, int ntn, int ry, int& e, int& mt, int& nt) {
+MOK_DEV bool dw_tile_of(int E, const int32_t* eorder, int ntm, int ntn, int ry, int& e, int& mt, int& nt) {
   const int cx = kXcds / ry;
   const int wg = (int)blockIdx.x, k = wg % kXcds, i = wg / kXcds;
   const int by = k / cx, bx = k % cx;
@@ -911,9 +913,10 @@ MOK_DEV bool dw_tile_of(int E, int ntm, int ntn, int ry, int& e, int& mt, int& n
   const int c0 = bx * ntn / cx, c1 = (bx + 1) * ntn / cx;
   const int h = r1 - r0, w = c1 - c0, nb = h * w;
   if (nb <= 0) return false;
-  e = i / nb;
-  if (e >= E) return false;
-  const int j = i - e * nb;
+  const int pos = i / nb;
+  if (pos >= E) return false;
+  e = eorder[pos];
+  const int j = i - pos * nb;
   const int gi = j / (4 * w), hg = min(4, h - 4 * gi), jj = j - gi * 4 * w;
   nt = c0 + jj / hg;
   mt = r0 + 4 * gi + jj % hg;

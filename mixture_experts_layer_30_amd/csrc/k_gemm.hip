@@ -708,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd_kernel(mok_bwd_args a, in
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
   int e, mt_, nt_;
-  if (!dw_tile_of(a.E, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  if (!dw_tile_of(a.E, a.eorder, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
   const int tl = mt_ * (int)((a.I + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((I + G::BN - 1) / G::BN);
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu_kernel(mok_bwd_args a, i
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, false>>()];
   int e, mt_, nt_;
-  if (!dw_tile_of(a.E, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  if (!dw_tile_of(a.E, a.eorder, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
   const int tl = mt_ * (int)((a.H + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((H + G::BN - 1) / G::BN);
@@ -959,7 +959,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwd8_kernel(mok_bwd_args a, i
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
   int e, mt_, nt_;
-  if (!dw_tile_of(a.E, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  if (!dw_tile_of(a.E, a.eorder, ntm, (int)((a.I + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
   const int tl = mt_ * (int)((a.I + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((I + G::BN - 1) / G::BN);
@@ -977,7 +977,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dwgu8_kernel(mok_bwd_args a, 
   using G = G256;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[tile_lds_bytes<Smem<G, true>>()];
   int e, mt_, nt_;
-  if (!dw_tile_of(a.E, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
+  if (!dw_tile_of(a.E, a.eorder, ntm, (int)((a.H + G::BN - 1) / G::BN), ry, e, mt_, nt_)) return;
   const int tl = mt_ * (int)((a.H + G::BN - 1) / G::BN) + nt_;
   const int64_t H = a.H, I = a.I;
   const int ntn = (int)((H + G::BN - 1) / G::BN);

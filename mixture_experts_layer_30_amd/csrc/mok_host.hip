@@ -77,7 +77,7 @@ mok_status resolve(const mok_problem* p, const mok_config* c, Resolved* r) {
 }
 
 struct SchedLayout {
-  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, tok,
+  size_t status, counts, offsets, perm, dest, n_fwd, fwd_tiles, mb_start, n_bwd, bwd_tiles, tok, eorder,
       chunk_counts, total;
 };
 
@@ -96,6 +96,8 @@ SchedLayout sched_layout(const Resolved& r) {
   L.bwd_tiles = o; o = align_up(o + sizeof(mok_tile) * (size_t)r.max_bwd_tiles);
   // token of each permuted row (perm[p] / k), read by the GEMMs' row loaders
   L.tok = o;       o = align_up(o + 4 * ((size_t)r.R + kTokPad));
+  // experts by descending count (ties to the lower id)
+  L.eorder = o;    o = align_up(o + 4 * (size_t)r.E);
   // scratch of the build: per-chunk counts per bucket
   const int64_t chunk = mok_schedule_chunk_rows(r.R);
   L.chunk_counts = o; o = align_up(o + 4 * (size_t)((r.R + chunk - 1) / chunk) * (r.E + 1));
@@ -118,6 +120,7 @@ mok_sched_ptrs sched_ptrs(const Resolved& r, void* base) {
   s.mb_tile_start = reinterpret_cast<int32_t*>(b + L.mb_start);
   s.n_bwd_tiles = reinterpret_cast<int32_t*>(b + L.n_bwd);
   s.bwd_tiles = reinterpret_cast<mok_tile*>(b + L.bwd_tiles);
+  s.eorder = reinterpret_cast<int32_t*>(b + L.eorder);
   return s;
 }
 
@@ -405,6 +408,7 @@ mok_status mok_get_schedule_layout(const mok_problem* problem, const mok_config*
   out->perm = L.perm; out->dest = L.dest; out->n_fwd_tiles = L.n_fwd;
   out->fwd_tiles = L.fwd_tiles; out->mb_tile_start = L.mb_start; out->n_bwd_tiles = L.n_bwd;
   out->bwd_tiles = L.bwd_tiles; out->total = L.total; out->arrays = L.chunk_counts;
+  out->expert_order = L.eorder;
   out->minibatch_rows = r.M; out->ring_slots = r.n_slots; out->n_minibatches = r.n_mb;
   out->max_fwd_tiles = r.max_fwd_tiles; out->max_bwd_tiles = r.max_bwd_tiles;
   out->fwd_tile_rows = kTileRowsFwd; out->bwd_tile_rows = kTileRowsBwd;
@@ -624,7 +628,8 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   mok_bwd_args a;
   memset(&a, 0, sizeof a);
   a.T = r.T; a.H = r.H; a.I = r.I; a.E = r.E; a.topk = r.k;
-  a.perm = sp.perm; a.offsets = sp.offsets; a.tiles = sp.bwd_tiles; a.n_tiles = sp.n_bwd_tiles;
+  a.perm = sp.perm; a.offsets = sp.offsets; a.eorder = sp.eorder;
+  a.tiles = sp.bwd_tiles; a.n_tiles = sp.n_bwd_tiles;
   a.max_tiles = r.max_bwd_tiles;
   a.wg = static_cast<const bf16_t*>(weights->w_gate);
   a.wu = static_cast<const bf16_t*>(weights->w_up);

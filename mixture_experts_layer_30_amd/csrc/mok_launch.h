@@ -18,6 +18,7 @@ struct mok_sched_ptrs {
   int32_t* mb_tile_start;
   int32_t* n_bwd_tiles;
   mok_tile* bwd_tiles;
+  int32_t* eorder;       // [E] experts by descending count, ties to the lower id
 };
 
 // Zero entries after the R entries of the token table: the GEMM loaders read
@@ -144,6 +145,7 @@ struct mok_bwd_args {
   int E, topk;
   const int32_t* perm;
   const int32_t* offsets;
+  const int32_t* eorder;  // experts by descending count (the weight-gradient order)
   const mok_tile* tiles;
   const int32_t* n_tiles;
   int max_tiles;

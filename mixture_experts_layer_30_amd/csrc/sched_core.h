@@ -160,6 +160,7 @@ template <int NT>
 struct ScanLds {
   int sums[2 * (NT / 64) + 1];
   int s_off[kMaxBuckets + 1];
+  int s_cnt[kMaxBuckets];
   int s_flag;
 };
 
@@ -207,6 +208,7 @@ MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int3
       base[b] = excl;
       if (v < nb) {
         L.s_off[v] = excl;
+        L.s_cnt[v] = run[b];
         if (v < E) s.counts[v] = run[b];
         s.offsets[v] = excl;                     // offsets[E] = valid rows
         if (v == E && run[b] > 0) L.s_flag = 1;
@@ -276,6 +278,17 @@ MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int3
     start_b += nbk[b];
   }
   for (int q = tid; q < kTokPad; q += NT) s.tok[R + q] = 0;
+  // experts by descending count, ties to the lower id: the rank of e is the
+  // number of experts before it in that order
+  for (int e = tid; e < E; e += NT) {
+    const int ce = L.s_cnt[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const int cf = L.s_cnt[f];
+      rank += (cf > ce || (cf == ce && f < e)) ? 1 : 0;
+    }
+    s.eorder[rank] = e;
+  }
   if (tid == 0) {
     *s.n_fwd_tiles = total_f;
     *s.n_bwd_tiles = total_b;

@@ -110,6 +110,7 @@ def read_schedule(w: Workspace):
         "fwd_tiles": arr(L.fwd_tiles, 4 * nf).reshape(nf, 4),
         "mb_tile_start": arr(L.mb_tile_start, L.n_minibatches + 1),
         "bwd_tiles": arr(L.bwd_tiles, 4 * nb).reshape(nb, 4),
+        "expert_order": arr(L.expert_order, E),
         "M": L.minibatch_rows, "n_slots": L.ring_slots, "n_mb": L.n_minibatches,
         "fwd_tile_rows": L.fwd_tile_rows, "bwd_tile_rows": L.bwd_tile_rows,
     }

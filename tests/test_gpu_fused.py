@@ -66,7 +66,8 @@ def same_bits(a, b):
 def assert_same_schedule(ws1, ws2):
     from mixture_experts_layer_30_amd import functional as F
     s1, s2 = F.read_schedule(ws1), F.read_schedule(ws2)
-    for key in ("status", "counts", "offsets", "perm", "dest", "fwd_tiles", "mb_tile_start", "bwd_tiles"):
+    for key in ("status", "counts", "offsets", "perm", "dest", "fwd_tiles", "mb_tile_start", "bwd_tiles",
+                "expert_order"):
         assert np.array_equal(np.asarray(s1[key]), np.asarray(s2[key])), key
 
 

@@ -39,6 +39,8 @@ def check(ids, E, **cfg):
     np.testing.assert_array_equal(got["offsets"], ref["offsets"])
     np.testing.assert_array_equal(got["perm"], ref["perm"])
     np.testing.assert_array_equal(got["dest"], ref["dest"])
+    # the weight-gradient GEMMs' expert order: descending count, ties to the lower id
+    np.testing.assert_array_equal(got["expert_order"], np.argsort(-np.asarray(ref["counts"]), kind="stable"))
     nvalid = int(ref["offsets"][E])
     check_tiles(got["fwd_tiles"], ref["offsets"], E, nvalid, got["fwd_tile_rows"], got["M"])
     check_tiles(got["bwd_tiles"], ref["offsets"], E, nvalid, got["bwd_tile_rows"], 0)
