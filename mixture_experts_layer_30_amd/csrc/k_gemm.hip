@@ -375,9 +375,11 @@ MOK_DEV PersistPlan persist_plan(const mok_fwd_args& a) {
 }
 
 // Thread 0 of every workgroup: records whether it runs on the XCD of its
-// queue q (misplaced flag) and arrives at counter `arrived`.
-MOK_DEV void persist_arrive(const PersistCounters& C, int* arrived, int q) {
-  if (xcc_id() != (uint32_t)q) __hip_atomic_fetch_or(C.misplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// queue q (misplaced flag; set regardless with force_agent) and arrives at
+// counter `arrived`.
+MOK_DEV void persist_arrive(const PersistCounters& C, int* arrived, int q, bool force_agent) {
+  if (force_agent || xcc_id() != (uint32_t)q)
+    __hip_atomic_fetch_or(C.misplaced, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_fetch_add(arrived, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_persistent_kernel(mok_fwd_arg
 
   // placement: every workgroup on the XCD of its queue, or agent-scope sync
   if (threadIdx.x == 0) {
-    persist_arrive(C, C.arrived, q);
+    persist_arrive(C, C.arrived, q, ps.force_agent != 0);
     int agent_sync = -1;   // -1: the grid did not gather (stop)
     if (persist_spin(C.arrived, (int)gridDim.x, C.stop, ps)) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -507,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void layer_fwd_kernel(mok_fwd_args a, 
     __syncthreads();
   }
   persist_release(true);
-  if (threadIdx.x == 0) persist_arrive(C, step + 0, q);
+  if (threadIdx.x == 0) persist_arrive(C, step + 0, q, ps.force_agent != 0);
 
   // 2. the scan
   if (g == 0) {

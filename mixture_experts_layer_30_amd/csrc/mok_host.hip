@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -478,6 +479,10 @@ mok_persist_args persist_args(const Resolved& r, const mok_sched_ptrs& sp, uint8
   ps.max_tiles = r.max_fwd_tiles;
   ps.max_mb_tiles = max_mb_tiles;
   ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
+  // MOK_PERSIST_AGENT_SYNC=1 selects the agent-scope synchronisation of a
+  // misplaced grid on any placement (to test that path)
+  const char* env = getenv("MOK_PERSIST_AGENT_SYNC");
+  ps.force_agent = (env && env[0] == '1') ? 1 : 0;
   return ps;
 }
 

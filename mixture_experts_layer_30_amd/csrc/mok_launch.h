@@ -119,6 +119,9 @@ struct mok_persist_args {
   int max_tiles;         // bound on mb_tile_start[n_mb]
   int max_mb_tiles;      // bound on the row tiles of one minibatch
   uint64_t spin_limit;   // ticks of the 64-bit real-time counter one wait may last
+  int force_agent;       // 1: synchronise at agent scope even when every workgroup
+                         // runs on the XCD of its queue (the path taken otherwise
+                         // only on a different placement; for tests)
 };
 inline int64_t mok_persist_counters(int max_tiles) { return mok::persist_counter_count(max_tiles); }
 // grid: a multiple of 8, at most the workgroups resident at once (one per CU)

@@ -132,3 +132,28 @@ def test_persistent_bitwise_deterministic_10_runs():
         y, _, s = run(p, d, driver=2)
         assert not (s & GIVE_UP)
         assert torch.equal(y.view(torch.int16), ref)
+
+
+@pytest.mark.parametrize("p", [SMALL[0], SMALL[1], CONFIGS[1]], ids=lambda p: p.name)
+def test_agent_scope_sync_path_matches(p, monkeypatch):
+    """The synchronisation a grid takes when some workgroup does not run on the
+    XCD of its queue (every signal releases, every wait acquires at agent
+    scope), forced on: driver 2 and the single launch stay bitwise equal to
+    driver 1, the give-up bit clear."""
+    import torch
+    from mixture_experts_layer_30_amd import functional as F
+    print(f"[persistent] {p.name} agent-scope sync", flush=True)
+    d = device_inputs(p)
+    cfg = dict(minibatch_rows=64, ring_slots=2) if p.T < 1000 else {}
+    y1, ws1, _ = run(p, d, training=True, driver=1, **cfg)
+    monkeypatch.setenv("MOK_PERSIST_AGENT_SYNC", "1")
+    y2, ws2, s2 = run(p, d, training=True, driver=2, **cfg)
+    assert not (s2 & GIVE_UP)
+    assert same_bits(y1, y2)
+    assert same_bits(ws1.fwd_ctx, ws2.fwd_ctx)
+    ws3 = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True, **cfg)
+    y3 = F.run_forward_fused(ws3, d["ids"], d["x"], d["w"], d["weights"])
+    torch.cuda.synchronize()
+    assert not (F.read_schedule(ws3)["status"] & GIVE_UP)
+    assert same_bits(y1, y3)
+    assert same_bits(ws1.fwd_ctx, ws3.fwd_ctx)
