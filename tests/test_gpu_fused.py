@@ -187,3 +187,25 @@ def test_fused_bitwise_deterministic_10_runs():
         torch.cuda.synchronize()
         assert not (F.read_schedule(ws)["status"] & GIVE_UP)
         assert torch.equal(y.view(torch.int16), ref)
+
+
+def test_fused_empty_input_writes_empty_schedule():
+    """T = 0: no layer work; the schedule is the empty one mok_build_schedule
+    writes (zero counts and offsets, no tiles)."""
+    import torch
+    from mixture_experts_layer_30_amd import functional as F
+    print("[fused] T=0", flush=True)
+    ws = F.get_workspace(0, 128, 128, 4, 2, training=True)
+    ws.schedule.fill_(0x5A)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    wts = tuple(torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in ((4, 128, 128),) * 3)
+    y = F.run_forward_fused(ws, ids, x, w, wts)
+    torch.cuda.synchronize()
+    s = F.read_schedule(ws)
+    assert y.shape == (0, 128)
+    assert s["status"] == 0
+    assert not s["counts"].any() and not s["offsets"].any()
+    assert s["fwd_tiles"].shape[0] == 0 and s["bwd_tiles"].shape[0] == 0
+    assert s["expert_order"].tolist() == [0, 1, 2, 3]
