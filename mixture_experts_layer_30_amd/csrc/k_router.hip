@@ -43,51 +43,69 @@ MOK_DEV void split3(float w0, float w1, uint32_t& hi, uint32_t& mid, uint32_t& l
   lo = (__float_as_uint(q0) >> 16) | (__float_as_uint(q1) & 0xFFFF0000u);
 }
 
-// Forward: one workgroup per 16 tokens. The logits x . Wr^T are a dense
-// contraction (16 token rows x E expert columns x H), done on the matrix
-// cores with v_mfma_f32_16x16x32_bf16 (lane l supplies row l%16 and the 8 K
-// values from 8(l/16), so four lanes read one full 128-byte line of a Wr
+// Forward: one workgroup per TT tokens (TT = 16, or 64 on large inputs with
+// E <= 128). The logits x . Wr^T are a dense contraction (TT token rows x E
+// expert columns x H), done on the matrix cores with
+// v_mfma_f32_16x16x32_bf16 (lane l supplies row l%16 of a 16-row tile and the
+// 8 K values from 8(l/16), so four lanes read one full 128-byte line of a Wr
 // row): x is bf16 already and Wr is split exactly into three bf16 parts, so
 // every product is exact and the fp32 sums run in the MFMA's fixed order.
 // Wave v sums the 32-wide K steps v, v + 8, ... for up to 64 experts at a
-// time; the eight partial sums are added in the order v = 0..7 through LDS. Then each wavefront selects the top-k of two
-// tokens: with E <= 64 by ranking each lane's expert against all others;
-// otherwise lane l holds experts l, l + 64, ... and each of k rounds takes
-// the best unselected (score, expert) pair of the wavefront.
+// time; the eight partial sums are added in the order v = 0..7 through LDS
+// (with TT = 64 one 16-row tile at a time). Each split of a Wr block serves
+// the TT/16 row tiles of the workgroup, so larger TT splits and reads Wr
+// fewer times per token; every logit is the same sum in the same order
+// whatever TT. Then each wavefront selects the top-k of TT/8 tokens: with
+// E <= 64 by ranking each lane's expert against all others; otherwise lane
+// l holds experts l, l + 64, ... and each of k rounds takes the best
+// unselected (score, expert) pair of the wavefront.
+template <int TT>
 __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w) {
-  __shared__ float lg[kRouterTokens * kRouterMaxE];                       // [32][E] logits
-  __shared__ float part[kRouterWaves - 1][kRouterTokens * kRouterGroup];  // waves 1..7 partials
+  constexpr int NR = TT / 16;                                             // 16-row tiles
+  constexpr int LGE = TT == 16 ? kRouterMaxE : 128;                       // logit row length in LDS
+  constexpr int NU = TT == 16 ? 4 : 2;                                    // K steps per load batch
+  __shared__ float lg[TT * LGE];                                          // [TT][E] logits
+  __shared__ float part[kRouterWaves - 1][16 * kRouterGroup];             // waves 1..7 partials
   __shared__ float bsh[kRouterMaxE];                                      // bias (0 if none)
-  const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
   const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
   const int r16 = lane & 15, kh = 8 * (lane >> 4);
   const int nsteps = H / 32;                                              // 32-wide K steps
-  const bool trow = t0 + r16 < T;
-  const bf16_t* xrow = x + (t0 + (trow ? r16 : 0)) * H + kh;   // row t0 exists: t0 < T
+  bool trow[NR];
+  const bf16_t* xrow[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    trow[r] = t0 + 16 * r + r16 < T;
+    xrow[r] = x + (t0 + (trow[r] ? 16 * r + r16 : 0)) * H + kh;           // row t0 exists: t0 < T
+  }
   for (int e = threadIdx.x; e < E; e += kRouterThreads) bsh[e] = bias ? bias[e] : 0.f;
   for (int g0 = 0; g0 < E; g0 += kRouterGroup) {
     const int nb = min(4, (E - g0 + 15) / 16);                           // column tiles in this group
-    f32x4_t acc[4];
+    f32x4_t acc[NR][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[r][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // wave v takes the K steps v, v + 8, v + 16, ... in ascending order, in
-    // batches of up to 4 whose loads are all issued before the first MFMA
-    for (int s0 = v; s0 < nsteps; s0 += 4 * kRouterWaves) {
-      const int nu = min(4, (nsteps - s0 + kRouterWaves - 1) / kRouterWaves);
-      uint4 xa[4];
-      float4 wv[4][4][2];
+    // batches of up to NU whose loads are all issued before the first MFMA
+    for (int s0 = v; s0 < nsteps; s0 += NU * kRouterWaves) {
+      const int nu = min(NU, (nsteps - s0 + kRouterWaves - 1) / kRouterWaves);
+      uint4 xa[NU][NR];
+      float4 wv[4][NU][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xa[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (u < nu && trow) xa[u] = *reinterpret_cast<const uint4*>(xrow + 32 * (s0 + kRouterWaves * u));
-      }
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          xa[u][r] = make_uint4(0u, 0u, 0u, 0u);
+          if (u < nu && trow[r]) xa[u][r] = *reinterpret_cast<const uint4*>(xrow[r] + 32 * (s0 + kRouterWaves * u));
+        }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int e = g0 + 16 * b + r16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NU; ++u) {
           wv[b][u][0] = wv[b][u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (b < nb && u < nu && e < E) {
             const float4* src =
@@ -98,9 +116,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < NU; ++u) {
         if (u >= nu) break;
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[u]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           if (b >= nb) break;
@@ -110,46 +127,55 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
           split3(p.z, p.w, hi.y, mid.y, lo.y);
           split3(q.x, q.y, hi.z, mid.z, lo.z);
           split3(q.z, q.w, hi.w, mid.w, lo.w);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[b], 0, 0, 0);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[b], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[u][r]);
+            acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, hi), acc[r][b], 0, 0, 0);
+            acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, mid), acc[r][b], 0, 0, 0);
+            acc[r][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, lo), acc[r][b], 0, 0, 0);
+          }
         }
       }
     }
-    // accumulator element i: token row 4(lane/16) + i, expert column lane%16
-    if (v > 0) {
+    // accumulator element i: token row 16r + 4(lane/16) + i, expert column
+    // lane%16; the partials of one row tile at a time through LDS
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b >= nb) break;
+    for (int r = 0; r < NR; ++r) {
+      if (v > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[v - 1][(4 * (lane >> 4) + i) * kRouterGroup + 16 * b + r16] = acc[b][i];
-      }
-    }
-    __syncthreads();
-    if (v == 0) {
+        for (int b = 0; b < 4; ++b) {
+          if (b >= nb) break;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b >= nb) break;
-        const int e = g0 + 16 * b + r16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 4 * (lane >> 4) + i;
-          const int pi = row * kRouterGroup + 16 * b + r16;
-          float s = acc[b][i];
-          for (int j = 0; j < kRouterWaves - 1; ++j) s += part[j][pi];
-          if (e < E) lg[row * E + e] = s;
+          for (int i = 0; i < 4; ++i) part[v - 1][(4 * (lane >> 4) + i) * kRouterGroup + 16 * b + r16] = acc[r][b][i];
         }
       }
+      __syncthreads();
+      if (v == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b >= nb) break;
+          const int e = g0 + 16 * b + r16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 4 * (lane >> 4) + i;
+            const int pi = row * kRouterGroup + 16 * b + r16;
+            float sum = acc[r][b][i];
+            for (int j = 0; j < kRouterWaves - 1; ++j) sum += part[j][pi];
+            if (e < E) lg[(16 * r + row) * E + e] = sum;
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
+  constexpr int TPW = TT / kRouterWaves;                                  // tokens per wavefront
   if (E <= 64) {
     // one expert per lane: its rank is the number of experts that beat it
     // (LDS broadcast reads, no cross-lane traffic); the k lanes of rank < k
     // write their own slot. The softmax runs over the selected experts in
     // ascending id, the same order in every lane.
-    for (int q = 0; q < kRouterTokens / kRouterWaves; ++q) {
-      const int tt = (kRouterTokens / kRouterWaves) * v + q;
+    for (int q = 0; q < TPW; ++q) {
+      const int tt = TPW * v + q;
       const int64_t t = t0 + tt;
       if (t >= T) break;
       const float* row = lg + tt * E;
@@ -171,8 +197,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
     }
     return;
   }
-  for (int q = 0; q < kRouterTokens / kRouterWaves; ++q) {
-    const int tt = (kRouterTokens / kRouterWaves) * v + q;
+  for (int q = 0; q < TPW; ++q) {
+    const int tt = TPW * v + q;
     const int64_t t = t0 + tt;
     if (t >= T) break;
     uint64_t taken = 0;                          // bit i: expert lane + 64 i selected
@@ -185,8 +211,8 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
       for (int i = 0; lane + 64 * i < E; ++i) {
         const int e = lane + 64 * i;
         if ((taken >> i) & 1) continue;
-        const float s = lg[tt * E + e] + bsh[e];
-        if (be == 0x7FFFFFFF || beats(s, e, bs, be)) { bs = s; be = e; }
+        const float sc = lg[tt * E + e] + bsh[e];
+        if (be == 0x7FFFFFFF || beats(sc, e, bs, be)) { bs = sc; be = e; }
       }
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) {
@@ -307,8 +333,17 @@ __global__ __launch_bounds__(64 * kDwrWaves) void router_dwr_kernel(
 hipError_t mok_launch_router_forward(const bf16_t* x, const float* wr, const float* bias, int64_t T, int H,
                                      int E, int k, int32_t* ids, float* w, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)((T + kRouterTokens - 1) / kRouterTokens);
-  hipLaunchKernelGGL(router_fwd_kernel, dim3(grid), dim3(kRouterThreads), 0, st, x, wr, bias, T, H, E, k, ids, w);
+  // 64-token workgroups once they still fill every compute unit several
+  // times over (and the logits of 64 tokens fit in LDS), else 16
+  if (E <= 128 && T >= 64 * 256) {
+    const unsigned grid = (unsigned)((T + 63) / 64);
+    hipLaunchKernelGGL(router_fwd_kernel<64>, dim3(grid), dim3(kRouterThreads), 0, st, x, wr, bias, T, H, E, k, ids,
+                       w);
+  } else {
+    const unsigned grid = (unsigned)((T + kRouterTokens - 1) / kRouterTokens);
+    hipLaunchKernelGGL(router_fwd_kernel<kRouterTokens>, dim3(grid), dim3(kRouterThreads), 0, st, x, wr, bias, T, H,
+                       E, k, ids, w);
+  }
   return hipGetLastError();
 }
 

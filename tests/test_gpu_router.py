@@ -103,6 +103,27 @@ def test_router_forward_full_size_and_deterministic():
     assert _check_selection(ids, w, logits, bias, p.k) >= 0.95 * p.T
 
 
+@pytest.mark.parametrize("E,k", [(48, 6), (128, 8)])   # rank-count and round-based selection
+def test_router_forward_64_token_workgroups_equal_16(E, k):
+    """T >= 16384 with E <= 128 runs 64-token workgroups: every logit is the
+    same sum in the same order as with 16-token workgroups, so ids and
+    weights are bitwise those of the 16-token path (run on the first 16000
+    tokens, below the switch), and match the oracle."""
+    import dataclasses
+    p = problem(16384, 1024, 128, E, k, seed=69)
+    x, wr_eh, bias = _inputs(p, True)
+    ids, w = _run(p, x, wr_eh, bias)
+    q = dataclasses.replace(p, T=16000)
+    ids16, w16 = _run(q, x[:16000], wr_eh, bias)
+    assert np.array_equal(ids[:16000], ids16)
+    assert np.array_equal(w[:16000].view(np.uint32), w16.view(np.uint32))
+    ids2, w2 = _run(p, x, wr_eh, bias)
+    assert np.array_equal(ids, ids2) and np.array_equal(w.view(np.uint32), w2.view(np.uint32))
+    sub = np.r_[0:1000, 16000:16384]             # both kinds of workgroup, and the last one
+    logits, _, _ = oracle.router_forward(bf16_to_f32(x[sub]).astype(np.float64), wr_eh.astype(np.float64), None, k)
+    assert _check_selection(ids[sub], w[sub], logits, bias, k) >= 0.8 * len(sub)
+
+
 @pytest.mark.parametrize("E,k", [(10, 3), (100, 40)])   # rank-count and round-based selection
 def test_router_exact_ties_go_to_the_lower_id(E, k):
     import torch
