@@ -262,12 +262,13 @@ __global__ __launch_bounds__(kThreads, 1) void down_kernel(mok_fwd_args a, int m
 // served by the workgroups that run on XCD q, so h goes from its writer to
 // its readers through one L2: the writer waits until its stores are in the
 // L2 before its counter moves, and the reader invalidates its CU's L1 after
-// the wait. A D item's obuf rows are read only after the launch, so it
-// signals without waiting for its stores. The hazard across XCDs is the reuse of ring rows: dirty h lines
-// of minibatch m left in one XCD's L2 must reach memory before another XCD
-// writes the same rows for minibatch m + N_s, so the last D item of a row
-// tile writes its XCD's L2 back (agent-scope release) before it marks the
-// tile retired, and the reuse waits on retired tiles. At the start every
+// the wait. A D item's obuf rows are read only after the item loop, so it
+// signals without waiting for its stores. The hazard across XCDs is the
+// reuse of ring rows: dirty h lines of minibatch m left in one XCD's L2
+// must reach memory before another XCD writes the same rows for minibatch
+// m + N_s, so the last D item of a row tile writes its XCD's L2 back
+// (agent-scope release) before it marks the tile retired, and the reuse
+// waits on retired tiles. At the start every
 // workgroup checks the XCD it runs on (HW_REG_XCC_ID) against its queue and
 // the grid agrees on the result (one arrival counter); if any workgroup is
 // elsewhere, every signal releases and every wait acquires at agent scope.
