@@ -23,6 +23,9 @@ constexpr int kRouterThreads = 64 * kRouterWaves;
 constexpr int kRouterMaxE = 512;
 constexpr int kRouterGroup = 64;                 // experts per accumulation group (4 column tiles)
 
+typedef __attribute__((ext_vector_type(4))) short rv4i16_t;
+typedef __attribute__((address_space(3))) rv4i16_t* lds_rv4_ptr;
+
 MOK_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOK_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -238,33 +241,56 @@ __global__ __launch_bounds__(kRouterThreads) void router_fwd_kernel(
 
 // Backward, per token: d_sel[t][j] = w_j (g_j - sum_i w_i g_i) (i, j
 // ascending), and dx[t] = sum_j d_sel[t][j] Wr[e_j] in fp32, j ascending,
-// rounded once to bf16. One thread per (token, 8 columns); the thread of
-// column chunk 0 also writes d_sel. Ids outside [0, E) contribute nothing.
+// rounded once to bf16. One wavefront per token: its ids, weights and
+// gradients are wave-uniform (scalar loads), lane l takes the 8-column chunks
+// l, l + 64, ..., two at a time with all their Wr loads in flight; lane 0
+// writes d_sel. Ids outside [0, E) contribute nothing.
 __global__ __launch_bounds__(256) void router_bwd_rows_kernel(
     const float* __restrict__ wr, const int32_t* __restrict__ ids, const float* __restrict__ w,
     const float* __restrict__ g, int64_t T, int H, int E, int k, float* __restrict__ d_sel,
     bf16_t* __restrict__ dx) {
-  const int64_t nch = H / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = idx / nch, c = idx % nch;
+  const int64_t t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int lane = lane_id();
   if (t >= T) return;
+  const int64_t nch = H / 8;
   float s = 0.f;
   for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], g[t * k + j], s);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float dl = w[t * k + j] * (g[t * k + j] - s);
-    if (c == 0) d_sel[t * k + j] = dl;
-    const int e = ids[t * k + j];
-    if (e < 0 || e >= E) continue;
-    const float4* wrow = reinterpret_cast<const float4*>(wr + (int64_t)e * H + 8 * c);
-    const float4 a = wrow[0], b = wrow[1];
-    acc[0] = fmaf(dl, a.x, acc[0]); acc[1] = fmaf(dl, a.y, acc[1]);
-    acc[2] = fmaf(dl, a.z, acc[2]); acc[3] = fmaf(dl, a.w, acc[3]);
-    acc[4] = fmaf(dl, b.x, acc[4]); acc[5] = fmaf(dl, b.y, acc[5]);
-    acc[6] = fmaf(dl, b.z, acc[6]); acc[7] = fmaf(dl, b.w, acc[7]);
+  if (lane == 0)
+    for (int j = 0; j < k; ++j) d_sel[t * k + j] = w[t * k + j] * (g[t * k + j] - s);
+  for (int64_t c0 = lane; c0 < nch; c0 += 128) {
+    float acc[2][8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[b][q] = 0.f;
+    const int64_t cb[2] = {c0, min(c0 + 64, nch - 1)};
+    for (int j = 0; j < k; ++j) {
+      const float dl = w[t * k + j] * (g[t * k + j] - s);
+      const int e = ids[t * k + j];
+      if (e < 0 || e >= E) continue;
+      float4 a[2], b[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4* wrow = reinterpret_cast<const float4*>(wr + (int64_t)e * H + 8 * cb[u]);
+        a[u] = wrow[0];
+        b[u] = wrow[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        acc[u][0] = fmaf(dl, a[u].x, acc[u][0]); acc[u][1] = fmaf(dl, a[u].y, acc[u][1]);
+        acc[u][2] = fmaf(dl, a[u].z, acc[u][2]); acc[u][3] = fmaf(dl, a[u].w, acc[u][3]);
+        acc[u][4] = fmaf(dl, b[u].x, acc[u][4]); acc[u][5] = fmaf(dl, b[u].y, acc[u][5]);
+        acc[u][6] = fmaf(dl, b[u].z, acc[u][6]); acc[u][7] = fmaf(dl, b[u].w, acc[u][7]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && c0 + 64 >= nch) break;
+      reinterpret_cast<uint4*>(dx + t * H)[cb[u]] =
+          make_uint4(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]),
+                     pack_bf16x2(acc[u][4], acc[u][5]), pack_bf16x2(acc[u][6], acc[u][7]));
+    }
   }
-  reinterpret_cast<uint4*>(dx + t * H)[c] = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
 // dWr[e][h] = sum over the permuted rows p of expert e of d_sel[perm[p]] *
@@ -328,6 +354,155 @@ __global__ __launch_bounds__(64 * kDwrWaves) void router_dwr_kernel(
   }
 }
 
+// dWr for E <= 128 and k <= 8, as a dense contraction over the tokens on
+// the matrix cores: dWr[e][h] = sum over t of D[t][e] x[t][h] with D[t][e] =
+// d_sel[t][j] for the j with ids[t][j] == e (0 for the other experts). x is
+// read once (the per-expert kernel above reads each token's row k times), at
+// the price of E/k times the products, which are cheap here. Workgroup = NW
+// wavefronts over 32 output columns of every expert; wavefront v takes the
+// 32-token steps v, v + NW, ... in ascending order, each on its own: it
+// scatters its 32 tokens' d_sel into its LDS block D^T [EP][32] (cleared
+// again after use), stages the tokens' 32 x 32 slice of x in LDS, and runs
+// v_mfma_f32_16x16x32_bf16 with D^T split exactly into three bf16 parts (so
+// every product d_sel * x is exact and the fp32 sums follow the MFMA's fixed
+// order), the x operand read transposed (ds_read_b64_tr_b16). The next
+// step's ids, d_sel and x are loaded into registers before the current step
+// runs. The NW partial sums are added in the order v = 0 .. NW-1. Bitwise
+// reproducible.
+template <int EP, int NW>
+__global__ __launch_bounds__(64 * NW) void router_dwr_dense_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ ids, const float* __restrict__ d_sel, int64_t T,
+    int H, int E, int k, float* __restrict__ d_wr) {
+  constexpr int NC = 32;                          // output columns per workgroup
+  constexpr int RT = EP / 16, CT = NC / 16;       // 16 x 16 output tiles
+  constexpr int DP = 36;                          // D^T row pitch (floats)
+  constexpr int XB = 2 * NC;                      // x slice row bytes
+  constexpr int KMAX = 8;
+  static_assert((NW - 1) * EP * NC <= NW * EP * DP, "partials fit in the D^T blocks");
+  __shared__ __attribute__((aligned(16))) float dT[NW][EP * DP];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NW][32 * XB];
+  const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
+  const int g = lane >> 4, L = lane & 15;
+  const int64_t c0 = (int64_t)blockIdx.x * NC;
+  float* dw = dT[v];
+  uint8_t* xw = xs[v];
+  for (int i = lane; i < EP * DP; i += 64) dw[i] = 0.f;
+  f32x4_t acc[RT][CT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int64_t nsteps = (T + 31) / 32;
+  // this lane's share of a step: token t0 + (lane & 31)'s ids and d_sel
+  // (lanes < 32), and two 16-byte chunks of the x slice
+  int e_n[KMAX];
+  float d_n[KMAX];
+  uint4 x_n[2];
+  auto load = [&](int64_t s) {
+    const int64_t t0 = 32 * s, t = t0 + (lane & 31);
+    const bool tok_ok = s < nsteps && lane < 32 && t < T;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      e_n[j] = -1;
+      d_n[j] = 0.f;
+      if (tok_ok && j < k) {
+        e_n[j] = ids[t * k + j];
+        d_n[j] = d_sel[t * k + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = lane + 64 * u, r = q / (XB / 16), ch = q % (XB / 16);
+      x_n[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (s < nsteps && t0 + r < T) x_n[u] = *reinterpret_cast<const uint4*>(x + (t0 + r) * H + c0 + 8 * ch);
+    }
+  };
+  load(v);
+  for (int64_t s = v; s < nsteps; s += NW) {
+    int e_c[KMAX];
+    float d_c[KMAX];
+    uint4 x_c[2];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) { e_c[j] = e_n[j]; d_c[j] = d_n[j]; }
+    x_c[0] = x_n[0];
+    x_c[1] = x_n[1];
+    load(s + NW);                                // in flight while this step runs
+    // scatter (this lane's token; an expert appears once per token, duplicates add)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (e_c[j] >= 0 && e_c[j] < E) dw[e_c[j] * DP + lane] += d_c[j];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = lane + 64 * u, r = q / (XB / 16), ch = q % (XB / 16);
+      *reinterpret_cast<uint4*>(xw + r * XB + 16 * ch) = x_c[u];
+    }
+    // the wavefront's LDS writes land in order before its reads below
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16x8_t bfr[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      // lane 4q + p of a 16-lane group addresses k-row q, columns 4p..4p+3;
+      // lane L receives column L, 4 k-rows; two reads give k-rows 8g .. 8g+7
+      const uint8_t* a0 = xw + (8 * g + (L >> 2)) * XB + 2 * (16 * c + 4 * (L & 3));
+      const rv4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_rv4_ptr)(a0));
+      const rv4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_rv4_ptr)(a0 + 4 * XB));
+      typedef __attribute__((ext_vector_type(8))) short v8i16_t;
+      bfr[c] = __builtin_bit_cast(bf16x8_t, v8i16_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float4 p = *reinterpret_cast<const float4*>(dw + (16 * r + L) * DP + 8 * g);
+      const float4 q = *reinterpret_cast<const float4*>(dw + (16 * r + L) * DP + 8 * g + 4);
+      uint4 hi, mid, lo;
+      split3(p.x, p.y, hi.x, mid.x, lo.x);
+      split3(p.z, p.w, hi.y, mid.y, lo.y);
+      split3(q.x, q.y, hi.z, mid.z, lo.z);
+      split3(q.z, q.w, hi.w, mid.w, lo.w);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), bfr[c], acc[r][c], 0, 0, 0);
+        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, mid), bfr[c], acc[r][c], 0, 0, 0);
+        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), bfr[c], acc[r][c], 0, 0, 0);
+      }
+    }
+    // reads of this step done before the clear and the next step's writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (e_c[j] >= 0 && e_c[j] < E) dw[e_c[j] * DP + lane] = 0.f;
+  }
+  // accumulator element i: expert 16r + 4g + i, column 16c + L; the partials
+  // of waves 1 .. NW-1 go through the D^T blocks (free now)
+  __syncthreads();
+  float* part = &dT[0][0];
+  if (v > 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[((v - 1) * EP + 16 * r + 4 * g + i) * NC + 16 * c + L] = acc[r][c][i];
+  }
+  __syncthreads();
+  if (v == 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 16 * r + 4 * g + i, col = 16 * c + L;
+          float sum = acc[r][c][i];
+          for (int u = 0; u < NW - 1; ++u) sum += part[(u * EP + e) * NC + col];
+          if (e < E) d_wr[(int64_t)e * H + c0 + col] = sum;
+        }
+  }
+}
+
 }  // namespace
 
 hipError_t mok_launch_router_forward(const bf16_t* x, const float* wr, const float* bias, int64_t T, int H,
@@ -351,10 +526,22 @@ hipError_t mok_launch_router_backward(const bf16_t* x, const float* wr, const in
                                       const float* g, int64_t T, int H, int E, int k,
                                       const int32_t* offsets, const int32_t* perm, const int32_t* tok,
                                       float* d_sel, bf16_t* dx, float* d_wr, hipStream_t st) {
-  if (T > 0) {
-    const int64_t n = T * (H / 8);
-    hipLaunchKernelGGL(router_bwd_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, wr, ids, w, g,
-                       T, H, E, k, d_sel, dx);
+  if (T > 0)
+    hipLaunchKernelGGL(router_bwd_rows_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, wr, ids, w, g, T, H,
+                       E, k, d_sel, dx);
+  if (E <= 128 && k <= 8 && T > 0) {
+    // dense over the tokens (x read once); H is a multiple of 128
+    const dim3 grid((unsigned)(H / 32));
+    if (E <= 32)
+      hipLaunchKernelGGL((router_dwr_dense_kernel<32, 16>), grid, dim3(64 * 16), 0, st, x, ids, d_sel, T, H, E, k,
+                         d_wr);
+    else if (E <= 64)
+      hipLaunchKernelGGL((router_dwr_dense_kernel<64, 8>), grid, dim3(64 * 8), 0, st, x, ids, d_sel, T, H, E, k,
+                         d_wr);
+    else
+      hipLaunchKernelGGL((router_dwr_dense_kernel<128, 4>), grid, dim3(64 * 4), 0, st, x, ids, d_sel, T, H, E, k,
+                         d_wr);
+    return hipGetLastError();
   }
   const int ncol = (H + 511) / 512;
   hipLaunchKernelGGL(router_dwr_kernel, dim3((unsigned)(E * ncol)), dim3(64 * kDwrWaves), 0, st, x, d_sel, offsets, perm, tok,
