@@ -123,6 +123,19 @@ def test_calls_reject_bad_arguments_before_any_launch():
     wm = mok.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
     assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(wm), fake,
                           fake, fake, fake, fake, fake, fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
+    # single-launch forward: the schedule's and the forward's checks
+    assert L.mok_forward_fused(ctypes.byref(prob), None, None, fake, sb, fake, fake, ctypes.byref(w), fake, None,
+                               fake, ws, None) == mok.MOK_ERR_INVALID_ARG          # no topk_ids
+    assert L.mok_forward_fused(ctypes.byref(prob), None, fake, None, sb, fake, fake, ctypes.byref(w), fake, None,
+                               fake, ws, None) == mok.MOK_ERR_INVALID_ARG          # no schedule
+    assert L.mok_forward_fused(ctypes.byref(prob), None, fake, fake, sb - 1, fake, fake, ctypes.byref(w), fake,
+                               None, fake, ws, None) == mok.MOK_ERR_BUFFER_TOO_SMALL
+    assert L.mok_forward_fused(ctypes.byref(prob), None, fake, fake, sb, fake, fake, ctypes.byref(w), fake, None,
+                               fake, ws - 1, None) == mok.MOK_ERR_BUFFER_TOO_SMALL
+    assert L.mok_forward_fused(ctypes.byref(prob), None, fake, fake, sb, fake, fake, ctypes.byref(w0), fake, None,
+                               fake, ws, None) == mok.MOK_ERR_INVALID_ARG          # missing w_up
+    assert L.mok_forward_fused(ctypes.byref(pm), None, fake, fake, sb, fake, fake, ctypes.byref(w), fake, None,
+                               fake, wsm, None) == mok.MOK_ERR_INVALID_ARG         # MXFP8 without scales
     # quantize: K must be a multiple of 32
     assert L.mok_mxfp8_quantize(fake, 4, 48, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
     assert L.mok_mxfp8_quantize(fake, -1, 64, fake, fake, None) == mok.MOK_ERR_INVALID_ARG
