@@ -224,7 +224,8 @@ mok_status mok_build_schedule_noalloc(const mok_problem* problem, const mok_conf
  * expert outputs and the gate/up pre-activations (bf16). MXFP8 ([MoK card]
  * "Core concepts": weights pre-quantized with mok_mxfp8_quantize): x rows are
  * quantized along H (once per token) and h along I the same way on the fly;
- * accumulation is fp32, y is bf16. With config->driver == 2 the call may set
+ * accumulation is fp32, y is bf16. x, topk_w and y may be NULL when T = 0
+ * (nothing is read or written). With config->driver == 2 the call may set
  * MOK_STATUS_WATCHDOG in the schedule's status word (the only write to the
  * schedule). */
 mok_status mok_forward(const mok_problem* problem, const mok_config* config,

@@ -96,6 +96,13 @@ MOK_DEV uint32_t lds_addr(const void* p) {
 // keeps the compiler from moving LDS accesses across the barrier.
 MOK_DEV void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 
+// Workgroup barrier that waits for this wavefront's LDS operations only: its
+// global loads and stores stay in flight (the workgroup-scope release of
+// __syncthreads would wait for them). For reuse of LDS that holds no copy
+// targets; the wait and the barrier are one statement, so no LDS access is
+// placed between them.
+MOK_DEV void barrier_lds_only() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------------ row sources
 // Byte address of element k = 0 of operand row r (rows past the end clamp).
 struct RowsStrided {
@@ -811,9 +818,9 @@ MOK_DEV void store_tile_bf16(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int nro
   constexpr int CPR = G::BN / 8;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    __syncthreads();
+    barrier_lds_only();
     HS::put(lds, acc, half);
-    __syncthreads();
+    barrier_lds_only();
     const int rows = min(128, nrows - 128 * half);
     for (int idx = threadIdx.x; idx < 128 * CPR; idx += kThreads) {
       const int r = idx / CPR, c = (idx % CPR) * 8;
@@ -841,7 +848,7 @@ MOK_DEV void store_tile_bf16_t(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int n
   typedef __attribute__((ext_vector_type(2))) __bf16 b2_t;
   constexpr int PITCH = 512;
   const int l = lane_id();
-  __syncthreads();
+  barrier_lds_only();
 #pragma unroll
   for (int i = 0; i < G::FM; ++i)
 #pragma unroll
@@ -857,7 +864,7 @@ MOK_DEV void store_tile_bf16_t(uint8_t* lds, const Acc<G::FM, G::FN>& acc, int n
             make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     }
-  __syncthreads();
+  barrier_lds_only();
   constexpr int CPR = G::BN / 8;                                     // 16-byte chunks per row
 #pragma unroll 4
   for (int idx = threadIdx.x; idx < G::BM * CPR; idx += kThreads) {

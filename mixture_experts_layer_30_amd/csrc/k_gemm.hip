@@ -79,9 +79,9 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
     bf16_t* abp = a.ab ? a.ab + (int64_t)ft.t.p0 * 2 * I + n0 : nullptr;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (half) __syncthreads();
+      if (half) barrier_lds_only();
       HS::put(st, acc, half);
-      __syncthreads();
+      barrier_lds_only();
       const int rows = min(128, ft.nrows - 128 * half);
       for (int idx = threadIdx.x; idx < 128 * (HW / 8); idx += kThreads) {
         const int r = idx / (HW / 8), c = (idx % (HW / 8)) * 8;
@@ -113,9 +113,9 @@ MOK_DEV void gateup_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny
     bf16_t* abp = a.ab ? a.ab + (int64_t)ft.t.p0 * 2 * I + n0 : nullptr;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (half) __syncthreads();
+      if (half) barrier_lds_only();
       HS::put(st, acc, half);
-      __syncthreads();
+      barrier_lds_only();
       const int rows = min(128, ft.nrows - 128 * half);
       for (int idx = threadIdx.x; idx < 128 * (HW / 32); idx += kThreads) {
         const int r = idx / (HW / 32), blk = idx % (HW / 32);
@@ -212,7 +212,7 @@ MOK_DEV void down_tile(const mok_fwd_args& a, uint8_t* lds_raw, int ti, int ny) 
   // destination rows, staged in the top 1 KiB of LDS once every wavefront
   // has left the main loop
   int* rows = tile_rows<Smem<G, F8>>(lds_raw);
-  __syncthreads();
+  barrier_lds_only();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < ft.nrows ? a.perm[ft.t.p0 + r] : 0;
   bf16_t* ob = a.obuf + n0;
   store_bf16_x<kTrDown, G>(lds_raw, acc, ft.nrows, (int)(H - n0),
@@ -604,19 +604,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
   NoScales ns;
   Acc<G::FM, G::FN> acc;
   mainloop_rows<false, G, false>(sm, la, lb, ns, ns, (int)(H / 32), nrows, acc);
-  // w_p of the tile's rows in the top 1 KiB of LDS (outside the bf16 ring and
-  // the fp32 half-tile; published by the barrier after the first staging)
-  float* wrow = reinterpret_cast<float*>(tile_rows<Smem<G, false>>(lds_raw));
-  for (int r = threadIdx.x; r < G::BM; r += kThreads) wrow[r] = r < nrows ? a.topk_w[a.perm[t.p0 + r]] : 0.f;
-  // dA, dB and h per element from an fp32 half-tile of dh in LDS and the
-  // saved a, b (16-byte loads and stores along the row). A thread keeps one
-  // 8-column group c and takes rows r0, r0 + 8, ..., r0 + 120 of each half,
-  // in two groups of 8 rows whose a, b loads are all issued before the
-  // group's stores (the first group's before the staging): a wait for a load
-  // issued after stores also waits for those stores, so loads interleaved
-  // with the stores would serialise every row.
+  // Epilogue: dA, dB and h per element from an fp32 half-tile of dh in LDS,
+  // the saved a, b and w_p (16-byte loads and stores along the rows). A
+  // thread keeps one 8-column chunk c and takes rows r0, r0 + 8, ..., r0 +
+  // 120 of each half, in two groups of 8 rows whose a, b loads are all
+  // issued before the group's stores (the first group's before the staging):
+  // a wait for a load issued after stores also waits for those stores, so
+  // loads interleaved with the stores would serialise every row. The
+  // barriers wait for LDS operations only, so the loads stay in flight
+  // through the staging. w_p per permuted row comes from wperm (loaded with
+  // the first group) into the top 1 KiB of LDS, outside the fp32 half-tile.
   using HS = HalfF32<G>;
-  const int c = (threadIdx.x % (G::BN / 8)) * 8, r0 = threadIdx.x / (G::BN / 8);
+  float* wrow = reinterpret_cast<float*>(tile_rows<Smem<G, false>>(lds_raw));
+  const int tid = (int)threadIdx.x;                    // (kThreads == G::BM: one row each)
+  float wmine = a.wperm[t.p0 + min(tid, nrows - 1)];
+  wmine = tid < nrows ? wmine : 0.f;
+  const int c = (tid % (G::BN / 8)) * 8, r0 = tid / (G::BN / 8);
   const bool colok = n0 + c < I;
   const bf16_t* abt = a.ab + (int64_t)t.p0 * 2 * I + n0 + c;
 #pragma unroll
@@ -635,9 +638,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh_kernel(mok_bwd_args a, int
         }
       }
       if (grp == 0) {
-        if (half) __syncthreads();
+        barrier_lds_only();               // the main loop's (half 1: half 0's) LDS reads are done
         HS::put(lds_raw, acc, half);
-        __syncthreads();
+        if (half == 0) wrow[tid] = wmine;
+        barrier_lds_only();
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -685,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx_kernel(mok_bwd_args a, int
   Acc<G::FM, G::FN> acc;
   mainloop_x<kTrDx, G, false>(sm, la, lb, ns, ns, (int)(2 * I / 32), nrows, acc);
   int* rows = tile_rows<Smem<G, false>>(lds_raw);
-  __syncthreads();
+  barrier_lds_only();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   bf16_t* d = a.dxrows + n0;
   store_bf16_x<kTrDx, G>(lds_raw, acc, nrows, (int)(H - n0),
@@ -807,9 +811,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
         }
       }
       if (grp == 0) {
-        if (half) __syncthreads();
+        if (half) barrier_lds_only();
         HS::put(lds_raw, acc, half);
-        __syncthreads();
+        barrier_lds_only();
       }
 #pragma unroll
       for (int i2 = 0; i2 < 2; ++i2) {
@@ -875,7 +879,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dh8_kernel(mok_bwd_args a, in
     // first row): one 32-row block x two adjacent columns per item, read from
     // the stashed bf16 values; rows past the tile's end are zero up to the
     // expert's padded length. Same bits as quantizing stored bf16 rows.
-    __syncthreads();
+    barrier_lds_only();
     const int64_t N = 2 * I;
     const int koffe = a.koff[t.e], kp = a.koff[t.e + 1] - koffe;
     const int rbase = t.p0 - a.offsets[t.e] + 128 * half;   // padded-axis position of row 0 of the half
@@ -937,7 +941,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dx8_kernel(mok_bwd_args a, in
   Acc<G::FM, G::FN> acc;
   mainloop_x<kTrDx, G, true>(sm, la, lb, lsa, lsb, (int)(K / 64), nrows, acc);
   int* rows = tile_rows<Smem<G, true>>(lds_raw);
-  __syncthreads();
+  barrier_lds_only();
   for (int r = threadIdx.x; r < G::BM; r += kThreads) rows[r] = r < nrows ? a.perm[t.p0 + r] : 0;
   bf16_t* d = a.dxrows + n0;
   store_bf16_x<kTrDx, G>(lds_raw, acc, nrows, (int)(H - n0), [&](int r) { return d + (int64_t)rows[r] * H; });

@@ -41,12 +41,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 // place and apply w themselves); the MXFP8 backward (QUANT) also quantizes
 // each row dO[dest[i]] = bf16(w[i] * dy[t]) along H from those bf16 values
 // into permuted order (a 32-column block is the 4 chunks of 4 adjacent
-// lanes); the bf16 dO rows themselves are never stored.
+// lanes); the bf16 dO rows themselves are never stored. With wperm, each
+// routed row's weight is also written at its permuted position (wperm[dest[i]]
+// = w[i]), the per-row scale the bf16 dh epilogue applies.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void reverse_combine_kernel(
     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ obuf, const float* __restrict__ w,
     const int32_t* __restrict__ dest, const int32_t* __restrict__ offsets_E, int64_t T, int topk,
-    int64_t H, float* __restrict__ dw, uint8_t* __restrict__ dOq,
+    int64_t H, float* __restrict__ dw, float* __restrict__ wperm, uint8_t* __restrict__ dOq,
     uint8_t* __restrict__ dOs) {
   // the token of this wavefront, read from lane 0 so that its dest and w
   // entries are loaded once per wavefront through the scalar unit
@@ -111,7 +113,10 @@ __global__ __launch_bounds__(256) void reverse_combine_kernel(
       float pt = part[u];
 #pragma unroll
       for (int s = 32; s >= 1; s >>= 1) pt += __shfl_xor(pt, s);
-      if (lane == 0 && j0 + u < topk) dw[t * topk + j0 + u] = ok[u] ? pt : 0.0f;
+      if (lane == 0 && j0 + u < topk) {
+        dw[t * topk + j0 + u] = ok[u] ? pt : 0.0f;
+        if (wperm && ok[u]) wperm[pos[u]] = wv[u];
+      }
     }
   }
 }
@@ -331,15 +336,15 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
 
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, uint8_t* dOq,
+                                      int topk, int64_t H, float* dw, float* wperm, uint8_t* dOq,
                                       uint8_t* dOs, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (dOq)
     hipLaunchKernelGGL(reverse_combine_kernel<true>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy, obuf,
-                       w, dest, offsets_E, T, topk, H, dw, dOq, dOs);
+                       w, dest, offsets_E, T, topk, H, dw, wperm, dOq, dOs);
   else
     hipLaunchKernelGGL(reverse_combine_kernel<false>, dim3(grid_for(T, 4)), dim3(256), 0, st, dy,
-                       obuf, w, dest, offsets_E, T, topk, H, dw, dOq, dOs);
+                       obuf, w, dest, offsets_E, T, topk, H, dw, wperm, dOq, dOs);
   return hipGetLastError();
 }
 

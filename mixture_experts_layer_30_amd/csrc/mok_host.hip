@@ -131,7 +131,7 @@ struct FwdWs {
   size_t ring_h, ring_hs, obuf, xq, xqs, ctr, total;
 };
 struct BwdWs {
-  size_t dab, hb, dxrows;
+  size_t dab, wperm, hb, dxrows;
   // MXFP8 only
   size_t dOq, dOs, dabq, dabs, dOT, dOTs, hT, hTs, dabT, dabTs, xT, xTs, koff;
   size_t total;
@@ -156,6 +156,7 @@ BwdWs bwd_ws(const Resolved& r) {
   BwdWs w;
   size_t o = 0;
   w.dab = o;    o = align_up(o + (r.mx ? 0 : (size_t)r.R * 4 * r.I));   // bf16 dA|dB (bf16 path only)
+  w.wperm = o;  o = align_up(o + (r.mx ? 0 : (size_t)r.R * 4));         // w per permuted row (bf16 path only)
   w.hb = o;     o = align_up(o + (size_t)r.R * 2 * r.I);
   w.dxrows = o; o = align_up(o + (size_t)r.R * 2 * r.H);
   w.dOq = w.dOs = w.dabq = w.dabs = w.dOT = w.dOTs = w.hT = w.hTs = w.dabT = w.dabTs = w.xT = w.xTs = w.koff = 0;
@@ -495,7 +496,7 @@ mok_status mok_forward(const mok_problem* problem, const mok_config* config, con
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
-  if (!schedule || !weights || !y || (r.T > 0 && (!x || !topk_w))) return MOK_ERR_INVALID_ARG;
+  if (!schedule || !weights || (r.T > 0 && (!x || !topk_w || !y))) return MOK_ERR_INVALID_ARG;
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
   const FwdWs W = fwd_ws(r);
@@ -559,7 +560,7 @@ mok_status mok_forward_fused(const mok_problem* problem, const mok_config* confi
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
-  if (!schedule || !weights || !y || (r.R > 0 && !topk_ids) || (r.T > 0 && (!x || !topk_w)))
+  if (!schedule || !weights || (r.R > 0 && !topk_ids) || (r.T > 0 && (!x || !topk_w || !y)))
     return MOK_ERR_INVALID_ARG;
   if (!weights->w_gate || !weights->w_up || !weights->w_down) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->s_gate || !weights->s_up || !weights->s_down)) return MOK_ERR_INVALID_ARG;
@@ -647,6 +648,8 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   a.dy = static_cast<const bf16_t*>(dy);
   a.x = static_cast<const bf16_t*>(x);
   a.dab = r.mx ? nullptr : reinterpret_cast<bf16_t*>(ws + W.dab);   // bf16 path only
+  float* wperm = r.mx ? nullptr : reinterpret_cast<float*>(ws + W.wperm);
+  a.wperm = wperm;
   a.hb = reinterpret_cast<bf16_t*>(ws + W.hb);
   a.dxrows = reinterpret_cast<bf16_t*>(ws + W.dxrows);
   a.dwg = static_cast<bf16_t*>(dw_gate);
@@ -669,7 +672,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
     if (r.T > 0) {
       // also quantizes the dO rows along H for dh
       MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
-                                         sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, a.dOq, a.dOs, st));
+                                         sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, nullptr, a.dOq, a.dOs, st));
       MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh8(a, st));
       // dO rows w * dy formed from the dy rows in place (bitwise the stored rows' values)
       MOK_RUN("token_quantize_dO", mok_launch_token_quantize(static_cast<const bf16_t*>(dy), r.H, sp.perm, r.k,
@@ -692,7 +695,7 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   }
   if (r.T > 0) {
     MOK_RUN("reverse_combine", mok_launch_reverse_combine(static_cast<const bf16_t*>(dy), obuf, topk_w, sp.dest,
-                                       sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, nullptr, nullptr, st));
+                                       sp.offsets + r.E, r.T, r.k, r.H, d_topk_w, wperm, nullptr, nullptr, st));
     MOK_RUN("bwd_dh_gemm", mok_launch_bwd_dh(a, st));
   }
   MOK_RUN("bwd_dwd_gemm", mok_launch_bwd_dwd(a, st));

@@ -45,7 +45,7 @@ hipError_t mok_launch_combine(const bf16_t* obuf, const float* w, const int32_t*
 // dO[dest[t*k+j]] = bf16(w[t][j] * dy[t]) quantized along H (dOq, dOs).
 hipError_t mok_launch_reverse_combine(const bf16_t* dy, const bf16_t* obuf, const float* w,
                                       const int32_t* dest, const int32_t* offsets_E, int64_t T,
-                                      int topk, int64_t H, float* dw, uint8_t* dOq,
+                                      int topk, int64_t H, float* dw, float* wperm, uint8_t* dOq,
                                       uint8_t* dOs, hipStream_t st);
 
 // dx[t] = sum_j dxrows[t*k+j] (valid rows only), fp32, j ascending.
@@ -157,6 +157,7 @@ struct mok_bwd_args {
   const bf16_t* wd;
   const int32_t* tok;     // token of each permuted row (schedule)
   const float* topk_w;    // [T][k] combine weights
+  const float* wperm;     // [R] combine weight of each permuted row (bf16 path)
   const bf16_t* dy;       // [T][H] upstream gradient
   const bf16_t* x;        // [T][H] layer input
   const bf16_t* ab;       // [R][2I] permuted (saved by forward)

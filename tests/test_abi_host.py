@@ -113,6 +113,9 @@ def test_calls_reject_bad_arguments_before_any_launch():
     w0 = mok.Weights(0x1000, None, 0x1000, None, None, None)
     assert L.mok_forward(ctypes.byref(prob), None, fake, fake, fake, ctypes.byref(w0), fake, None,
                          fake, ws, None) == mok.MOK_ERR_INVALID_ARG
+    assert prob.T > 0                        # y is required when there are tokens
+    assert L.mok_forward(ctypes.byref(prob), None, fake, fake, fake, ctypes.byref(w), None, None,
+                         fake, ws, None) == mok.MOK_ERR_INVALID_ARG
     # MXFP8 forward needs scales; its backward needs the transposed weight copies
     pm = P(dtype=mok.MOK_MXFP8)
     wsm, _, cbm = mok.buffer_sizes(pm)
