@@ -411,8 +411,9 @@ MOK_DEV bool persist_item_loop(const mok_fwd_args& a, fwd_args_cptr ap, const mo
       if (!wg_agree(w, s_ok)) return false;
       persist_acquire(agent);
       persist_down<F8>(ap, (lds_u8*)lds_raw, it.ti, it.col);
-      // no wait for the obuf stores (read after the item loop only); the
-      // tile's h reads are complete (its main loop consumed every copy)
+      // the obuf stores need no agent-scope release (they are read after the
+      // item loop only); the tile's h reads are complete (its main loop
+      // consumed every copy)
       __syncthreads();
       if (threadIdx.x == 0) {
         const int done = __hip_atomic_fetch_add(C.dcnt + it.ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
