@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--driver", type=int, default=0)
     ap.add_argument("--minibatch-rows", type=int, default=0)
     ap.add_argument("--ring-slots", type=int, default=0)
+    ap.add_argument("--digest", action="store_true",
+                    help="with --only-step: one more step after the timing, and the digest of its outputs "
+                         "(to compare two builds bitwise)")
     ap.add_argument("--only-step", action="store_true",
                     help="the headline step only (no other legs); for counter runs")
     ap.add_argument("--step-dtype", choices=("bf16", "mxfp8"), default="bf16",
@@ -816,6 +819,12 @@ def main():
     if not args.only_step:
         out["determinism"] = {"runs": 10, "bitwise_identical": same, "digest": dig,
                               "outputs": "y, dx, dWg, dWu, dWd, d topk_w"}
+    elif args.digest:
+        for o in outs:
+            o.fill_(7)
+        step()
+        torch.cuda.synchronize()
+        out["digest"] = {"digest": digest(outs)[1], "outputs": "y, dx, dWg, dWu, dWd, d topk_w"}
 
     if not args.only_step:
         log("[bench] forward-only timing")
