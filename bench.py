@@ -102,6 +102,12 @@ def parse():
     ap.add_argument("--digest", action="store_true",
                     help="with --only-step: one more step after the timing, and the digest of its outputs "
                          "(to compare two builds bitwise)")
+    ap.add_argument("--only-router", action="store_true",
+                    help="the router front end only (forward and backward on the workload's tokens, "
+                         "--steps calls each after one untimed call); for kernel traces")
+    ap.add_argument("--router-stats-record", metavar="STATS_CSV",
+                    help="write the router kernel-duration summary from a rocprofv3 --kernel-trace --stats "
+                         "run of --only-router (its *_kernel_stats.csv) and exit; needs no GPU")
     ap.add_argument("--only-step", action="store_true",
                     help="the headline step only (no other legs); for counter runs")
     ap.add_argument("--step-dtype", choices=("bf16", "mxfp8"), default="bf16",
@@ -285,6 +291,35 @@ def write_kernel_stats_record(args):
     lines += ["", json.dumps({"workload": p.name, "step_dtype": args.step_dtype,
                               "sources_sha256": kernel_sources_sha256(), "kernels": rec})]
     path = os.path.join(ROOT, "profiles", f"moe_kernel_stats_{tag}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
+
+
+def write_router_stats_record(args):
+    """Kernel durations of the router front end from a rocprofv3 --kernel-trace
+    --stats run of --only-router, as a markdown summary under profiles/."""
+    import csv
+    from synthetic import CONFIGS
+    p = CONFIGS[args.config]
+    rows = [r for r in csv.DictReader(open(args.router_stats_record)) if "router" in r["Name"]]
+    lines = [f"# Kernel durations: router front end, {p.name}", "",
+             "Command (repository root on an MI355X, ROCm 7.2):", "", "```", "cd /tmp && export TMPDIR=/tmp",
+             "rocprofv3 --kernel-trace --stats -d <d> -o run -f csv -- python3 /root/repo/bench.py --only-router "
+             f"--steps 20 --config {args.config}",
+             f"python3 bench.py --config {args.config} --router-stats-record <d>/run_kernel_stats.csv", "```", "",
+             "One untimed call of each, then 20 forward and 20 backward calls on the workload's tokens (the "
+             "router kernels only; the schedule build between them is left out). The forward is one kernel "
+             "(logits, top-k, softmax); the backward two (the per-token dx rows and dWr).", "",
+             "| kernel | calls | average us | total ms |", "|---|---:|---:|---:|"]
+    rec = {}
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        n = _short(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{n}` | {r['Calls']} | {avg:.1f} | {float(r['TotalDurationNs']) / 1e6:.3f} |")
+        rec[n] = {"calls": int(r["Calls"]), "avg_us": round(avg, 2)}
+    lines += ["", json.dumps({"workload": p.name, "kernels": rec})]
+    path = os.path.join(ROOT, "profiles", f"moe_router_kernel_stats_{workload_tag(p)}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(f"wrote {os.path.relpath(path, ROOT)}", file=sys.stderr)
@@ -663,6 +698,48 @@ def forward_drivers(d, steps, warmup, stream):
     return rec
 
 
+
+def router_leg(d, p, K, stream, cfg, gx):
+    """Router front end on the workload's tokens (outside the layer step: the
+    layer takes topk_ids / topk_w as inputs): forward and backward, per-call
+    time from the library tracer's HIP events."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    from synthetic import router_weights
+    H = p.H
+    wr, rbias = router_weights(p)
+    dwr = torch.from_numpy(np.ascontiguousarray(wr.T)).cuda()
+    drb = torch.from_numpy(np.where(np.isfinite(rbias), rbias, -1e30).astype(np.float32)).cuda()
+    rids, rw = torch.empty_like(d.ids), torch.empty_like(d.w)
+    rsel, rgw = torch.empty_like(d.w), torch.empty_like(dwr)
+    rg = torch.from_numpy(np.random.default_rng(p.seed + 11).standard_normal((p.T, p.k)).astype(np.float32)).cuda()
+    wsr = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=False, **cfg)
+    prob = mok.make_problem(p.T, p.H, p.I, p.E, p.k)
+
+    def router_fwd():
+        mok.router_forward(prob, d.x, dwr, drb, rids, rw, stream)
+
+    def router_bwd():
+        mok.router_backward(prob, wsr.schedule, d.x, dwr, rids, rw, rg, rsel, gx, rgw, wsr.config, stream)
+
+    router_fwd()
+    mok.build_schedule(wsr.problem, rids, wsr.schedule, wsr.config, stream)
+    router_bwd()
+    rfst, rbst = traced(router_fwd, K), traced(router_bwd, K)
+    ms_rf = rfst["router_forward"][1] / rfst["router_forward"][0]
+    ms_rb = rbst["router_backward"][1] / rbst["router_backward"][0]
+    b_f = p.T * 2 * H + p.E * H * 4 + p.T * p.k * 8
+    b_b = 2 * p.T * 2 * H + 2 * p.E * H * 4 + p.T * p.k * 20
+    return {
+        "workload": p.name, "forward_ms": round(ms_rf, 4), "backward_ms": round(ms_rb, 4),
+        "forward_gbs": round(b_f / (ms_rf * 1e-3) / 1e9, 1), "backward_gbs": round(b_b / (ms_rb * 1e-3) / 1e9, 1),
+        "forward_bytes": b_f, "backward_bytes": b_b,
+        "logit_tflops": round(2 * p.T * p.E * H / (ms_rf * 1e-3) / 1e12, 3),
+        "timing": "HIP events around each call on the launch stream (mok_trace), averaged over the calls"}
+
 def main():
     args = parse()
     if args.traffic_record:
@@ -673,6 +750,9 @@ def main():
         return
     if args.kernel_stats_record:
         write_kernel_stats_record(args)
+        return
+    if args.router_stats_record:
+        write_router_stats_record(args)
         return
     if args.mfma_record:
         write_mfma_record(args)
@@ -687,7 +767,7 @@ def main():
 
     import mixture_experts_layer_30_amd as mok
     from mixture_experts_layer_30_amd import functional as F
-    from synthetic import CONFIGS, router_weights
+    from synthetic import CONFIGS
 
     assert torch.cuda.is_available(), "no GPU visible"
     mok.lib()
@@ -696,13 +776,17 @@ def main():
     cfg = dict(driver=args.driver, minibatch_rows=args.minibatch_rows, ring_slots=args.ring_slots)
 
     peaks = None
-    if not args.only_step:
+    if not args.only_step and not args.only_router:
         log("[bench] measured peaks (matrix cores, copy)")
         peaks = measure_peaks(stream)
         log(f"[bench] {peaks}")
 
     p = CONFIGS[args.config]
     d = Dev(p)
+    if args.only_router:
+        rr = router_leg(d, p, K, stream, cfg, torch.empty_like(d.x))
+        print(json.dumps({"router": rr, "steps": K}))
+        return
     mx_step = args.step_dtype == "mxfp8"
     ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=True,
                          dtype=mok.MOK_MXFP8 if mx_step else mok.MOK_BF16, **cfg)
@@ -868,37 +952,7 @@ def main():
         # router front end on the same tokens (outside the layer step: the
         # layer takes topk_ids / topk_w as inputs)
         log("[bench] router timing")
-        import numpy as np
-        wr, rbias = router_weights(p)
-        dwr = torch.from_numpy(np.ascontiguousarray(wr.T)).cuda()
-        drb = torch.from_numpy(np.where(np.isfinite(rbias), rbias, -1e30).astype(np.float32)).cuda()
-        rids, rw = torch.empty_like(d.ids), torch.empty_like(d.w)
-        rsel, rgw = torch.empty_like(d.w), torch.empty_like(dwr)
-        rg = torch.from_numpy(np.random.default_rng(p.seed + 11).standard_normal((p.T, p.k)).astype(np.float32)).cuda()
-        wsr = F.get_workspace(p.T, p.H, p.I, p.E, p.k, training=False, **cfg)
-        prob = mok.make_problem(p.T, p.H, p.I, p.E, p.k)
-
-        def router_fwd():
-            mok.router_forward(prob, d.x, dwr, drb, rids, rw, stream)
-
-        def router_bwd():
-            mok.router_backward(prob, wsr.schedule, d.x, dwr, rids, rw, rg, rsel, gx, rgw, wsr.config, stream)
-
-        router_fwd()
-        mok.build_schedule(wsr.problem, rids, wsr.schedule, wsr.config, stream)
-        router_bwd()
-        rfst, rbst = traced(router_fwd, K), traced(router_bwd, K)
-        ms_rf = rfst["router_forward"][1] / rfst["router_forward"][0]
-        ms_rb = rbst["router_backward"][1] / rbst["router_backward"][0]
-        b_f = p.T * 2 * H + p.E * H * 4 + p.T * p.k * 8
-        b_b = 2 * p.T * 2 * H + 2 * p.E * H * 4 + p.T * p.k * 20
-        out["router"] = {
-            "workload": p.name, "forward_ms": round(ms_rf, 4), "backward_ms": round(ms_rb, 4),
-            "forward_gbs": round(b_f / (ms_rf * 1e-3) / 1e9, 1), "backward_gbs": round(b_b / (ms_rb * 1e-3) / 1e9, 1),
-            "forward_bytes": b_f, "backward_bytes": b_b,
-            "logit_tflops": round(2 * p.T * p.E * H / (ms_rf * 1e-3) / 1e12, 3),
-            "timing": "HIP events around each call on the launch stream (mok_trace), averaged over the calls"}
-        del wsr
+        out["router"] = router_leg(d, p, K, stream, cfg, gx)
 
     if args.cpu_tokens > 0:
         log(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens")
