@@ -68,11 +68,14 @@ typedef enum { MOK_BF16 = 0, MOK_MXFP8 = 1 } mok_dtype;
  * the stream has passed the call. */
 #define MOK_STATUS_BAD_EXPERT_ID 0x1   /* some topk_ids value was outside [0, E) */
 #define MOK_STATUS_WATCHDOG      0x2   /* driver 2 gave up: a wait between its
-                                          tiles passed its time limit (2 s), or
-                                          the schedule's tile table failed its
-                                          checks; y and fwd_ctx are incomplete.
-                                          Set by mok_forward (driver 2) and
-                                          mok_forward_fused.                    */
+                                          tiles passed its time limit (2 s; the
+                                          environment variable
+                                          MOK_PERSIST_SPIN_TICKS=n sets it to n
+                                          ticks of the 100 MHz counter, for
+                                          tests), or the schedule's tile table
+                                          failed its checks; y and fwd_ctx are
+                                          incomplete. Set by mok_forward
+                                          (driver 2) and mok_forward_fused.     */
 
 /* Problem shape. Supported: T >= 0, 1 <= topk <= E <= 512, T*topk < 2^31,
  * H and I multiples of 128. dtype MOK_MXFP8 selects the MXFP8 forward and

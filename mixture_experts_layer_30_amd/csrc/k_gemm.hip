@@ -519,8 +519,11 @@ __global__ __launch_bounds__(kThreads, 1) void layer_fwd_kernel(mok_fwd_args a, 
     if (threadIdx.x == 0) ok = persist_spin(step + 0, G, C.stop, ps);
     if (!wg_agree(ok, &s_ok)) return;
     persist_acquire(true);
+    // (a give-up of another workgroup may already be in the status word,
+    // which the host cleared before the launch)
     mok_sched::sched_scan<kThreads>(L.s, L.R, a.E, L.nchunks, L.bh, a.M, L.bm_f, L.bm_b, a.n_mb, L.max_f,
-                                    L.max_b, *reinterpret_cast<mok_sched::ScanLds<kThreads>*>(lds_raw));
+                                    L.max_b, *reinterpret_cast<mok_sched::ScanLds<kThreads>*>(lds_raw),
+                                    ps.give_up_bit);
     persist_release(true);
     if (threadIdx.x == 0) __hip_atomic_store(step + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

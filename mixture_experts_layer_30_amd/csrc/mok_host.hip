@@ -480,6 +480,10 @@ mok_persist_args persist_args(const Resolved& r, const mok_sched_ptrs& sp, uint8
   ps.max_tiles = r.max_fwd_tiles;
   ps.max_mb_tiles = max_mb_tiles;
   ps.spin_limit = (uint64_t)wclk_khz * 1000ull * kPersistWaitSeconds;
+  // MOK_PERSIST_SPIN_TICKS=n replaces the limit by n ticks of the real-time
+  // counter (0: a wait not met at once gives up), to test the give-up path
+  const char* ticks = getenv("MOK_PERSIST_SPIN_TICKS");
+  if (ticks && ticks[0]) ps.spin_limit = strtoull(ticks, nullptr, 10);
   // MOK_PERSIST_AGENT_SYNC=1 selects the agent-scope synchronisation of a
   // misplaced grid on any placement (to test that path)
   const char* env = getenv("MOK_PERSIST_AGENT_SYNC");
@@ -605,6 +609,7 @@ mok_status mok_forward_fused(const mok_problem* problem, const mok_config* confi
   // expert FFN and combine in one persistent launch (layer_fwd_kernel); its
   // counters are cleared by a fill kernel on the same stream first.
   MOK_RUN("layer_clear", mok_launch_zero(ps.ctr, 4 * mok_persist_counters(r.max_fwd_tiles), st));
+  MOK_RUN("layer_clear", mok_launch_zero(sp.status, 4, st));     // the scan keeps a give-up set before it
   MOK_RUN("layer_fwd", mok_launch_layer_fwd(a, ps, L, grid, r.mx, st));
   return MOK_OK;
 }

@@ -167,9 +167,13 @@ struct ScanLds {
 // 2. totals, offsets, chunk bases (bh becomes the base of chunk c in bucket
 // v), tile tables; one NT-thread workgroup. Thread tid owns the BPT
 // consecutive buckets (and experts) from tid * BPT: with NT = 1024 one each.
+// The status word gets bit 0 (bad expert ids); the bits in keep_bits that
+// other workgroups may already have set in it (atomically, in a launch that
+// also runs this scan, after clearing the word beforehand) are kept.
 template <int NT>
 MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int32_t* __restrict__ bh, int M,
-                        int bm_f, int bm_b, int n_mb, int max_f, int max_b, ScanLds<NT>& L) {
+                        int bm_f, int bm_b, int n_mb, int max_f, int max_b, ScanLds<NT>& L,
+                        int32_t keep_bits = 0) {
   constexpr int BPT = (kMaxBuckets + NT - 1) / NT;
   const int tid = threadIdx.x, nb = E + 1;
   if (tid == 0) L.s_flag = 0;
@@ -292,7 +296,12 @@ MOK_DEV void sched_scan(const mok_sched_ptrs& s, int R, int E, int nchunks, int3
   if (tid == 0) {
     *s.n_fwd_tiles = total_f;
     *s.n_bwd_tiles = total_b;
-    *s.status = L.s_flag ? 1 : 0;
+    if (keep_bits) {
+      __hip_atomic_fetch_and(s.status, keep_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(s.status, L.s_flag ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *s.status = L.s_flag ? 1 : 0;
+    }
   }
 }
 

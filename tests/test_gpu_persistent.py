@@ -7,7 +7,9 @@ Its results must be bitwise those of the one-launch-per-stage driver (which
 workgroup runs a tile never changes what the tile computes) and match the
 oracle; the status word must not carry the give-up bit. Small cases stress
 slot reuse (one slot, many minibatches); the full-size cases run the bench
-workload's forward with saved context, bf16 and MXFP8."""
+workload's forward with saved context, bf16 and MXFP8. The give-up path
+itself is forced from the host with a zero wait limit: every workgroup must
+leave, the bit must be set, and the next call must be exact again."""
 import functools
 
 import numpy as np
@@ -157,3 +159,36 @@ def test_agent_scope_sync_path_matches(p, monkeypatch):
     assert not (F.read_schedule(ws3)["status"] & GIVE_UP)
     assert same_bits(y1, y3)
     assert same_bits(ws1.fwd_ctx, ws3.fwd_ctx)
+
+
+def test_forced_give_up_ends_every_workgroup_and_recovers(monkeypatch):
+    """Failure handling, forced from the host: with the wait limit set to 0
+    ticks of the real-time counter (MOK_PERSIST_SPIN_TICKS=0), the first wait
+    that is not met at once gives up. Every workgroup of driver 2 and of the
+    single launch must then leave (the call completes), the status word must
+    carry the give-up bit, and the next calls with the normal limit must give
+    driver 1's results bitwise (the counters are cleared before each launch)."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    p = SMALL[1]
+    print(f"[persistent] {p.name} forced give-up", flush=True)
+    d = device_inputs(p)
+    y1, _, _ = run(p, d, driver=1)
+    monkeypatch.setenv("MOK_PERSIST_SPIN_TICKS", "0")
+    _, _, s2 = run(p, d, driver=2)
+    assert s2 & GIVE_UP, f"status {s2:#x}"
+    ws3 = F.get_workspace(p.T, p.H, p.I, p.E, p.k)
+    F.run_forward_fused(ws3, d["ids"], d["x"], d["w"], d["weights"])
+    torch.cuda.synchronize()
+    # (the schedule itself may be incomplete: read only its status word)
+    off = mok.schedule_layout(ws3.problem, ws3.config).status
+    assert int(ws3.schedule[off:off + 4].cpu().view(torch.int32)[0]) & GIVE_UP
+    monkeypatch.delenv("MOK_PERSIST_SPIN_TICKS")
+    y4, _, s4 = run(p, d, driver=2)
+    assert not (s4 & GIVE_UP)
+    assert same_bits(y1, y4)
+    y5 = F.run_forward_fused(ws3, d["ids"], d["x"], d["w"], d["weights"])
+    torch.cuda.synchronize()
+    assert not (F.read_schedule(ws3)["status"] & GIVE_UP)
+    assert same_bits(y1, y5)
