@@ -272,7 +272,8 @@ mok_status mok_forward_fused(const mok_problem* problem, const mok_config* confi
  *   d_topk_w[t][j] = <dy[t], out[t*k+j]>           (fp32)
  *   dx [T][H], dw_gate/dw_up [E][I][H], dw_down [E][H][I]   (bf16)
  * Every reduction runs in a fixed order with no atomics; an expert with no
- * rows gets exact-zero weight gradients. */
+ * rows gets exact-zero weight gradients. fwd_ctx, x, topk_w, dy, dx and
+ * d_topk_w may be NULL when T = 0 (then every weight gradient is zero). */
 mok_status mok_backward(const mok_problem* problem, const mok_config* config,
                         const void* schedule, const void* fwd_ctx,
                         const void* x, const float* topk_w, const mok_weights* weights,

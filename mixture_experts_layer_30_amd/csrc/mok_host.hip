@@ -623,7 +623,8 @@ mok_status mok_backward(const mok_problem* problem, const mok_config* config,
   Resolved r;
   mok_status s = resolve(problem, config, &r);
   if (s != MOK_OK) return s;
-  if (!schedule || !fwd_ctx || !weights || !dw_gate || !dw_up || !dw_down) return MOK_ERR_INVALID_ARG;
+  if (!schedule || !weights || !dw_gate || !dw_up || !dw_down) return MOK_ERR_INVALID_ARG;
+  if (r.T > 0 && !fwd_ctx) return MOK_ERR_INVALID_ARG;
   if (r.mx && (!weights->w_down_t || !weights->w_gu_t || !weights->s_down_t || !weights->s_gu_t))
     return MOK_ERR_INVALID_ARG;
   if (r.T > 0 && (!x || !topk_w || !dy || !dx || !d_topk_w)) return MOK_ERR_INVALID_ARG;

@@ -123,6 +123,9 @@ def test_calls_reject_bad_arguments_before_any_launch():
     assert 0 < cbm == cb                     # obuf and a, b in both formats (x is read in place)
     assert L.mok_forward(ctypes.byref(pm), None, fake, fake, fake, ctypes.byref(w), fake, None,
                          fake, wsm, None) == mok.MOK_ERR_INVALID_ARG
+    # the backward needs the forward's context when there are tokens
+    assert L.mok_backward(ctypes.byref(prob), None, fake, None, fake, fake, ctypes.byref(w), fake,
+                          fake, fake, fake, fake, fake, fake, ws, None) == mok.MOK_ERR_INVALID_ARG
     wm = mok.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
     assert L.mok_backward(ctypes.byref(pm), None, fake, fake, fake, fake, ctypes.byref(wm), fake,
                           fake, fake, fake, fake, fake, fake, wsm, None) == mok.MOK_ERR_INVALID_ARG

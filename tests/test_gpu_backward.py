@@ -166,3 +166,29 @@ def test_backward_bitwise_deterministic():
         _, out = gpu_fwd_bwd(p, d, dy)
         for a, b in zip(out, ref):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_empty_input_forward_backward():
+    """T = 0: the forward writes nothing (y is empty, passed as NULL) and the
+    backward writes exact-zero weight gradients for every expert (all empty),
+    over buffers that held other bytes."""
+    import torch
+    from mixture_experts_layer_30_amd import functional as F
+    T, H, I, E, k = 0, 128, 256, 4, 2
+    print("[backward] T=0", flush=True)
+    ws = F.get_workspace(T, H, I, E, k, training=True)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    wts = tuple(torch.randn(s, generator=g).to(torch.bfloat16).cuda() for s in ((E, I, H), (E, I, H), (E, H, I)))
+    F.run_schedule(ws, ids)
+    y = F.run_forward(ws, x, w, wts)
+    dy = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    dx, dtw = torch.empty_like(x), torch.empty_like(w)
+    dwg, dwu, dwd = (torch.full_like(t, 3.0) for t in wts)
+    F.backward(ws.problem, ws.schedule, ws.fwd_ctx, x, w, wts, dy, dx, dwg, dwu, dwd, dtw, ws.workspace, ws.config)
+    torch.cuda.synchronize()
+    assert y.shape == (0, H) and dx.shape == (0, H) and dtw.shape == (0, k)
+    for name, t in (("dWg", dwg), ("dWu", dwu), ("dWd", dwd)):
+        assert not t.view(torch.int16).any(), f"{name} of an empty layer must be exactly zero"
