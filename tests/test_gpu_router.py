@@ -182,3 +182,26 @@ def test_router_backward_matches_oracle(p):
     torch.cuda.synchronize()
     assert torch.equal(d_sel, d_sel2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
     assert torch.equal(dwr.view(torch.int32), dwr2.view(torch.int32))
+
+
+def test_router_empty_input():
+    """T = 0: the forward writes nothing; the backward writes dWr = 0 exactly
+    (over a buffer that held other values), the token arrays being empty."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    T, H, E, k = 0, 256, 16, 4
+    print("[router] T=0", flush=True)
+    prob = mok.make_problem(T, H, 128, E, k)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    wr = torch.randn((E, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    mok.router_forward(prob, x, wr, None, ids, w)
+    ws = F.get_workspace(T, H, 128, E, k, training=False)
+    F.run_schedule(ws, ids)
+    dwr = torch.full((E, H), 3.0, dtype=torch.float32, device="cuda")
+    mok.router_backward(prob, ws.schedule, x, wr, ids, w, torch.empty_like(w), torch.empty_like(w),
+                        torch.empty_like(x), dwr, config=ws.config)
+    torch.cuda.synchronize()
+    assert not dwr.view(torch.int32).any()
