@@ -192,3 +192,26 @@ def test_forced_give_up_ends_every_workgroup_and_recovers(monkeypatch):
     torch.cuda.synchronize()
     assert not (F.read_schedule(ws3)["status"] & GIVE_UP)
     assert same_bits(y1, y5)
+
+
+def test_persistent_invalid_ids_match_launch_per_stage():
+    """Rows with expert ids outside [0, E) are left out of every tile: driver 2
+    stays bitwise equal to driver 1 (one slot, many minibatches), the bad-id
+    bit set and the give-up bit clear."""
+    import torch
+    p = problem(200, 256, 128, 6, 2, seed=23)
+    print(f"[persistent] {p.name} invalid ids", flush=True)
+    d = device_inputs(p)
+    ids = d["ids"].clone()
+    ids[7, 1] = 99
+    ids[150, 0] = -1
+    ids[33, 0] = 6
+    d = dict(d, ids=ids)
+    y1, _, s1 = run(p, d, driver=1, minibatch_rows=64, ring_slots=1)
+    y2, _, s2 = run(p, d, driver=2, minibatch_rows=64, ring_slots=1)
+    assert s1 & 1 and s2 & 1 and not (s2 & GIVE_UP), f"status {s1:#x} {s2:#x}"
+    assert same_bits(y1, y2)
+    x, ids_h, w, wg, wu, wd = host_inputs(p)
+    ids_h = ids.cpu().numpy()
+    ref, _ = oracle.forward(f64(x), ids_h, w.astype(np.float64), ExpertsF64(wg, wu, wd))
+    assert_close_bf16(from_dev_bf16(y2), ref, "y")
