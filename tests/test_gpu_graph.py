@@ -3,7 +3,8 @@ only kernels on the caller's stream, with no allocation, memset or host sync,
 so it can be captured in a HIP graph and replayed. Every replay must give
 bitwise the results of the eager step; replays are interleaved with eager
 work and synchronisations, and one replay follows an in-place change of the
-inputs (the graph reads the buffers it was captured with)."""
+inputs (the graph reads the buffers it was captured with). Also with the
+persistent driver and with the single-launch forward."""
 import numpy as np
 import pytest
 
@@ -17,13 +18,15 @@ pytestmark = pytest.mark.gpu
 class Step:
     """Buffers of one layer step; run() enqueues schedule + forward + backward."""
 
-    def __init__(self, p, d, dy_bits, mx):
+    def __init__(self, p, d, dy_bits, mx, kind="default"):
         import torch
         import mixture_experts_layer_30_amd as mok
         from mixture_experts_layer_30_amd import functional as F
         self.mok = mok
+        self.kind = kind
         dtype = mok.MOK_MXFP8 if mx else mok.MOK_BF16
-        self.ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=dtype, training=True)
+        cfg = dict(driver=2) if kind == "persistent" else {}
+        self.ws = F.get_workspace(p.T, p.H, p.I, p.E, p.k, dtype=dtype, training=True, **cfg)
         self.d = d
         if mx:
             self.wts = F.quantize_weights(*d["weights"]) + F.quantize_weights_backward(*d["weights"])
@@ -38,9 +41,13 @@ class Step:
 
     def run(self):
         mok, ws, d = self.mok, self.ws, self.d
-        mok.build_schedule(ws.problem, d["ids"], ws.schedule, ws.config)
-        mok.forward(ws.problem, ws.schedule, d["x"], d["w"], self.wts, self.y, ws.workspace, ws.fwd_ctx,
-                    ws.config)
+        if self.kind == "single-launch":
+            mok.forward_fused(ws.problem, d["ids"], ws.schedule, d["x"], d["w"], self.wts, self.y, ws.workspace,
+                              ws.fwd_ctx, ws.config)
+        else:
+            mok.build_schedule(ws.problem, d["ids"], ws.schedule, ws.config)
+            mok.forward(ws.problem, ws.schedule, d["x"], d["w"], self.wts, self.y, ws.workspace, ws.fwd_ctx,
+                        ws.config)
         mok.backward(ws.problem, ws.schedule, ws.fwd_ctx, d["x"], d["w"], self.wts, self.dy, self.dx,
                      self.dwg, self.dwu, self.dwd, self.dtw, ws.workspace, ws.config)
 
@@ -53,12 +60,17 @@ def _bits(ts):
     return [t.contiguous().view(-1).view(torch.uint8).cpu().numpy().copy() for t in ts]
 
 
-@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
-def test_step_replays_bitwise_in_a_hip_graph(mx):
+@pytest.mark.parametrize("mx,kind", [(False, "default"), (True, "default"), (False, "persistent"),
+                                     (False, "single-launch")],
+                         ids=["bf16", "mxfp8", "bf16-persistent", "bf16-single-launch"])
+def test_step_replays_bitwise_in_a_hip_graph(mx, kind):
+    """(persistent, single-launch: the forward's counters are cleared by fill
+    kernels captured with it, so every replay starts from zero counters)"""
     import torch
     p = problem(300, 256, 384, 16, 4, seed=61)
+    print(f"[graph] mx={mx} {kind}", flush=True)
     d = device_inputs(p)
-    step = Step(p, d, make_dy(p), mx)
+    step = Step(p, d, make_dy(p), mx, kind)
 
     step.run()
     torch.cuda.synchronize()
