@@ -147,7 +147,7 @@ def permute_bytes(p):
     R, T, H = p.R, p.T, p.H
     return {
         "combine": R * 2 * H + R * 8 + T * 2 * H,                # obuf rows, w + dest, y rows
-        "reverse_combine": R * 2 * H + T * 2 * H + R * 12,       # obuf rows, dY, w/dest/dw
+        "reverse_combine": R * 2 * H + T * 2 * H + R * 16,       # obuf rows, dY, w/dest/dw, w at dest
         "reverse_dispatch": R * 2 * H + R * 4 + T * 2 * H,       # dX rows, dest, dx rows
     }
 
