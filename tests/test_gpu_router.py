@@ -76,7 +76,8 @@ def _check_selection(ids, w, logits, bias, k):
 CASES = [problem(37, 256, 128, 5, 2, seed=61), problem(300, 128, 128, 64, 8, seed=62),
          problem(200, 384, 128, 12, 3, seed=63), problem(64, 512, 128, 512, 8, seed=64),
          problem(129, 256, 128, 32, 4, seed=66, zipf_s=1.2, empty_den=4), problem(9, 128, 128, 6, 6, seed=67),
-         problem(40, 256, 128, 128, 64, seed=68)]      # E > 64 (round-based selection), maximum k
+         problem(40, 256, 128, 128, 64, seed=68),      # E > 64 (round-based selection), maximum k
+         problem(100, 256, 128, 100, 4, seed=70)]      # 64 < E <= 128 with k <= 8: the widest dense dWr tile
 
 
 @pytest.mark.parametrize("with_bias", [False, True], ids=["nobias", "bias"])
@@ -179,6 +180,41 @@ def test_router_backward_matches_oracle(p):
     # bitwise reproducible
     d_sel2, dx2, dwr2 = torch.empty_like(d_sel), torch.empty_like(dx), torch.empty_like(dwr)
     mok.router_backward(*args[:7], d_sel2, dx2, dwr2, config=ws.config)
+    torch.cuda.synchronize()
+    assert torch.equal(d_sel, d_sel2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(dwr.view(torch.int32), dwr2.view(torch.int32))
+
+
+def test_router_backward_full_size():
+    """The fwd+bwd workload's router (T=16384 H=7168 E=32 top-4, Zipf(0.8)
+    selection bias): d_sel, dWr (the dense contraction over all 16384 tokens)
+    and every dx row against the oracle, bitwise the same on a second call."""
+    import torch
+    import mixture_experts_layer_30_amd as mok
+    from mixture_experts_layer_30_amd import functional as F
+    p = CONFIGS[4]
+    print(f"[router] backward {p.name}", flush=True)
+    x, wr_eh, bias = _inputs(p, True)
+    ids, w = _run(p, x, wr_eh, bias)
+    g = np.random.default_rng(p.seed + 100).standard_normal((p.T, p.k)).astype(np.float32)
+    ws = F.get_workspace(p.T, p.H, 128, p.E, p.k, training=False)
+    F.run_schedule(ws, torch.from_numpy(ids).cuda())
+    prob = mok.make_problem(p.T, p.H, 128, p.E, p.k)
+    d_sel = torch.empty((p.T, p.k), dtype=torch.float32, device="cuda")
+    dx = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
+    dwr = torch.empty((p.E, p.H), dtype=torch.float32, device="cuda")
+    args = (prob, ws.schedule, to_dev_bf16(x), torch.from_numpy(wr_eh).cuda(), torch.from_numpy(ids).cuda(),
+            torch.from_numpy(w).cuda(), torch.from_numpy(g).cuda())
+    mok.router_backward(*args, d_sel, dx, dwr, config=ws.config)
+    torch.cuda.synchronize()
+    ref_sel, _, ref_dwr, ref_dx = oracle.router_backward(bf16_to_f32(x).astype(np.float64),
+                                                         wr_eh.astype(np.float64), ids, w.astype(np.float64),
+                                                         g.astype(np.float64))
+    assert np.allclose(d_sel.cpu().numpy(), ref_sel, rtol=1e-5, atol=1e-6)
+    assert rel_fro(dwr.cpu().numpy(), ref_dwr) < 1e-5
+    assert_close_bf16(from_dev_bf16(dx), ref_dx, "router dx")
+    d_sel2, dx2, dwr2 = torch.empty_like(d_sel), torch.empty_like(dx), torch.empty_like(dwr)
+    mok.router_backward(*args, d_sel2, dx2, dwr2, config=ws.config)
     torch.cuda.synchronize()
     assert torch.equal(d_sel, d_sel2) and torch.equal(dx.view(torch.int16), dx2.view(torch.int16))
     assert torch.equal(dwr.view(torch.int32), dwr2.view(torch.int32))
