@@ -155,6 +155,26 @@ def test_large_hidden_step_bitwise_deterministic_10_runs():
                 assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"run {run} differs"
 
 
+@pytest.mark.parametrize("p", [problem(300, 128, 384, 16, 4, seed=42), CONFIGS[4]], ids=lambda p: p.name)
+def test_ring_configuration_leaves_every_output_bitwise_unchanged(p):
+    """Each routed row's arithmetic does not depend on the minibatch, ring slot
+    or tile it lands in, so y and every gradient are bitwise the same for any
+    minibatch size and slot count: one minibatch (M = R), the default ring,
+    many minibatches through one slot, and a ragged size through three."""
+    import torch
+    dy = make_dy(p)
+    d = device_inputs(p)
+    y0, out0 = gpu_fwd_bwd(p, d, dy, minibatch_rows=p.R, ring_slots=1)
+    ref = [y0.clone()] + [t.clone() for t in out0]
+    small = max(256, p.R // 16)
+    for cfg in ({}, dict(minibatch_rows=small, ring_slots=1), dict(minibatch_rows=small + 128 * 3 + 64,
+                                                                   ring_slots=3)):
+        print(f"[ring] {p.name} {cfg}", flush=True)
+        y, out = gpu_fwd_bwd(p, d, dy, **cfg)
+        for name, a, b in zip(("y", "dx", "dWg", "dWu", "dWd", "d topk_w"), [y] + list(out), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (cfg, name)
+
+
 def test_backward_bitwise_deterministic():
     import torch
     p = problem(2048, 512, 256, 16, 4, seed=45, zipf_s=1.0)
