@@ -43,6 +43,29 @@ class ExpertsF64:
         return f64(self.wg[e]), f64(self.wu[e]), f64(self.wd[e])
 
 
+class ExpertsSliceI:
+    """experts[e] restricted to the intermediate channels [i0, i1): rows of Wg
+    and Wu, columns of Wd. Every quantity the MXFP8 weight gradients are made
+    of is channel-local: a and b (x and the Wg, Wu rows blocked along H), dh
+    (dO and the Wd columns blocked along H), dA, dB and h elementwise, and
+    their token-blocked copies blocked per channel along the rows; nothing
+    in that path is blocked along I. So the backward's dWg, dWu rows and dWd
+    columns of the range come out as with all channels (not dX, whose
+    operand dA|dB is blocked along 2I, nor d topk_w, which takes the forward
+    output)."""
+
+    def __init__(self, experts, i0, i1):
+        assert 0 <= i0 < i1
+        self.ex, self.i0, self.i1 = experts, i0, i1
+
+    def __len__(self):
+        return len(self.ex)
+
+    def __getitem__(self, e):
+        wg, wu, wd = self.ex[e]
+        return wg[self.i0:self.i1], wu[self.i0:self.i1], wd[:, self.i0:self.i1]
+
+
 def rel_fro(got, ref):
     n = np.linalg.norm(ref)
     return np.linalg.norm(got - ref) / (n if n > 0 else 1.0)

@@ -230,15 +230,44 @@ def test_mxfp8_backward_bitwise_deterministic():
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
+@pytest.mark.parametrize("p", [problem(300, 512, 384, 16, 4, seed=52), CONFIGS[4]], ids=lambda p: p.name)
+def test_mxfp8_ring_configuration_leaves_every_output_bitwise_unchanged(p):
+    """As in bf16: every quantization block lies inside one row (along H or I)
+    or inside one expert's token axis, none inside a minibatch, so y and
+    every gradient are bitwise the same for any minibatch size and slot
+    count."""
+    import torch
+    from synthetic import make_dy
+    from test_gpu_forward import device_inputs
+    d = device_inputs(p)
+    dy = make_dy(p)
+    y0, g0 = gpu_mx_fwd_bwd(p, d, dy, minibatch_rows=p.R, ring_slots=1)
+    ref = [y0.clone()] + [t.clone() for t in g0]
+    small = max(256, p.R // 16)
+    for cfg in ({}, dict(minibatch_rows=small, ring_slots=1), dict(minibatch_rows=small + 128 * 3 + 64,
+                                                                   ring_slots=3)):
+        print(f"[mxfp8 ring] {p.name} {cfg}", flush=True)
+        y, g = gpu_mx_fwd_bwd(p, d, dy, **cfg)
+        for name, a, b in zip(("y", "dx", "dWg", "dWu", "dWd", "d topk_w"), [y] + list(g), ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (cfg, name)
+
+
 @pytest.mark.timeout(900)
-def test_mxfp8_fwd_bwd_full_size_sampled():
-    """The benchmark workload (T=4096, H=2048, E=64, top-8, I=768) through the
-    MXFP8 forward with context and the MXFP8 backward at the default
-    minibatch: sampled tokens for dx and d topk_w, the least and most loaded
-    experts for the weight gradients."""
+@pytest.mark.parametrize("cfg", [1, 4], ids=["T4096_H2048_E64_k8", "T16384_H7168_E32_k4"])
+def test_mxfp8_fwd_bwd_full_size_sampled(cfg):
+    """Two full-size workloads (T=4096 H=2048 E=64 top-8 I=768; the fwd+bwd
+    workload T=16384 H=7168 E=32 top-4 I=2048 with Zipf(0.8) loads) through
+    the MXFP8 forward with context and the MXFP8 backward at the default
+    minibatch: sampled tokens for dx and d topk_w, the least and the most
+    loaded expert for the weight gradients. On the fwd+bwd workload the most
+    loaded expert (about 12000 rows: the longest token-axis K loop) is checked
+    on its last 256 intermediate channels (ExpertsSliceI: the same values as
+    with all channels, at a fraction of the oracle's time)."""
+    from moe_testlib import ExpertsSliceI
     from synthetic import make_dy
     from test_gpu_forward import device_inputs, host_inputs, sampled_tokens
-    p = CONFIGS[1]
+    p = CONFIGS[cfg]
+    print(f"[mxfp8 fwd+bwd] {p.name}", flush=True)
     x, ids, w, wg, wu, wd = host_inputs(p)
     dy = make_dy(p)
     _, (dx, dwg, dwu, dwd, dtw) = gpu_mx_fwd_bwd(p, device_inputs(p), dy)
@@ -250,10 +279,13 @@ def test_mxfp8_fwd_bwd_full_size_sampled():
             "d topk_w[sampled]": rel_fro(dtw.cpu().numpy()[toks].astype(np.float64), dwr)}
     counts = np.bincount(ids.reshape(-1), minlength=p.E)
     for e in (int(np.argmin(counts)), int(np.argmax(counts))):
-        dg, du, dd = oracle.backward_mxfp8_expert_weights(e, f64(x), ids, w.astype(np.float64), ex, f64(dy))
-        errs[f"dWg[{e}]"] = rel_fro(from_dev_bf16(dwg[e]), dg)
-        errs[f"dWu[{e}]"] = rel_fro(from_dev_bf16(dwu[e]), du)
-        errs[f"dWd[{e}]"] = rel_fro(from_dev_bf16(dwd[e]), dd)
+        i0 = p.I - 256 if (cfg == 4 and counts[e] > 4096) else 0
+        print(f"expert {e}: {counts[e]} rows, channels {i0}..{p.I}", flush=True)
+        dg, du, dd = oracle.backward_mxfp8_expert_weights(e, f64(x), ids, w.astype(np.float64),
+                                                          ExpertsSliceI(ex, i0, p.I), f64(dy))
+        errs[f"dWg[{e}]"] = rel_fro(from_dev_bf16(dwg[e])[i0:], dg)
+        errs[f"dWu[{e}]"] = rel_fro(from_dev_bf16(dwu[e])[i0:], du)
+        errs[f"dWd[{e}]"] = rel_fro(from_dev_bf16(dwd[e])[:, i0:], dd)
     print("MXFP8 backward, full size:", {k: f"{v:.3e}" for k, v in errs.items()}, flush=True)
     for k, v in errs.items():
         assert v <= REL_FRO_MXFP8, f"{k}: relative Frobenius error {v:.3e}"

@@ -151,3 +151,19 @@ def test_sampled_helpers_match_full():
     dx, dw = oracle.backward_mxfp8_tokens(x[toks], ids[toks], w[toks], ex, dy[toks])
     assert rel(dx, g["dx"][toks]) < 1e-12
     assert rel(dw, g["dw"][toks]) < 1e-12
+
+
+def test_channel_slice_matches_full():
+    """The GPU tests take the weight gradients of a hot expert on a range of
+    intermediate channels (moe_testlib.ExpertsSliceI): that range of the
+    full computation, up to fp64 rounding, for aligned and unaligned ranges
+    (no block of the weight-gradient path runs along I)."""
+    from moe_testlib import ExpertsSliceI
+    x, ids, w, ex = rand_case(40, 64, 128, 3, 2, seed=73)
+    dy = np.random.default_rng(74).standard_normal((40, 64))
+    for e in range(3):
+        dWg, dWu, dWd = oracle.backward_mxfp8_expert_weights(e, x, ids, w, ex, dy)
+        for i0, i1 in ((32, 96), (16, 80), (0, 128)):
+            sg, su, sd = oracle.backward_mxfp8_expert_weights(e, x, ids, w, ExpertsSliceI(ex, i0, i1), dy)
+            assert rel(sg, dWg[i0:i1]) < 1e-12 and rel(su, dWu[i0:i1]) < 1e-12
+            assert rel(sd, dWd[:, i0:i1]) < 1e-12
