@@ -56,7 +56,7 @@ extern "C" {
 typedef enum {
   MOK_OK = 0,
   MOK_ERR_INVALID_ARG = -1,      /* null pointer, bad size or shape            */
-  MOK_ERR_UNSUPPORTED = -2,      /* valid but not supported by this build      */
+  MOK_ERR_UNSUPPORTED = -2,      /* valid but not supported by this library    */
   MOK_ERR_BUFFER_TOO_SMALL = -3, /* a caller buffer is below mok_buffer_sizes  */
   MOK_ERR_DEVICE = -4            /* no gfx950 device, or a launch failed       */
 } mok_status;
